@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every function include/condensate.h
+declares, and rejects bad arguments on the host before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_transformer_attention_amd as ca
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "condensate.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ca_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ca.LIB_PATH):
+        from sparse_transformer_attention_amd import build
+        build.build(verbose=False)
+    return ca.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(ca.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_status_strings(lib):
+    for rc in (ca.CA_OK, ca.CA_ERR_INVALID_ARG, ca.CA_ERR_UNSUPPORTED, ca.CA_ERR_WORKSPACE, ca.CA_ERR_HIP):
+        s = ca.status_string(rc)
+        assert s.startswith("CA_")
+    assert ca.status_string(12345) == "unknown status"
+
+
+def good(**kw):
+    base = dict(batch=1, heads=32, kv_heads=8, d=128, n=131072, nq=1, W=256, topk=64, dtype="bf16", chunk=0)
+    base.update(kw)
+    return ca.params(**base)
+
+
+def ws_size(p):
+    n = ctypes.c_size_t(0)
+    rc = ca.load().ca_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    return rc, n.value
+
+
+BAD = [
+    (dict(batch=0), ca.CA_ERR_INVALID_ARG, "batch"),
+    (dict(heads=0), ca.CA_ERR_INVALID_ARG, "heads"),
+    (dict(kv_heads=0), ca.CA_ERR_INVALID_ARG, "heads"),
+    (dict(heads=30, kv_heads=8), ca.CA_ERR_INVALID_ARG, "multiple"),
+    (dict(n=0), ca.CA_ERR_INVALID_ARG, "n must"),
+    (dict(n=2**31), ca.CA_ERR_INVALID_ARG, "n must"),
+    (dict(nq=0), ca.CA_ERR_INVALID_ARG, "nq"),
+    (dict(n=100, nq=101), ca.CA_ERR_INVALID_ARG, "nq"),
+    (dict(W=0), ca.CA_ERR_INVALID_ARG, "W must"),
+    (dict(topk=-1), ca.CA_ERR_INVALID_ARG, "topk"),
+    (dict(d=96), ca.CA_ERR_UNSUPPORTED, "head dimension"),
+    (dict(dtype=7), ca.CA_ERR_UNSUPPORTED, "dtype"),
+    (dict(W=4000, topk=96), ca.CA_ERR_UNSUPPORTED, "exceeds"),
+    (dict(chunk=300), ca.CA_ERR_INVALID_ARG, "chunk"),
+    (dict(chunk=128), ca.CA_ERR_INVALID_ARG, "chunk"),
+    (dict(chunk=8192), ca.CA_ERR_INVALID_ARG, "chunk"),
+]
+
+
+@pytest.mark.parametrize("kw,rc,msg", BAD)
+def test_validation_codes(lib, kw, rc, msg):
+    p = good(**kw)
+    got, _ = ws_size(p)
+    assert got == rc
+    assert msg in ca.last_error()
+    # Every entry point validates the same way before any HIP call.
+    vp = ctypes.c_void_p(16)
+    assert lib.ca_condensate_attention_ex(ctypes.byref(p), vp, vp, vp, vp, vp, vp, 1 << 40, None) == rc
+    assert lib.ca_condensate_select(ctypes.byref(p), vp, vp, vp, vp, 1 << 40, None) == rc
+    assert lib.ca_attention_on_subset(ctypes.byref(p), vp, vp, vp, vp, vp, None) == rc
+
+
+def test_null_params_and_pointers(lib):
+    assert lib.ca_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == ca.CA_ERR_INVALID_ARG
+    p = good()
+    assert lib.ca_workspace_size(ctypes.byref(p), None) == ca.CA_ERR_INVALID_ARG
+    vp = ctypes.c_void_p(16)
+    assert lib.ca_condensate_attention_ex(ctypes.byref(p), None, vp, vp, vp, vp, vp, 1 << 40, None) == ca.CA_ERR_INVALID_ARG
+    assert lib.ca_condensate_select(ctypes.byref(p), vp, None, vp, vp, 1 << 40, None) == ca.CA_ERR_INVALID_ARG
+    assert lib.ca_attention_on_subset(ctypes.byref(p), vp, vp, vp, None, vp, None) == ca.CA_ERR_INVALID_ARG
+    assert lib.ca_condensate_attention(None, vp, vp, 16, 64, 1, 1, 4, 2, vp, vp) == ca.CA_ERR_INVALID_ARG
+    assert lib.ca_condensate_attention(vp, vp, vp, 16, 80, 1, 1, 4, 2, vp, vp) == ca.CA_ERR_UNSUPPORTED
+
+
+def test_workspace_checks(lib):
+    p = good()
+    rc, need = ws_size(p)
+    assert rc == ca.CA_OK and need > 0
+    vp = ctypes.c_void_p(16)
+    assert lib.ca_condensate_select(ctypes.byref(p), vp, vp, vp, vp, need - 1, None) == ca.CA_ERR_WORKSPACE
+    assert "smaller" in ca.last_error()
+    assert lib.ca_condensate_select(ctypes.byref(p), vp, vp, vp, None, need, None) == ca.CA_ERR_WORKSPACE
+
+
+def test_workspace_size_rules(lib):
+    # No candidates (topk = 0, or every position inside the window): no workspace at all.
+    assert ws_size(good(topk=0)) == (ca.CA_OK, 0)
+    assert ws_size(good(n=200, W=256)) == (ca.CA_OK, 0)
+    # Grows with the cache length and with the query count.
+    sizes = [ws_size(good(n=n))[1] for n in (4096, 65536, 131072, 1 << 20)]
+    assert sizes == sorted(sizes)
+    assert ws_size(good(nq=8, n=131072))[1] >= ws_size(good(nq=1, n=131072))[1]
+    # An explicit chunk is honoured: halving it doubles the candidate slots.
+    a = ws_size(good(chunk=1024))[1]
+    b = ws_size(good(chunk=512))[1]
+    assert b == 2 * a
