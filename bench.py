@@ -1,0 +1,217 @@
+"""Benchmark of the condensate-attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--chunk C] [--rotate R]
+
+A step is one call of ca_condensate_attention_ex: scores over every causal key, anchor/window
+masks, chunk-local exact top-k, global merge and set assembly, then the restricted softmax
+times V -- the whole path, on one batch of synthetic inputs already resident in HBM. The
+default workload is the 131,072-token GQA decode step (32 query heads, 8 KV heads, d=128,
+bf16, W=256, k=64). Distinct KV buffer sets are rotated between steps so that the key stream
+comes from HBM and not from the 256 MB last-level cache.
+
+Prints one JSON line with queries/s (query vectors per second), the step's algorithmic HBM
+GB/s, the roofline of the dominant kernel (score_select; durations from HIP events the library
+records around its own launches on the stream it uses) and the CPU oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "condensate-attn decode queries/sec + achieved HBM GB/s at 131K ctx (1 GPU)"
+HBM_PEAK_GBPS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "score_select_decode_131k_counters.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_transformer_attention_amd", "csrc", f)
+                  for f in ("select_kernels.hip", "device_utils.h", "ca_internal.h")]
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per score_select launch from the committed counter summary, or None when the
+    summary is absent, is for another workload, or predates the current kernel sources."""
+    if not os.path.exists(COUNTERS):
+        return None
+    text = open(COUNTERS).read()
+    m_sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]+)", text)
+    m_wl = re.search(r"workload:\s*(\S+)", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_wl and m_b) or m_wl.group(1) != workload or m_sha.group(1) != kernel_sources_sha():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_info():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode_131k_gqa_bf16")
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--rotate", type=int, default=0, help="KV buffer sets (0 = enough for 1 GiB of K)")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 10 times (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            torch.mul(src, 1.0, out=dst)   # one elementwise kernel: reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 1 << 30, "launches": 10}))
+        return
+
+    import numpy as np
+    import sparse_transformer_attention_amd as ca
+    from sparse_transformer_attention_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    seed = synth.default_seed(w) if args.seed is None else args.seed
+    x = synth.make_inputs(w, seed=seed, device="cuda")
+    eb = w.elem_bytes
+    k_bytes = w.batch * w.kv_heads * w.n * w.d * eb
+    rotate = args.rotate or max(1, -(-(1 << 30) // k_bytes))
+    sets = [(x["k"], x["v"])] + [(x["k"].clone(), x["v"].clone()) for _ in range(rotate - 1)]
+    q = x["q"]
+    p = ca.params_for(q, x["k"], w.W, w.topk, args.chunk)
+    ws = ca.alloc_workspace(p)
+    out = torch.empty((w.batch, w.heads, w.nq, w.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.batch, w.heads, w.nq, w.set_cap), dtype=torch.int32, device="cuda")
+
+    def step(s):
+        kk, vv = sets[s % rotate]
+        ca.condensate_attention_ex(p, q, kk, vv, out, idx, ws)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ca.profile_start(3 * args.steps)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for s in range(args.steps):
+        step(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = ca.profile_stop()
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Algorithmic bytes. score_select reads the key rows of the candidate range once per KV
+    # head plus the queries; the whole step reads all of K, the distinct V rows of the sets,
+    # the queries, and writes the outputs and index sets.
+    rmax = max(0, w.n - 1 - w.W)
+    q_bytes = w.batch * w.heads * w.nq * w.d * eb
+    score_bytes = w.batch * w.kv_heads * rmax * w.d * eb + q_bytes
+    idx_np = idx.cpu().numpy()
+    v_rows = 0
+    for b in range(w.batch):
+        for kvh in range(w.kv_heads):
+            rows = idx_np[b, kvh * w.group:(kvh + 1) * w.group].reshape(-1)
+            v_rows += len(np.unique(rows[rows >= 0]))
+    step_bytes = (k_bytes + v_rows * w.d * eb + q_bytes + w.batch * w.heads * w.nq * w.d * 4
+                  + idx_np.size * 4)
+    nqv = w.batch * w.heads * w.nq
+
+    launches, score_ms = prof.get("score_select", (0, 0.0))
+    score_avg_s = score_ms / max(1, launches) / 1e3
+    achieved = score_bytes / score_avg_s / 1e9 if launches else None
+    traffic = recorded_traffic(w.name)
+    kernels = {name: {"launches": n, "avg_us": round(t / max(1, n) * 1e3, 3)} for name, (n, t) in prof.items()}
+
+    record = {
+        "metric": METRIC,
+        "value": nqv / (ms_per_step / 1e3),
+        "unit": "query vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "kv_heads": w.kv_heads,
+                   "d": w.d, "n": w.n, "nq": w.nq, "W": w.W, "topk": w.topk, "accumulate": "f32",
+                   "chunk": args.chunk or "auto", "kv_sets_rotated": rotate, "seed": seed},
+        "hbm_gbps": step_bytes / (ms_per_step / 1e3) / 1e9,
+        "step_algorithmic_bytes": step_bytes,
+        "gpu_ms_per_step": gpu_ms / args.steps,
+        "kernels": kernels,
+        "roofline": {
+            "kernel": "score_select",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": (achieved / HBM_PEAK_GBPS) if achieved else None,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": score_bytes,
+            "avg_launch_us": score_avg_s * 1e6,
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        qc, kc, vc = q.cpu(), x["k"].cpu(), x["v"].cpu()
+        reps, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds:
+            t1 = time.perf_counter()
+            oracle.condensate(qc, kc, vc, w.W, w.topk)
+            t_cpu += time.perf_counter() - t1
+            reps += 1
+        record["cpu_baseline"] = {
+            "value": reps * nqv / t_cpu,
+            "unit": "query vectors/s",
+            "cores": oracle.threads_used(),
+            "kind": "oracle",
+            "sample": f"{reps} whole steps of the same workload ({nqv} query vectors each over "
+                      f"{w.n} keys), float64, {t_cpu:.1f} s",
+            "cpu": cpu_info(),
+        }
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,7 +32,7 @@
  *   - Nothing is thrown across this ABI. Calls on different streams may run concurrently as
  *     long as they do not share a workspace.
  *
- * Supported: d in {64, 128}; n < 2^31; heads % kv_heads == 0; W >= 1; topk >= 0;
+ * Supported: d in {64, 128}; n < 2^31; heads % kv_heads == 0; W >= 1; 0 <= topk <= 512;
  * 1 + W + topk <= CA_MAX_SET.
  */
 #ifndef CONDENSATE_H
@@ -67,8 +67,9 @@ typedef struct {
     int32_t W;         /* local window length, >= 1 (the window includes position i) */
     int32_t topk;      /* dynamic top-k size, >= 0 */
     int32_t dtype;     /* ca_dtype of q, k, v */
-    int32_t chunk;     /* key rows per score-and-select workgroup; 0 = automatic, else a
-                          power of two in [256, 4096] */
+    int32_t chunk;     /* key rows per unit of work of the scoring pass; 0 = automatic (256),
+                          else 256, 512 or 1024 (a hint: lowered to 512 when topk + chunk
+                          would exceed 1024). Results do not depend on it. */
 } ca_params;
 
 /* The one-call form, as the method is usually stated: float32 q/k/v, batch 1, every position
@@ -80,7 +81,8 @@ int ca_condensate_attention(const void *q, const void *k, const void *v, int64_t
                             float *out, int32_t *out_idx);
 
 /* Bytes of device workspace that ca_condensate_attention_ex / ca_condensate_select need for
- * problem p (may be 0). Host only. */
+ * problem p (may be 0). Host only. The workspace needs no initialisation: each call clears the
+ * part it relies on, on the call's stream, so calls that share a workspace must be ordered. */
 int ca_workspace_size(const ca_params *p, size_t *bytes);
 
 /* Full method, asynchronous on `stream`, caller-provided workspace (ws may be NULL only if
@@ -101,6 +103,22 @@ int ca_condensate_select(const ca_params *p, const void *q, const void *k, int32
  * zero output row. No workspace. */
 int ca_attention_on_subset(const ca_params *p, const void *q, const void *k, const void *v,
                            const int32_t *idx, float *out, void *stream);
+
+/* Measurement hooks (not part of the method). While profiling is on -- a process-wide switch --
+ * every kernel this library enqueues is bracketed by two HIP events recorded on the stream it
+ * is launched on, so the durations are the kernels' own. ca_profile_start pre-creates events
+ * for `reserve_launches` launches (more are created on demand) and clears earlier records.
+ * ca_profile_stop turns profiling off, waits for the recorded events, and writes one entry per
+ * kernel name (launches, summed milliseconds) into out[0..capacity), setting *count to the
+ * number of kernels seen. Not meant to be used from several threads at once. */
+typedef struct {
+    const char *kernel;  /* static name: "score_select", "finish" or "attend" */
+    int64_t launches;
+    double total_ms;
+} ca_kernel_time;
+
+int ca_profile_start(int32_t reserve_launches);
+int ca_profile_stop(ca_kernel_time *out, int32_t capacity, int32_t *count);
 
 /* Static text for a status code. */
 const char *ca_status_string(int status);

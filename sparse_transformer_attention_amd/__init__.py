@@ -29,7 +29,8 @@ CA_F32, CA_BF16 = 0, 1
 CA_MAX_SET = 4096
 
 EXPORTED = ("ca_condensate_attention", "ca_workspace_size", "ca_condensate_attention_ex",
-            "ca_condensate_select", "ca_attention_on_subset", "ca_status_string", "ca_last_error")
+            "ca_condensate_select", "ca_attention_on_subset", "ca_profile_start",
+            "ca_profile_stop", "ca_status_string", "ca_last_error")
 
 
 class Params(ctypes.Structure):
@@ -40,6 +41,11 @@ class Params(ctypes.Structure):
         ("W", ctypes.c_int32), ("topk", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("chunk", ctypes.c_int32),
     ]
+
+
+class KernelTime(ctypes.Structure):
+    """Mirror of ca_kernel_time."""
+    _fields_ = [("kernel", ctypes.c_char_p), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
 class CondensateError(RuntimeError):
@@ -67,12 +73,16 @@ def load() -> ctypes.CDLL:
         L.ca_condensate_attention_ex.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.ca_condensate_select.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.ca_attention_on_subset.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.ca_profile_start.argtypes = [ctypes.c_int32]
+        L.ca_profile_stop.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_int32)]
         L.ca_status_string.argtypes = [ctypes.c_int]
         L.ca_status_string.restype = ctypes.c_char_p
         L.ca_last_error.argtypes = []
         L.ca_last_error.restype = ctypes.c_char_p
         for f in (L.ca_condensate_attention, L.ca_workspace_size, L.ca_condensate_attention_ex,
-                  L.ca_condensate_select, L.ca_attention_on_subset):
+                  L.ca_condensate_select, L.ca_attention_on_subset, L.ca_profile_start,
+                  L.ca_profile_stop):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -181,3 +191,16 @@ def condensate(q, k, v, W: int, topk: int, chunk: int = 0, ws=None, stream=None)
         ws = alloc_workspace(p, q.device)
     condensate_attention_ex(p, q, k, v, out, out_idx, ws, stream)
     return out, out_idx
+
+
+def profile_start(reserve_launches: int = 0):
+    """Start bracketing every launch of this library with HIP events (see ca_profile_start)."""
+    _check(load().ca_profile_start(reserve_launches), "ca_profile_start")
+
+
+def profile_stop() -> dict:
+    """Stop profiling; returns {kernel name: (launches, total milliseconds)}."""
+    arr = (KernelTime * 8)()
+    n = ctypes.c_int32(0)
+    _check(load().ca_profile_stop(arr, 8, ctypes.byref(n)), "ca_profile_stop")
+    return {arr[i].kernel.decode(): (int(arr[i].launches), float(arr[i].total_ms)) for i in range(n.value)}

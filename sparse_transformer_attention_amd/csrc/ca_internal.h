@@ -9,31 +9,43 @@ namespace ca {
 
 // Work plan of one call: problem sizes plus the decode-path decomposition.
 //
-// Score-and-select ("stage 1a") runs on a grid of (chunk, query group, batch*kv_head).
-// A query group is up to G query vectors that read the same KV head: the g query heads of a
-// GQA group and/or consecutive query rows, ordered t = r*g + (h - kvh*g). A chunk is `chunk`
-// consecutive key rows of the candidate range {1 .. (n-1)-W} (the union of every query's R_i).
-// Each (query, chunk) pair leaves min(topk, |chunk & R_i|) keys in the candidate workspace.
+// score_topk works on units = (batch, KV head, query group): up to G query vectors that read
+// the same KV head (the g query heads of a GQA group and/or consecutive query rows, ordered
+// t = r*g + (h - kvh*g)). A unit's candidate rows {1 .. max (i-W)} are cut into chunks of
+// `chunk` rows; workgroup m of the unit's wpu workgroups takes chunks m, m + wpu, ...
+//
+// Workspace: [nqv][wpu] published k-th keys and [nqv][wpu] published best keys (cleared by the
+// library at the start of every call), [nqv][wpu] segment lengths (32-bit words), then at
+// lists_offset the segments, [nqv][wpu][topk] 64-bit ranking keys.
 struct Plan {
     int B, Hq, Hkv, g, d, W, topk, dtype;
     int64_t n, nq;
     int64_t nqv;          // query vectors: B*Hq*nq
     int cap;              // 1 + W + topk (out_idx row length)
     int64_t rmax;         // last candidate row of the last query: (n-1) - W (may be < 1)
-    int G;                // query vectors per score-and-select workgroup
-    int64_t groups;       // query groups per KV head: ceil(g*nq / G)
+    int G;                // query vectors per unit
+    int64_t groups;       // units per KV head: ceil(g*nq / G)
+    int64_t units;        // B * Hkv * groups
+    bool candidates;      // topk > 0 and some query has a non-empty R_i
     int chunk;            // key rows per chunk
-    int64_t nchunks;      // chunks over rows 1..rmax (0 if rmax < 1)
-    size_t cand_bytes;    // candidate keys: nqv * nchunks * topk * 8
+    int rcap;             // running-list capacity per query: 512, 768 or 1536
+    int wpu;              // workgroups per unit
+    int64_t nwg;          // score_topk workgroups
+    int64_t lmax;         // candidate slots per query (wpu * topk)
+    size_t lists_offset;  // byte offset of the lists in the workspace
     size_t ws_bytes;      // total workspace
 };
 
-// Launchers (enqueue only; return the hipError_t of the launch).
-hipError_t launch_score_select(const Plan &pl, const void *q, const void *k, uint64_t *cand,
+// Launchers (enqueue only; return the hipError_t of the last launch).
+hipError_t launch_score_select(const Plan &pl, const void *q, const void *k, void *ws,
                                hipStream_t s);
-hipError_t launch_merge_assemble(const Plan &pl, const uint64_t *cand, int32_t *out_idx,
-                                 hipStream_t s);
+// Merge + set assembly (+ restricted softmax times V when out != nullptr), one workgroup per
+// query vector.
+hipError_t launch_finish(const Plan &pl, const void *ws, const void *q, const void *k,
+                         const void *v, int32_t *out_idx, float *out, hipStream_t s);
+// Restricted softmax times V on caller-supplied index sets.
 hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k, const void *v,
                                     const int32_t *idx, float *out, hipStream_t s);
+size_t topk_lds_bytes(const Plan &pl);
 
 }  // namespace ca

@@ -4,10 +4,65 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "ca_internal.h"
 #include "condensate.h"
 
 namespace {
+
+// ---- measurement hooks: HIP events around each launch while profiling is on ----------------
+enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_COUNT = 3 };
+const char *const kKernelNames[K_COUNT] = {"score_select", "finish", "attend"};
+
+struct Profiler {
+    std::mutex mu;
+    bool on = false;
+    std::vector<hipEvent_t> pool;
+    struct Rec { int kernel; hipEvent_t start, stop; };
+    std::vector<Rec> recs;
+
+    hipEvent_t take() {
+        if (pool.empty()) {
+            hipEvent_t e = nullptr;
+            if (hipEventCreate(&e) != hipSuccess) return nullptr;
+            return e;
+        }
+        hipEvent_t e = pool.back();
+        pool.pop_back();
+        return e;
+    }
+};
+Profiler g_prof;
+
+// Brackets one launch with events when profiling is on.
+struct ProfScope {
+    int kernel;
+    hipStream_t s;
+    hipEvent_t start = nullptr;
+    ProfScope(int k, hipStream_t st) : kernel(k), s(st) {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        if (!g_prof.on) return;
+        start = g_prof.take();
+        if (start && hipEventRecord(start, s) != hipSuccess) {
+            g_prof.pool.push_back(start);
+            start = nullptr;
+        }
+    }
+    void done() {
+        if (!start) return;
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        hipEvent_t stop = g_prof.take();
+        if (stop && hipEventRecord(stop, s) == hipSuccess) {
+            g_prof.recs.push_back({kernel, start, stop});
+        } else {
+            g_prof.pool.push_back(start);
+            if (stop) g_prof.pool.push_back(stop);
+        }
+        start = nullptr;
+    }
+};
 
 thread_local char g_last_error[512] = "";
 
@@ -23,9 +78,9 @@ int hip_fail(hipError_t e, const char *what) {
     return fail(CA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
-constexpr int kMinChunk = 256, kMaxChunk = 4096;
-constexpr int kKeyLdsBytes = 32 * 1024;  // LDS for one score-and-select workgroup's keys
-constexpr int64_t kTargetBlocks = 1024;  // score-and-select workgroups to aim for (256 CUs)
+constexpr int kMinChunk = 256, kMaxChunk = 1024, kDefaultChunk = 256;
+constexpr int kMaxTopk = 512;            // running lists hold topk + chunk <= 1024 keys
+constexpr int64_t kTargetBlocks = 1024;  // score_topk workgroups to aim for (4 per CU)
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -49,6 +104,8 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         return fail(CA_ERR_UNSUPPORTED, "head dimension %d is not supported (64 or 128)", p->d);
     if ((int64_t)p->W + p->topk + 1 > CA_MAX_SET)
         return fail(CA_ERR_UNSUPPORTED, "1 + W + topk = %lld exceeds %d", (long long)p->W + p->topk + 1, CA_MAX_SET);
+    if (p->topk > kMaxTopk)
+        return fail(CA_ERR_UNSUPPORTED, "topk %d exceeds %d", p->topk, kMaxTopk);
     if (p->chunk != 0 && (!is_pow2(p->chunk) || p->chunk < kMinChunk || p->chunk > kMaxChunk))
         return fail(CA_ERR_INVALID_ARG, "chunk must be 0 or a power of two in [%d, %d] (got %d)",
                     kMinChunk, kMaxChunk, p->chunk);
@@ -66,32 +123,39 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     P.G = nvec >= 4 ? 4 : (nvec >= 2 ? 2 : 1);
     if (P.G > gmax) P.G = gmax;
     P.groups = (nvec + P.G - 1) / P.G;
+    P.units = (int64_t)P.B * P.Hkv * P.groups;
+    P.candidates = P.topk > 0 && P.rmax >= 1;
 
-    P.chunk = 0;
-    P.nchunks = 0;
-    P.cand_bytes = 0;
-    if (P.topk > 0 && P.rmax >= 1) {
-        const int lds_cap = kKeyLdsBytes / (4 * P.G);
-        int chunk = p->chunk;
-        if (chunk == 0) {
-            // Largest chunk that still gives about kTargetBlocks workgroups.
-            const int64_t units = (int64_t)P.B * P.Hkv * P.groups;
-            chunk = kMaxChunk;
-            while (chunk > kMinChunk && units * ((P.rmax + chunk - 1) / chunk) < kTargetBlocks) chunk >>= 1;
-        }
-        if (chunk > lds_cap) chunk = lds_cap;
+    // Running-list capacity: 512, 768 or 1536 keys, the smallest that takes k plus one chunk
+    // (topk <= 512 and chunk <= 1024, so 1536 always does); the list is cut back to k only when
+    // another chunk might not fit. Halve the chunk while the selection buffers exceed 64 KiB of
+    // LDS.
+    int chunk = p->chunk ? p->chunk : kDefaultChunk;
+    for (;;) {
         P.chunk = chunk;
-        P.nchunks = (P.rmax + chunk - 1) / chunk;
-        const int64_t blocks = P.nchunks * P.groups * (int64_t)P.B * P.Hkv;
-        if (blocks > (int64_t)UINT32_MAX / 256)
-            return fail(CA_ERR_UNSUPPORTED, "problem too large for one launch (%lld workgroups)", (long long)blocks);
-        const double bytes = (double)P.nqv * (double)P.nchunks * (double)P.topk * 8.0;
-        if (bytes > 9.0e18) return fail(CA_ERR_UNSUPPORTED, "workspace size overflows");
-        P.cand_bytes = (size_t)P.nqv * (size_t)P.nchunks * (size_t)P.topk * sizeof(uint64_t);
+        const int need = P.topk + chunk;
+        P.rcap = need <= 512 ? 512 : need <= 768 ? 768 : 1536;
+        if (ca::topk_lds_bytes(P) <= 64 * 1024 || chunk <= kMinChunk) break;
+        chunk /= 2;
     }
-    if (P.nqv > (int64_t)UINT32_MAX / 256)
-        return fail(CA_ERR_UNSUPPORTED, "too many query vectors for one launch (%lld)", (long long)P.nqv);
-    P.ws_bytes = P.cand_bytes;
+    const int64_t nchunks = P.rmax >= 1 ? (P.rmax + chunk - 1) / chunk : 0;
+    if (P.units >= kTargetBlocks || nchunks <= 1) {
+        P.wpu = 1;
+    } else {
+        int64_t w = (kTargetBlocks + P.units - 1) / P.units;
+        P.wpu = (int)(w < nchunks ? w : nchunks);
+    }
+    P.nwg = P.wpu > 1 ? P.units * P.wpu : P.units;
+    P.lmax = (int64_t)P.wpu * (P.topk > 0 ? P.topk : 1);
+    if (P.nwg > (int64_t)UINT32_MAX / 256 || P.nqv > (int64_t)UINT32_MAX / 256)
+        return fail(CA_ERR_UNSUPPORTED, "problem too large for one launch");
+    const double list_bytes = (double)P.nqv * (double)P.lmax * 8.0;
+    if (list_bytes > 9.0e18) return fail(CA_ERR_UNSUPPORTED, "workspace size overflows");
+    const size_t slot_bytes = ((size_t)(3 * P.nqv * P.wpu) * sizeof(uint32_t) + 255) & ~(size_t)255;
+    P.lists_offset = slot_bytes;
+    P.ws_bytes = P.candidates ? slot_bytes + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) : 0;
+    if (ca::topk_lds_bytes(P) > 64 * 1024)
+        return fail(CA_ERR_UNSUPPORTED, "selection buffers exceed the LDS budget");
     return CA_OK;
 }
 
@@ -102,17 +166,30 @@ int check_ws(const ca::Plan &pl, void *ws, size_t ws_bytes) {
     return CA_OK;
 }
 
-// Stage 1: scores, chunk-local top-k, merge and set assembly into out_idx.
-int run_select(const ca::Plan &pl, const void *q, const void *k, int32_t *out_idx, void *ws,
-               hipStream_t s) {
-    uint64_t *cand = static_cast<uint64_t *>(ws);
+// Scores and candidate lists, then the merge and set assembly into out_idx; with out != nullptr
+// the restricted softmax times V runs in the same (finish) kernel.
+int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, int32_t *out_idx,
+             float *out, void *ws, hipStream_t s) {
     hipError_t e;
-    if (pl.nchunks > 0) {
-        e = ca::launch_score_select(pl, q, k, cand, s);
-        if (e != hipSuccess) return hip_fail(e, "score_select launch");
+    if (pl.candidates) {
+        ProfScope ps(K_SCORE, s);
+        e = ca::launch_score_select(pl, q, k, ws, s);
+        ps.done();
+        if (e != hipSuccess) return hip_fail(e, "score_topk launch");
     }
-    e = ca::launch_merge_assemble(pl, cand, out_idx, s);
-    if (e != hipSuccess) return hip_fail(e, "merge_assemble launch");
+    ProfScope pf(K_FINISH, s);
+    e = ca::launch_finish(pl, pl.candidates ? ws : nullptr, q, k, v, out_idx, out, s);
+    pf.done();
+    if (e != hipSuccess) return hip_fail(e, "finish launch");
+    return CA_OK;
+}
+
+int run_attend(const ca::Plan &pl, const void *q, const void *k, const void *v,
+               const int32_t *idx, float *out, hipStream_t s) {
+    ProfScope pa(K_ATTEND, s);
+    hipError_t e = ca::launch_gather_softmax_av(pl, q, k, v, idx, out, s);
+    pa.done();
+    if (e != hipSuccess) return hip_fail(e, "attend launch");
     return CA_OK;
 }
 
@@ -149,7 +226,7 @@ int ca_condensate_select(const ca_params *p, const void *q, const void *k, int32
     if (rc != CA_OK) return rc;
     if (!q || !k || !out_idx) return fail(CA_ERR_INVALID_ARG, "q, k and out_idx must be non-NULL");
     if ((rc = check_ws(pl, ws, ws_bytes)) != CA_OK) return rc;
-    return run_select(pl, q, k, out_idx, ws, static_cast<hipStream_t>(stream));
+    return run_path(pl, q, k, nullptr, out_idx, nullptr, ws, static_cast<hipStream_t>(stream));
 }
 
 int ca_attention_on_subset(const ca_params *p, const void *q, const void *k, const void *v,
@@ -158,9 +235,7 @@ int ca_attention_on_subset(const ca_params *p, const void *q, const void *k, con
     int rc = make_plan(p, &pl);
     if (rc != CA_OK) return rc;
     if (!q || !k || !v || !idx || !out) return fail(CA_ERR_INVALID_ARG, "q, k, v, idx and out must be non-NULL");
-    hipError_t e = ca::launch_gather_softmax_av(pl, q, k, v, idx, out, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "attend launch");
-    return CA_OK;
+    return run_attend(pl, q, k, v, idx, out, static_cast<hipStream_t>(stream));
 }
 
 int ca_condensate_attention_ex(const ca_params *p, const void *q, const void *k, const void *v,
@@ -172,11 +247,7 @@ int ca_condensate_attention_ex(const ca_params *p, const void *q, const void *k,
     if (!q || !k || !v || !out || !out_idx)
         return fail(CA_ERR_INVALID_ARG, "q, k, v, out and out_idx must be non-NULL");
     if ((rc = check_ws(pl, ws, ws_bytes)) != CA_OK) return rc;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((rc = run_select(pl, q, k, out_idx, ws, s)) != CA_OK) return rc;
-    hipError_t e = ca::launch_gather_softmax_av(pl, q, k, v, out_idx, out, s);
-    if (e != hipSuccess) return hip_fail(e, "attend launch");
-    return CA_OK;
+    return run_path(pl, q, k, v, out_idx, out, ws, static_cast<hipStream_t>(stream));
 }
 
 int ca_condensate_attention(const void *q, const void *k, const void *v, int64_t n, int32_t d,
@@ -208,6 +279,55 @@ int ca_condensate_attention(const void *q, const void *k, const void *v, int64_t
         e = hipFree(ws);
         if (e != hipSuccess && rc == CA_OK) rc = hip_fail(e, "hipFree(workspace)");
     }
+    return rc;
+}
+
+int ca_profile_start(int32_t reserve_launches) {
+    if (reserve_launches < 0) return fail(CA_ERR_INVALID_ARG, "reserve_launches must be >= 0");
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    for (auto &r : g_prof.recs) {
+        g_prof.pool.push_back(r.start);
+        g_prof.pool.push_back(r.stop);
+    }
+    g_prof.recs.clear();
+    while ((int64_t)g_prof.pool.size() < 2 * (int64_t)reserve_launches) {
+        hipEvent_t e = nullptr;
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+        g_prof.pool.push_back(e);
+    }
+    g_prof.recs.reserve(reserve_launches);
+    g_prof.on = true;
+    return CA_OK;
+}
+
+int ca_profile_stop(ca_kernel_time *out, int32_t capacity, int32_t *count) {
+    if (!count || (capacity > 0 && !out)) return fail(CA_ERR_INVALID_ARG, "out/count must be non-NULL");
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.on = false;
+    int64_t launches[K_COUNT] = {0, 0, 0};
+    double ms[K_COUNT] = {0, 0, 0};
+    int rc = CA_OK;
+    for (auto &r : g_prof.recs) {
+        if (rc == CA_OK) {
+            hipError_t e = hipEventSynchronize(r.stop);
+            float t = 0.f;
+            if (e == hipSuccess) e = hipEventElapsedTime(&t, r.start, r.stop);
+            if (e != hipSuccess) rc = hip_fail(e, "reading profile events");
+            launches[r.kernel] += 1;
+            ms[r.kernel] += t;
+        }
+        g_prof.pool.push_back(r.start);
+        g_prof.pool.push_back(r.stop);
+    }
+    g_prof.recs.clear();
+    int n = 0;
+    for (int kid = 0; kid < K_COUNT; ++kid) {
+        if (!launches[kid]) continue;
+        if (n < capacity) out[n] = {kKernelNames[kid], launches[kid], ms[kid]};
+        ++n;
+    }
+    *count = n;
     return rc;
 }
 

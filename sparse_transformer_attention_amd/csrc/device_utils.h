@@ -38,6 +38,11 @@ __device__ __forceinline__ float dpp_xor1(float x) {
 __device__ __forceinline__ float dpp_xor2(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
 }
+// Value of the lane at the mirrored position within each group of 8 (lane i <-> 7 - i), which
+// always pairs a lane of the lower half of the group with one of the upper half.
+__device__ __forceinline__ float dpp_half_mirror(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+}
 
 // Order-preserving map of a float32 score to uint32 (larger score -> larger key); -0 is
 // folded onto +0 so that equal scores give equal keys. Every finite score maps to a key
@@ -51,6 +56,85 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 // Count of set bits of `m` in lanes below this one.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// DPP lane move (gfx9 controls): row_shr:n = 0x110+n, row_ror:n = 0x120+n, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143. Lanes of disabled rows, or reading outside their row, get `old`.
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROW_MASK, BANK_MASK, false);
+}
+
+// Inclusive prefix sum over the 64 lanes, all in DPP (no LDS traffic).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+    x += dpp_u32<0x111>(0u, x);
+    x += dpp_u32<0x112>(0u, x);
+    x += dpp_u32<0x114>(0u, x);
+    x += dpp_u32<0x118>(0u, x);
+    x += dpp_u32<0x142, 0xA>(0u, x);
+    x += dpp_u32<0x143, 0xC>(0u, x);
+    return x;
+}
+
+// Maximum / minimum over the 64 lanes (result uniform), DPP within rows then 4 lane reads.
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t x) {
+    uint32_t o;
+    o = dpp_u32<0x121>(x, x); x = o > x ? o : x;
+    o = dpp_u32<0x122>(x, x); x = o > x ? o : x;
+    o = dpp_u32<0x124>(x, x); x = o > x ? o : x;
+    o = dpp_u32<0x128>(x, x); x = o > x ? o : x;
+    const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+    const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
+}
+__device__ __forceinline__ uint32_t wave_min_u32_dpp(uint32_t x) {
+    uint32_t o;
+    o = dpp_u32<0x121>(x, x); x = o < x ? o : x;
+    o = dpp_u32<0x122>(x, x); x = o < x ? o : x;
+    o = dpp_u32<0x124>(x, x); x = o < x ? o : x;
+    o = dpp_u32<0x128>(x, x); x = o < x ? o : x;
+    const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+    const uint32_t ab = a < b ? a : b, cd = c < d ? c : d;
+    return ab < cd ? ab : cd;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) { const uint32_t o = __shfl_xor(x, off); x = o > x ? o : x; }
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) { const uint32_t o = __shfl_xor(x, off); x = o < x ? o : x; }
+    return x;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = __shfl_xor((unsigned long long)x, off);
+        x = o > x ? o : x;
+    }
+    return x;
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = __shfl_xor((unsigned long long)x, off);
+        x = o < x ? o : x;
+    }
+    return x;
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
 }
 
 // Orders LDS traffic between the lanes of one wavefront (no workgroup barrier).

@@ -1,0 +1,350 @@
+// The end of the condensate-attention path on gfx950, one workgroup per query vector:
+//   merge    exact top-k' of the candidates score_topk left in the query's segments (ranking
+//            keys (score_key << 32) | ~position; k' = min(k, |R_i|));
+//   assemble C_i = {0} u top-k' u {i-W+1..i} in ascending order, written to out_idx (pages of
+//            "The Condensate Theorem", metaphor-xennon blog, section 2.1 Definition 1);
+//   attend   (optional) the restricted softmax times V on that set, straight from LDS.
+// Plus the standalone attend kernel for caller-supplied sets (flash_attention_on_subset of the
+// section 5.2.2 sketch).
+#include "attend_core.h"
+#include "ca_internal.h"
+#include "device_utils.h"
+#include "select_core.h"
+
+namespace ca {
+namespace {
+
+struct FinishArgs {
+    int64_t n, nq;
+    int Hq, Hkv, g, W, topk, cap, wpu;
+    float scale_log2e;
+    const uint32_t *cnt;    // [nqv][wpu] keys in each segment
+    const uint64_t *lists;  // [nqv][wpu][topk] segments of candidate ranking keys
+};
+
+constexpr int kGather = 1024;  // candidates gathered into LDS for the one-wavefront select
+constexpr int kMaxKeysPerThread = 16;  // candidate keys held in registers per thread
+
+template <int NT>
+struct SelectShared {
+    uint32_t hist[NT / 64][320];  // words 256 + lane absorb keys outside the current prefix
+    uint64_t red64[2][NT / 64];
+    uint32_t wtot[NT / 64];
+    uint32_t pick[3];
+    int sel_count;
+};
+
+// Maximum / minimum of 64-bit values over the lanes of a wavefront (uniform result).
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t x) {
+    const uint32_t hi = (uint32_t)(x >> 32);
+    const uint32_t hmax = wave_max_u32_dpp(hi);
+    const uint32_t lmax = wave_max_u32_dpp(hi == hmax ? (uint32_t)x : 0u);
+    return ((uint64_t)hmax << 32) | lmax;
+}
+__device__ __forceinline__ uint64_t wave_min_u64_dpp(uint64_t x) {
+    const uint32_t hi = (uint32_t)(x >> 32);
+    const uint32_t hmin = wave_min_u32_dpp(hi);
+    const uint32_t lmin = wave_min_u32_dpp(hi == hmin ? (uint32_t)x : 0xFFFFFFFFu);
+    return ((uint64_t)hmin << 32) | lmin;
+}
+
+// Exact top-kp of one query's candidates: the first cnt[w] keys of each segment w of
+// lists[w][0..topk) (distinct, non-zero; at least kp of them). The kp positions go to
+// js[0..kp), ascending (js needs room for 2*kp). Up to kGather candidates are gathered into
+// LDS by wavefront 0, which then selects alone with the keys in registers; more are selected by
+// the whole workgroup, re-reading the segments on every radix pass.
+template <int NT>
+__device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt,
+                                                const uint64_t *__restrict__ lists, int wpu,
+                                                int topk, int kp, int32_t *js, uint64_t *sel,
+                                                uint64_t *gathered, SelectShared<NT> &sh) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (wave == 0) {
+        int base = 0;
+        for (int j0 = 0; j0 < wpu; j0 += 64) {
+            const int w = j0 + lane;
+            const int c = w < wpu ? (int)cnt[w] : 0;
+            int tot;
+            const int off = base + wave_excl_scan(c, &tot);
+            for (int e = 0; e < c; ++e)
+                if (off + e < kGather) gathered[off + e] = lists[(size_t)w * topk + e];
+            base += tot;
+        }
+        if (lane == 0) sh.sel_count = base;
+    }
+    __syncthreads();
+    const int n = sh.sel_count;
+    __syncthreads();
+    if (n <= kGather) {
+        if (wave == 0) {
+            uint64_t kk[kMaxKeysPerThread];
+#pragma unroll
+            for (int e = 0; e < kMaxKeysPerThread; ++e) {
+                const int f = lane + 64 * e;
+                kk[e] = f < n ? gathered[f] : 0ull;
+            }
+            (void)wave_keep_top_u64(kk, kp, &sh.hist[0][0], sel);
+        }
+        __syncthreads();
+        for (int t = tid; t < kp; t += NT) js[t] = rank_key_pos(sel[t]);
+    } else {
+        const int64_t slots = (int64_t)wpu * topk;
+        auto key_at = [&](int64_t f) -> uint64_t {
+            const int w = (int)(f / topk);
+            const int e = (int)(f - (int64_t)w * topk);
+            return e < (int)cnt[w] ? lists[f] : 0ull;
+        };
+        uint64_t kmax = 0ull, kmin = ~0ull;
+        for (int64_t f = tid; f < slots; f += NT) {
+            const uint64_t x = key_at(f);
+            if (x) { kmax = x > kmax ? x : kmax; kmin = x < kmin ? x : kmin; }
+        }
+        kmax = wave_max_u64_dpp(kmax);
+        kmin = wave_min_u64_dpp(kmin);
+        if (lane == 0) { sh.red64[0][wave] = kmax; sh.red64[1][wave] = kmin; }
+        __syncthreads();
+        kmax = sh.red64[0][0];
+        kmin = sh.red64[1][0];
+#pragma unroll
+        for (int w2 = 1; w2 < NW; ++w2) {
+            kmax = sh.red64[0][w2] > kmax ? sh.red64[0][w2] : kmax;
+            kmin = sh.red64[1][w2] < kmin ? sh.red64[1][w2] : kmin;
+        }
+        int hb = 63 - __builtin_clzll((kmax ^ kmin) | 1ull);
+        uint64_t mask = hb >= 63 ? 0ull : (~0ull << (hb + 1));
+        uint64_t prefix = kmax & mask;
+        int rem = kp;
+        if (kp >= n) { hb = -1; mask = 0ull; prefix = 0ull; }
+        while (hb >= 0) {
+            const int lb = hb >= 7 ? hb - 7 : 0;
+            const uint32_t dmask = (2u << (hb - lb)) - 1u;
+            for (int t = tid; t < NW * 320; t += NT) (&sh.hist[0][0])[t] = 0u;
+            __syncthreads();
+            for (int64_t f = tid; f < slots; f += NT) {
+                const uint64_t x = key_at(f);
+                const bool in = x && (x & mask) == prefix;
+                atomicAdd(&sh.hist[wave][in ? (uint32_t)(x >> lb) & dmask : 256u + lane], 1u);
+            }
+            __syncthreads();
+            uint32_t own = 0u, pre = 0u;
+            if (tid < 256) {
+#pragma unroll
+                for (int w2 = 0; w2 < NW; ++w2) own += sh.hist[w2][tid];
+                pre = wave_incl_scan_u32(own);
+                if (lane == 63) sh.wtot[wave] = pre;
+            }
+            __syncthreads();
+            if (tid < 256) {
+                uint32_t before = 0u, all = 0u;
+#pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2) {
+                    before += w2 < wave ? sh.wtot[w2] : 0u;
+                    all += sh.wtot[w2];
+                }
+                const uint32_t incl = all - (before + pre) + own;  // keys in bins >= tid
+                if (incl >= (uint32_t)rem && incl - own < (uint32_t)rem) {  // exactly one bin
+                    sh.pick[0] = (uint32_t)tid;
+                    sh.pick[1] = own;
+                    sh.pick[2] = incl - own;
+                }
+            }
+            __syncthreads();
+            const uint32_t digit = sh.pick[0], h_digit = sh.pick[1], above = sh.pick[2];
+            rem -= (int)above;
+            prefix |= (uint64_t)digit << lb;
+            mask |= (uint64_t)dmask << lb;
+            __syncthreads();
+            if (h_digit == (uint32_t)rem) break;  // distinct keys: reached by the last digit
+            hb = lb - 1;
+        }
+        if (tid == 0) sh.sel_count = 0;
+        __syncthreads();
+        for (int64_t f = tid; f < slots; f += NT) {
+            const uint64_t x = key_at(f);
+            if (x && (x & mask) >= prefix) {
+                const int pos = atomicAdd(&sh.sel_count, 1);
+                if (pos < kp) js[pos] = rank_key_pos(x);
+            }
+        }
+    }
+    __syncthreads();
+    // Ascending order: each position's rank is the number of smaller ones; the sorted copy
+    // goes to js[kp..2kp) and then back.
+    for (int t0 = 0; t0 < kp; t0 += NT) {
+        const int t = t0 + tid;
+        if (t < kp) {
+            const int32_t j = js[t];
+            int rank = 0;
+#pragma unroll 8
+            for (int u = 0; u < kp; ++u) rank += js[u] < j;
+            js[kp + rank] = j;
+        }
+    }
+    __syncthreads();
+    for (int t = tid; t < kp; t += NT) js[t] = js[kp + t];
+    __syncthreads();
+}
+
+template <typename T, int D, int NT, bool ATTEND>
+__global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                    const T *__restrict__ v,
+                                                    int32_t *__restrict__ out_idx,
+                                                    float *__restrict__ out, FinishArgs a) {
+    extern __shared__ int32_t fsm[];  // js[2*cap] positions, sc[cap] scores, sel[topk] keys
+    __shared__ union {
+        SelectShared<NT> sel;
+        AttendShared<NT, D, T> att;
+    } shu;  // the select and the attend phases never overlap
+    SelectShared<NT> &ssh = shu.sel;
+    AttendShared<NT, D, T> &ash = shu.att;
+    __shared__ uint64_t gathered[kGather];
+    int32_t *js = fsm;
+    float *sc = reinterpret_cast<float *>(fsm + 2 * a.cap);
+    uint64_t *sel = reinterpret_cast<uint64_t *>(fsm + 3 * a.cap + (a.cap & 1));
+
+    const int tid = threadIdx.x;
+    const int64_t qv = blockIdx.x;
+    const int64_t r = qv % a.nq;
+    const int64_t i = a.n - a.nq + r;
+    const int64_t wlo = (i - a.W + 1 > 0) ? i - a.W + 1 : 0;
+    const int64_t rl = i - a.W;
+    const int64_t n_r = rl >= 1 ? rl : 0;
+    const int kp = (int)(a.topk < n_r ? a.topk : n_r);
+
+    // js layout: [0 if the anchor is separate][top-k' ascending][window ascending]
+    const int base = wlo > 0 ? 1 : 0;
+    if (kp > 0)
+        select_segments<NT>(a.cnt + qv * a.wpu, a.lists + qv * a.wpu * a.topk, a.wpu, a.topk, kp,
+                            js + base, sel, gathered, ssh);
+    const int wcount = (int)(i - wlo + 1);
+    const int count = base + kp + wcount;
+    if (tid == 0 && base) js[0] = 0;
+    for (int t = tid; t < wcount; t += NT) js[base + kp + t] = (int32_t)(wlo + t);
+    __syncthreads();
+    int32_t *row = out_idx + qv * a.cap;
+    for (int t = tid; t < a.cap; t += NT) row[t] = t < count ? js[t] : -1;
+    if constexpr (ATTEND) {
+        const int64_t bh = qv / a.nq;
+        const int h = (int)(bh % a.Hq);
+        const int b = (int)(bh / a.Hq);
+        const size_t kv0 = ((size_t)b * a.Hkv + h / a.g) * (size_t)a.n * D;
+        attend_set<NT, D, T>(q + qv * D, k + kv0, v + kv0, js, sc, count, a.n, a.scale_log2e,
+                             out + qv * D, ash);
+    }
+}
+
+// Caller-supplied sets: ordered compaction of the valid entries of the index row, then attend.
+template <typename T, int D, int NT>
+__global__ __launch_bounds__(NT) void attend_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                    const T *__restrict__ v,
+                                                    const int32_t *__restrict__ idx,
+                                                    float *__restrict__ out, FinishArgs a) {
+    extern __shared__ int32_t asm_[];  // js[cap], then sc[cap]
+    __shared__ int wave_cnt[NT / 64];
+    __shared__ AttendShared<NT, D, T> ash;
+    int32_t *js = asm_;
+    float *sc = reinterpret_cast<float *>(asm_ + a.cap);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t qv = blockIdx.x;
+    const int64_t r = qv % a.nq;
+    const int64_t bh = qv / a.nq;
+    const int h = (int)(bh % a.Hq);
+    const int b = (int)(bh / a.Hq);
+    const int64_t i = a.n - a.nq + r;
+    const int32_t *row = idx + qv * a.cap;
+
+    int count = 0;
+    for (int c0 = 0; c0 < a.cap; c0 += NT) {
+        const int c = c0 + tid;
+        const int32_t j = c < a.cap ? row[c] : -1;
+        const bool ok = j >= 0 && j <= i;
+        const uint64_t m = __ballot(ok);
+        if (lane == 0) wave_cnt[wave] = __popcll(m);
+        __syncthreads();
+        int off = count, tot = 0;
+        for (int w2 = 0; w2 < NT / 64; ++w2) {
+            off += w2 < wave ? wave_cnt[w2] : 0;
+            tot += wave_cnt[w2];
+        }
+        if (ok) js[off + lanes_below(m)] = j;
+        count += tot;
+        __syncthreads();
+    }
+    float *o = out + qv * D;
+    if (count == 0) {
+        for (int t = tid; t < D; t += NT) o[t] = 0.f;
+        return;
+    }
+    const size_t kv0 = ((size_t)b * a.Hkv + h / a.g) * (size_t)a.n * D;
+    attend_set<NT, D, T>(q + qv * D, k + kv0, v + kv0, js, sc, count, a.n, a.scale_log2e, o, ash);
+}
+
+FinishArgs finish_args(const Plan &pl, const void *ws) {
+    FinishArgs a;
+    a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g;
+    a.W = pl.W; a.topk = pl.topk; a.cap = pl.cap; a.wpu = pl.wpu;
+    a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
+    a.cnt = ws ? static_cast<const uint32_t *>(ws) + 2 * pl.nqv * pl.wpu : nullptr;
+    a.lists = ws ? reinterpret_cast<const uint64_t *>(static_cast<const char *>(ws) + pl.lists_offset) : nullptr;
+    return a;
+}
+
+// Few query vectors: 1024 threads each (latency); many: 256.
+constexpr int64_t kWideBelow = 4096;
+
+template <typename T, int D, bool ATTEND>
+hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const void *k,
+                           const void *v, int32_t *out_idx, float *out, hipStream_t s) {
+    const FinishArgs a = finish_args(pl, ws);
+    const size_t shmem = (size_t)pl.cap * (3 * sizeof(int32_t)) + 8 + (size_t)pl.topk * sizeof(uint64_t);
+    const dim3 grid((unsigned)pl.nqv);
+    const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v);
+    const size_t fixed1024 = kGather * sizeof(uint64_t) +
+                             (sizeof(SelectShared<1024>) > sizeof(AttendShared<1024, D, T>)
+                                  ? sizeof(SelectShared<1024>) : sizeof(AttendShared<1024, D, T>));
+    const bool wide = pl.nqv < kWideBelow && shmem + fixed1024 <= 64 * 1024;
+    if (wide)
+        hipLaunchKernelGGL((finish_kernel<T, D, 1024, ATTEND>), grid, dim3(1024), shmem, s, qt, kt, vt, out_idx, out, a);
+    else
+        hipLaunchKernelGGL((finish_kernel<T, D, 256, ATTEND>), grid, dim3(256), shmem, s, qt, kt, vt, out_idx, out, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_attend_t(const Plan &pl, const void *q, const void *k, const void *v,
+                           const int32_t *idx, float *out, hipStream_t s) {
+    const FinishArgs a = finish_args(pl, nullptr);
+    const size_t shmem = (size_t)pl.cap * (sizeof(int32_t) + sizeof(float));
+    const dim3 grid((unsigned)pl.nqv);
+    const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v);
+    const bool wide = pl.nqv < kWideBelow && shmem + sizeof(AttendShared<1024, D, T>) <= 64 * 1024;
+    if (wide)
+        hipLaunchKernelGGL((attend_kernel<T, D, 1024>), grid, dim3(1024), shmem, s, qt, kt, vt, idx, out, a);
+    else
+        hipLaunchKernelGGL((attend_kernel<T, D, 256>), grid, dim3(256), shmem, s, qt, kt, vt, idx, out, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_finish(const Plan &pl, const void *ws, const void *q, const void *k,
+                         const void *v, int32_t *out_idx, float *out, hipStream_t s) {
+    const bool attend = out != nullptr;
+#define CA_FIN(T, D) (attend ? launch_finish_t<T, D, true>(pl, ws, q, k, v, out_idx, out, s) \
+                             : launch_finish_t<T, D, false>(pl, ws, q, k, v, out_idx, out, s))
+    if (pl.dtype == 1) return pl.d == 128 ? CA_FIN(__bf16, 128) : CA_FIN(__bf16, 64);
+    return pl.d == 128 ? CA_FIN(float, 128) : CA_FIN(float, 64);
+#undef CA_FIN
+}
+
+hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k, const void *v,
+                                    const int32_t *idx, float *out, hipStream_t s) {
+    if (pl.dtype == 1)
+        return pl.d == 128 ? launch_attend_t<__bf16, 128>(pl, q, k, v, idx, out, s)
+                           : launch_attend_t<__bf16, 64>(pl, q, k, v, idx, out, s);
+    return pl.d == 128 ? launch_attend_t<float, 128>(pl, q, k, v, idx, out, s)
+                       : launch_attend_t<float, 64>(pl, q, k, v, idx, out, s);
+}
+
+}  // namespace ca

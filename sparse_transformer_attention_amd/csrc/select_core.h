@@ -1,0 +1,134 @@
+// Exact wavefront-level top-k selection on 64-bit ranking keys, shared by the score and finish
+// kernels. A ranking key orders candidates the way the top-k part of the condensate set does
+// (pages of "The Condensate Theorem", metaphor-xennon blog, section 2.2.3): higher score first,
+// and on equal scores the smaller position first:
+//     key = (score_key(s) << 32) | ~j,
+// so keys of distinct positions are distinct and the order is total. 0 marks an empty slot
+// (every real key has a high word >= 0x00800000).
+#pragma once
+
+#include "device_utils.h"
+
+namespace ca {
+
+// Exclusive prefix sum over the lanes of a wavefront; *total gets the wavefront sum.
+__device__ __forceinline__ int wave_excl_scan(int x, int *total) {
+    const uint32_t incl = wave_incl_scan_u32((uint32_t)x);
+    *total = (int)__builtin_amdgcn_readlane(incl, 63);
+    return (int)incl - x;
+}
+
+__device__ __forceinline__ uint64_t make_rank_key(uint32_t skey, uint32_t pos) {
+    return ((uint64_t)skey << 32) | (uint32_t)(~pos);
+}
+__device__ __forceinline__ int32_t rank_key_pos(uint64_t key) { return (int32_t)(~(uint32_t)key); }
+
+// One wavefront keeps the `keep` largest of the distinct non-zero keys kr[0..E) of its lanes
+// (0 = empty) and writes them to dst[0..min(keep, count)) in any order. dst may be the keys'
+// own source: every lane holds its keys in registers before anything is written. Radix select
+// (8-bit digits, starting at the highest bit where the keys differ) with a 320-word LDS
+// histogram per wavefront (words 256 + lane absorb keys outside the current prefix).
+// Returns the high word of the smallest kept key (0xFFFFFFFF if none is kept). With
+// dst == nullptr nothing is written: only that high word is computed.
+template <int E>
+__device__ __forceinline__ uint32_t wave_keep_top_u64(const uint64_t (&kr)[E], int keep,
+                                                      uint32_t *hist, uint64_t *dst) {
+    const int lane = threadIdx.x & 63;
+    int nz = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) nz += kr[e] != 0ull;
+    int total;
+    (void)wave_excl_scan(nz, &total);
+    uint64_t prefix = 0ull, mask = 0ull;
+    if (keep < total) {
+        uint32_t hmax = 0u, hmin = 0xFFFFFFFFu;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t hi = (uint32_t)(kr[e] >> 32);
+            if (kr[e]) { hmax = hi > hmax ? hi : hmax; hmin = hi < hmin ? hi : hmin; }
+        }
+        hmax = wave_max_u32_dpp(hmax);
+        hmin = wave_min_u32_dpp(hmin);
+        int hb;
+        uint32_t lmax = 0u;
+        if (hmax != hmin) {
+            hb = 32 + 31 - __builtin_clz(hmax ^ hmin);
+        } else {
+            uint32_t lmin = 0xFFFFFFFFu;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint32_t lo = (uint32_t)kr[e];
+                if (kr[e]) { lmax = lo > lmax ? lo : lmax; lmin = lo < lmin ? lo : lmin; }
+            }
+            lmax = wave_max_u32_dpp(lmax);
+            lmin = wave_min_u32_dpp(lmin);
+            hb = 31 - __builtin_clz((lmax ^ lmin) | 1u);
+        }
+        // Bits above hb are common to every key. (A 64-bit shift by 64 is undefined: hb == 63
+        // whenever the scores have both signs.)
+        mask = hb >= 63 ? 0ull : (~0ull << (hb + 1));
+        prefix = (((uint64_t)hmax << 32) | lmax) & mask;
+        int rem = keep;
+        while (hb >= 0) {
+            const int lb = hb >= 7 ? hb - 7 : 0;
+            const uint32_t dmask = (2u << (hb - lb)) - 1u;
+            reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0, 0, 0, 0);
+            wave_sync();
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint64_t key = kr[e];
+                const bool in = key != 0ull && (key & mask) == prefix;
+                atomicAdd(&hist[in ? (uint32_t)(key >> lb) & dmask : 256u + lane], 1u);
+            }
+            wave_sync();
+            const uint4 h = reinterpret_cast<const uint4 *>(hist)[lane];  // bins 4l..4l+3
+            const uint32_t own = h.x + h.y + h.z + h.w;
+            const uint32_t pre = wave_incl_scan_u32(own);
+            const uint32_t all = __builtin_amdgcn_readlane(pre, 63);
+            const uint32_t excl = all - pre, incl = excl + own;  // keys in bins >= 4l+4, >= 4l
+            const uint32_t c3 = excl + h.w, c2 = c3 + h.z, c1 = c2 + h.y, c0 = incl;
+            const uint32_t r = (uint32_t)rem;
+            const bool mine = (incl >= r) && (excl < r);
+            const int u = (c3 >= r) ? 3 : (c2 >= r) ? 2 : (c1 >= r) ? 1 : 0;
+            const uint32_t hd = (u == 3) ? h.w : (u == 2) ? h.z : (u == 1) ? h.y : h.x;
+            const uint32_t cd = (u == 3) ? c3 : (u == 2) ? c2 : (u == 1) ? c1 : c0;
+            int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+            src = src < 0 ? 0 : src;
+            const uint32_t digit = __builtin_amdgcn_readlane((uint32_t)(4 * lane + u), src);
+            const uint32_t h_digit = __builtin_amdgcn_readlane(hd, src);
+            const uint32_t above = __builtin_amdgcn_readlane(cd - hd, src);
+            rem -= (int)above;
+            prefix |= (uint64_t)digit << lb;
+            mask |= (uint64_t)dmask << lb;
+            wave_sync();
+            if (h_digit == (uint32_t)rem) break;  // distinct keys: reached by the last digit
+            hb = lb - 1;
+        }
+    }
+    const int lim = keep < total ? keep : total;
+    int cnt = 0;
+    uint32_t tmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const bool sel = kr[e] != 0ull && (kr[e] & mask) >= prefix;
+        cnt += sel;
+        const uint32_t hi = (uint32_t)(kr[e] >> 32);
+        tmin = (sel && hi < tmin) ? hi : tmin;
+    }
+    if (dst != nullptr) {
+        int tot;
+        int pos = wave_excl_scan(cnt, &tot);
+        wave_sync();  // every lane holds its keys before dst (possibly their source) is written
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (kr[e] != 0ull && (kr[e] & mask) >= prefix) {
+                if (pos < lim) dst[pos] = kr[e];
+                ++pos;
+            }
+        }
+        wave_sync();
+    }
+    return wave_min_u32_dpp(tmin);
+}
+
+}  // namespace ca

@@ -68,7 +68,8 @@ BAD = [
     (dict(W=4000, topk=96), ca.CA_ERR_UNSUPPORTED, "exceeds"),
     (dict(chunk=300), ca.CA_ERR_INVALID_ARG, "chunk"),
     (dict(chunk=128), ca.CA_ERR_INVALID_ARG, "chunk"),
-    (dict(chunk=8192), ca.CA_ERR_INVALID_ARG, "chunk"),
+    (dict(chunk=2048), ca.CA_ERR_INVALID_ARG, "chunk"),
+    (dict(topk=513, W=16), ca.CA_ERR_UNSUPPORTED, "topk"),
 ]
 
 
@@ -115,7 +116,7 @@ def test_workspace_size_rules(lib):
     sizes = [ws_size(good(n=n))[1] for n in (4096, 65536, 131072, 1 << 20)]
     assert sizes == sorted(sizes)
     assert ws_size(good(nq=8, n=131072))[1] >= ws_size(good(nq=1, n=131072))[1]
-    # An explicit chunk is honoured: halving it doubles the candidate slots.
-    a = ws_size(good(chunk=1024))[1]
-    b = ws_size(good(chunk=512))[1]
-    assert b == 2 * a
+    # Every valid chunk gives a usable plan.
+    for c in (0, 256, 512, 1024):
+        assert ws_size(good(chunk=c))[0] == ca.CA_OK
+    assert ws_size(good(topk=512, W=16))[0] == ca.CA_OK

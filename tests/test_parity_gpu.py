@@ -103,7 +103,7 @@ def test_attention_on_subset_any_order_and_padding():
     assert torch.count_nonzero(out).item() == 0
 
 
-@pytest.mark.parametrize("chunk", [256, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("chunk", [256, 512, 1024])
 def test_chunk_size_does_not_change_results(chunk):
     w = W_(heads=8, kv_heads=2, n=9000, nq=2, W=64, topk=48)
     x = synth.make_inputs(w, seed=5)
