@@ -34,6 +34,13 @@ struct Plan {
     int64_t lmax;         // candidate slots per query (wpu * topk)
     size_t lists_offset;  // byte offset of the lists in the workspace
     size_t ws_bytes;      // total workspace
+    // Decode path (score_keys + filter): key rows per unit, blocks of 256 rows per unit, and
+    // the offsets of the key buffer [units][rstride][G] and block maxima [units][nblk][G]. The
+    // segments are then filter splits of 1024 rows (wpu per query).
+    bool stream;
+    int64_t rstride;
+    int nblk;
+    size_t keys_offset, bmax_offset;
 };
 
 // Launchers (enqueue only; return the hipError_t of the last launch).
@@ -47,5 +54,8 @@ hipError_t launch_finish(const Plan &pl, const void *ws, const void *q, const vo
 hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k, const void *v,
                                     const int32_t *idx, float *out, hipStream_t s);
 size_t topk_lds_bytes(const Plan &pl);
+hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s);
+hipError_t launch_filter(const Plan &pl, void *ws, hipStream_t s);
+size_t stream_keys_bytes(const Plan &pl);
 
 }  // namespace ca

@@ -44,6 +44,11 @@ __device__ __forceinline__ float dpp_half_mirror(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
 }
 
+// Value of the lane at the mirrored position within each group of 16 (lane i <-> 15 - i).
+__device__ __forceinline__ float dpp_mirror16(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+}
+
 // Order-preserving map of a float32 score to uint32 (larger score -> larger key); -0 is
 // folded onto +0 so that equal scores give equal keys. Every finite score maps to a key
 // >= 0x00800000, so 0 is free to mean "no candidate".

@@ -1,0 +1,85 @@
+// Key-row scoring shared by the score kernels on gfx950: each K row is read with 16-byte
+// loads, LPR lanes per row (whole 128-byte lines per instruction), the lane's slices are dotted
+// with the same slices of G query rows in fp32 (bf16 dot2 or fp32 FMA), and DPP exchanges sum
+// the LPR partial products of a row (pages of "The Condensate Theorem", metaphor-xennon blog,
+// section 2.1: the scores q_i . k_j of every causal key).
+#pragma once
+
+#include "device_utils.h"
+
+namespace ca {
+
+// Loads the K rows of one streaming round: row groups gi0 + 4*uu (RPG = 64/LPR rows each, LPR
+// lanes per row) of the chunk [r0, rend). Rows past the chunk's end are clamped to its last row
+// (loaded, never used), so every load is unconditional.
+template <int LPR, int P, int U>
+__device__ __forceinline__ void load_round(const uint4 *__restrict__ kbase, int r0, int rend, int gi0,
+                                           int lane, uint4 (&dst)[U][P]) {
+    constexpr int RQ = P * LPR;      // 16-byte words per row
+    constexpr int RPG = 64 / LPR;    // rows per wavefront load
+    const int sl = lane % LPR;
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) {
+        int row = r0 + (gi0 + 4 * uu) * RPG + lane / LPR;
+        row = row < rend ? row : rend - 1;
+        const uint4 *src = kbase + (int64_t)row * RQ;
+#pragma unroll
+        for (int p = 0; p < P; ++p) dst[uu][p] = src[p * LPR + sl];
+    }
+}
+
+// Sum of the G partial dot products over the LPR lanes of a row. Each exchange halves the
+// queries a lane carries while it carries several, so the result has G lanes per row, one per
+// query: query (lane % LPR) / (LPR / G) of the row.
+template <int LPR, int G>
+__device__ __forceinline__ float reduce_row(const float (&acc)[G], int lane) {
+    if constexpr (LPR == 16) {
+        const bool lo = (lane & 8) == 0;
+        if constexpr (G == 4) {
+            const float k0 = lo ? acc[0] : acc[2], s0 = lo ? acc[2] : acc[0];
+            const float k1 = lo ? acc[1] : acc[3], s1 = lo ? acc[3] : acc[1];
+            const float a0 = k0 + dpp_mirror16(s0);
+            const float a1 = k1 + dpp_mirror16(s1);
+            const bool b4 = (lane & 4) != 0;
+            float x = (b4 ? a1 : a0) + dpp_half_mirror(b4 ? a0 : a1);
+            x += dpp_xor2(x);
+            return x + dpp_xor1(x);
+        } else if constexpr (G == 2) {
+            float x = (lo ? acc[0] : acc[1]) + dpp_mirror16(lo ? acc[1] : acc[0]);
+            x += dpp_half_mirror(x);
+            x += dpp_xor2(x);
+            return x + dpp_xor1(x);
+        } else {
+            float x = acc[0] + dpp_mirror16(acc[0]);
+            x += dpp_half_mirror(x);
+            x += dpp_xor2(x);
+            return x + dpp_xor1(x);
+        }
+    } else {
+        const bool hi = (lane & 4) != 0;
+        if constexpr (G == 4) {
+            const float k0 = hi ? acc[2] : acc[0], s0 = hi ? acc[0] : acc[2];
+            const float k1 = hi ? acc[3] : acc[1], s1 = hi ? acc[1] : acc[3];
+            const float a0 = k0 + dpp_half_mirror(s0);
+            const float a1 = k1 + dpp_half_mirror(s1);
+            const bool hi1 = (lane & 2) != 0;
+            const float b0 = (hi1 ? a1 : a0) + dpp_xor2(hi1 ? a0 : a1);
+            return b0 + dpp_xor1(b0);
+        } else if constexpr (G == 2) {
+            float x = (hi ? acc[1] : acc[0]) + dpp_half_mirror(hi ? acc[0] : acc[1]);
+            x += dpp_xor2(x);
+            return x + dpp_xor1(x);
+        } else {
+            float x = acc[0] + dpp_half_mirror(acc[0]);
+            x += dpp_xor2(x);
+            return x + dpp_xor1(x);
+        }
+    }
+}
+
+// Adds the NS (key, row) results a lane holds to its query's running list. First chunk of a
+// unit (direct): the lists are empty and there is no threshold yet, so the key of row r goes to
+// position r - row0 (0 when r is no candidate of the query). Otherwise the keys that reach the
+// query's threshold are appended: one LDS atomic per query and call, positions from the
+// ballots.
+}  // namespace ca

@@ -131,4 +131,126 @@ __device__ __forceinline__ uint32_t wave_keep_top_u64(const uint64_t (&kr)[E], i
     return wave_min_u32_dpp(tmin);
 }
 
+// A high word that at least `keep` of the wavefront's non-zero values v[0..E) reach, close to
+// their keep-th largest: the lower edge of the 8-bit radix bin, over the highest bits where
+// the values differ, that holds the keep-th largest value (one histogram pass). 0 when there
+// are fewer than `keep` values.
+template <int E>
+__device__ __forceinline__ uint32_t wave_bound_u32(const uint32_t (&v)[E], int keep, uint32_t *hist) {
+    const int lane = threadIdx.x & 63;
+    int nz = 0;
+    uint32_t hmax = 0u, hmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (v[e]) { ++nz; hmax = v[e] > hmax ? v[e] : hmax; hmin = v[e] < hmin ? v[e] : hmin; }
+    }
+    int total;
+    (void)wave_excl_scan(nz, &total);
+    if (keep < 1 || total < keep) return 0u;
+    hmax = wave_max_u32_dpp(hmax);
+    hmin = wave_min_u32_dpp(hmin);
+    if (hmax == hmin) return hmax;
+    const int hb = 31 - __builtin_clz(hmax ^ hmin);
+    const int lb = hb >= 7 ? hb - 7 : 0;
+    const uint32_t dmask = (2u << (hb - lb)) - 1u;
+    reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0, 0, 0, 0);
+    wave_sync();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (v[e]) atomicAdd(&hist[(v[e] >> lb) & dmask], 1u);
+    wave_sync();
+    const uint4 h = reinterpret_cast<const uint4 *>(hist)[lane];  // bins 4l..4l+3
+    const uint32_t own = h.x + h.y + h.z + h.w;
+    const uint32_t pre = wave_incl_scan_u32(own);
+    const uint32_t all = __builtin_amdgcn_readlane(pre, 63);
+    const uint32_t excl = all - pre;  // values in bins >= 4l+4
+    const uint32_t c3 = excl + h.w, c2 = c3 + h.z, c1 = c2 + h.y, c0 = c1 + h.x;
+    const uint32_t r = (uint32_t)keep;
+    const bool mine = (c0 >= r) && (excl < r);
+    const int u = (c3 >= r) ? 3 : (c2 >= r) ? 2 : (c1 >= r) ? 1 : 0;
+    int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+    src = src < 0 ? 0 : src;
+    const uint32_t digit = __builtin_amdgcn_readlane((uint32_t)(4 * lane + u), src);
+    wave_sync();
+    const uint32_t pfx = hb >= 31 ? 0u : (hmax >> (hb + 1)) << (hb + 1);
+    return pfx | (digit << lb);
+}
+
+// One wavefront thins its distinct non-zero keys kr[0..E) (0 = empty) to those whose high word
+// reaches the 8-bit radix bin that holds the keep-th largest high word: at least `keep` keys,
+// usually a few more. One histogram pass over the highest differing bits of the high words
+// replaces the full select. The kept keys go to dst[0..count) in any order (dst may be their
+// source). If the kept set would exceed `limit` keys, or every high word is the same, it falls
+// back to the exact top-keep. Returns the number kept; *thr gets a high word that at least
+// `keep` kept keys reach (0 when there are no more than `keep` keys).
+template <int E>
+__device__ __forceinline__ int wave_thin_u64(const uint64_t (&kr)[E], int keep, int limit, uint32_t *hist,
+                                             uint64_t *dst, uint32_t *thr) {
+    const int lane = threadIdx.x & 63;
+    int nz = 0;
+    uint32_t hmax = 0u, hmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t hi = (uint32_t)(kr[e] >> 32);
+        if (kr[e]) { ++nz; hmax = hi > hmax ? hi : hmax; hmin = hi < hmin ? hi : hmin; }
+    }
+    int total;
+    (void)wave_excl_scan(nz, &total);
+    hmax = wave_max_u32_dpp(hmax);
+    hmin = wave_min_u32_dpp(hmin);
+    uint32_t t = 0u;
+    if (total > keep) {
+        if (hmax == hmin) {
+            *thr = wave_keep_top_u64(kr, keep, hist, dst);
+            return keep;
+        }
+        const int hb = 31 - __builtin_clz(hmax ^ hmin);
+        const int lb = hb >= 7 ? hb - 7 : 0;
+        const uint32_t dmask = (2u << (hb - lb)) - 1u;
+        reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0, 0, 0, 0);
+        wave_sync();
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (kr[e]) atomicAdd(&hist[((uint32_t)(kr[e] >> 32) >> lb) & dmask], 1u);
+        wave_sync();
+        const uint4 h = reinterpret_cast<const uint4 *>(hist)[lane];  // bins 4l..4l+3
+        const uint32_t own = h.x + h.y + h.z + h.w;
+        const uint32_t pre = wave_incl_scan_u32(own);
+        const uint32_t all = __builtin_amdgcn_readlane(pre, 63);
+        const uint32_t excl = all - pre;  // keys in bins >= 4l+4
+        const uint32_t c3 = excl + h.w, c2 = c3 + h.z, c1 = c2 + h.y, c0 = c1 + h.x;
+        const uint32_t r = (uint32_t)keep;
+        const bool mine = (c0 >= r) && (excl < r);
+        const int u = (c3 >= r) ? 3 : (c2 >= r) ? 2 : (c1 >= r) ? 1 : 0;
+        const uint32_t cd = (u == 3) ? c3 : (u == 2) ? c2 : (u == 1) ? c1 : c0;
+        int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+        src = src < 0 ? 0 : src;
+        const uint32_t digit = __builtin_amdgcn_readlane((uint32_t)(4 * lane + u), src);
+        const uint32_t kept = __builtin_amdgcn_readlane(cd, src);
+        wave_sync();
+        if ((int)kept > limit) {
+            *thr = wave_keep_top_u64(kr, keep, hist, dst);
+            return keep;
+        }
+        const uint32_t pfx = hb >= 31 ? 0u : (hmax >> (hb + 1)) << (hb + 1);
+        t = pfx | (digit << lb);
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cnt += kr[e] != 0ull && (uint32_t)(kr[e] >> 32) >= t;
+    int tot;
+    int pos = wave_excl_scan(cnt, &tot);
+    wave_sync();  // every lane holds its keys before dst (possibly their source) is written
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (kr[e] != 0ull && (uint32_t)(kr[e] >> 32) >= t) {
+            dst[pos] = kr[e];
+            ++pos;
+        }
+    }
+    wave_sync();
+    *thr = t;
+    return tot;
+}
+
 }  // namespace ca

@@ -8,18 +8,20 @@
 // of the unit's candidate range {1..max_i (i-W)} are cut into chunks of `chunk` rows; the wpu
 // workgroups serving a unit take every wpu-th chunk.
 // For each chunk the workgroup streams the K rows once (16-byte loads, 8 lanes per row, whole
-// 128-byte lines per instruction), computes fp32 dot products for its G queries (bf16 dot2 or
-// fp32 FMA, DPP lane reductions), and keeps the score keys in LDS. Then wavefront t updates
-// query t's running list: keys below the admission threshold are dropped, the rest are added,
-// and a list longer than k is cut back to its exact top-k (radix select). The threshold is the
-// largest of the list's own k-th key and the k-th keys the unit's other workgroups have
-// published in their slots; every one of them is a lower bound of the query's final k-th key,
-// so no member of the final top-k is ever dropped. Each workgroup also publishes its best key;
-// the k'-th largest of those (distinct keys, one per workgroup) is a lower bound too, and a much
-// tighter one. At the end each workgroup writes the keys of its list that reach the best bound
-// it can see, and their count, to its own segment. No two workgroups write the same word, so
-// nothing waits on a contended atomic.
+// 128-byte lines per instruction) and computes fp32 dot products for its G queries (bf16 dot2 or
+// fp32 FMA, DPP lane reductions). A score that reaches its query's admission threshold is added
+// to the query's running list in LDS at once (one LDS counter per query, one atomic per
+// wavefront and query). At the end of a chunk, wavefront t looks after query t's list: a list
+// that might not take another chunk is cut back to its exact top-k (radix select), and the
+// threshold is raised to the largest of the list's own k-th key and the bounds the unit's other
+// workgroups have published. Every one of those is a lower bound of the query's final k-th key,
+// so no member of the final top-k is ever dropped: each workgroup publishes the k-th key of its
+// list and its best key, and the k'-th largest of the best keys (distinct keys, one per
+// workgroup) is a tight bound. At the end each workgroup writes the keys of its list that reach
+// the best bound it can see (at most k), and their count, to its own segment. No two
+// workgroups write the same word, so nothing waits on a contended atomic.
 #include "ca_internal.h"
+#include "score_core.h"
 #include "select_core.h"
 
 namespace ca {
@@ -47,52 +49,85 @@ __device__ __forceinline__ uint32_t load_slot(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Loads the K rows of one streaming round: row groups gi0 + 4*uu (8 rows each) of the chunk
-// [r0, rend). Rows past the chunk's end are clamped to its last row (loaded, never used), so
-// every load is unconditional.
-template <int P, int U>
-__device__ __forceinline__ void load_round(const uint4 *__restrict__ kbase, int r0, int rend, int gi0,
-                                           int lane, uint4 (&dst)[U][P]) {
-    constexpr int RQ = P * 8;  // 16-byte words per row
-    const int s = lane & 7;
+template <int G, int NS>
+__device__ __forceinline__ void emit_keys(const uint32_t (&keyv)[NS], const int (&rowv)[NS], bool direct,
+                                          uint32_t my_thr, bool writer, int my_t, int my_rlast, int row0,
+                                          int rows_end, const uint64_t (&qmask)[G], uint64_t my_mask,
+                                          uint32_t *rcnt, uint64_t *run, int rcap, int lane) {
+    uint64_t *dst = run + (size_t)my_t * rcap;
+    if (direct) {
 #pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-        int row = r0 + (gi0 + 4 * uu) * 8 + (lane >> 3);
-        row = row < rend ? row : rend - 1;
-        const uint4 *src = kbase + (int64_t)row * RQ;
+        for (int e = 0; e < NS; ++e)
+            if (writer && rowv[e] < rows_end)
+                dst[rowv[e] - row0] = rowv[e] <= my_rlast ? make_rank_key(keyv[e], (uint32_t)rowv[e]) : 0ull;
+        return;
+    }
+    uint64_t bal[NS];
+    uint64_t any = 0ull;
 #pragma unroll
-        for (int p = 0; p < P; ++p) dst[uu][p] = src[p * 8 + s];
+    for (int e = 0; e < NS; ++e) {
+        bal[e] = __ballot(writer && rowv[e] < rows_end && rowv[e] <= my_rlast && keyv[e] >= my_thr);
+        any |= bal[e];
+    }
+    if (any == 0ull) return;
+    uint32_t off = 0u;
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+        uint32_t cnt_t = 0u;
+#pragma unroll
+        for (int e = 0; e < NS; ++e) cnt_t += (uint32_t)__popcll(bal[e] & qmask[t]);
+        if (cnt_t != 0u) {
+            uint32_t b0 = 0u;
+            if (lane == 0) b0 = atomicAdd(&rcnt[t], cnt_t);
+            b0 = __builtin_amdgcn_readlane(b0, 0);
+            off = (my_t == t) ? b0 : off;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < NS; ++e) {
+        const uint64_t m = bal[e] & my_mask;
+        if ((m >> lane) & 1ull) dst[off + lanes_below(m)] = make_rank_key(keyv[e], (uint32_t)rowv[e]);
+        off += (uint32_t)__popcll(m);
     }
 }
 
 template <typename T, int D, int G, int RE>
-__global__ __launch_bounds__(256) void score_topk_kernel(const T *__restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RE <= 12 ? 4 : 2))) void score_topk_kernel(const T *__restrict__ q,
                                                          const T *__restrict__ k, TopkArgs a) {
-    // LDS: keys32 [G][chunk], run [G][rcap] (u64), hist [4][320], query rows [G][D] (T)
+    // LDS: run [G][rcap] (u64), hist [4][320], query rows [G][D] (T), list lengths [G],
+    // admission thresholds [G].
     extern __shared__ __align__(16) uint32_t smem[];
     constexpr int EB = sizeof(T);
-    constexpr int RB = D * EB;          // bytes per key row
-    constexpr int P = RB / 128;         // 16-byte loads per lane per row (8 lanes per row)
-    constexpr int U = 8 / P;            // row groups (8 rows each) per wavefront round
-    // RE: run keys per lane during a cut (rcap == 64 * RE)
+    constexpr int RB = D * EB;               // bytes per key row
+    constexpr int LPR = RB >= 256 ? 16 : 8;  // lanes per row
+    constexpr int RPG = 64 / LPR;            // rows per wavefront load
+    constexpr int P = RB / (16 * LPR);       // 16-byte loads per lane per row
+    constexpr int U = 8 / P;                 // row groups per wavefront round (8 loads per lane)
+    // RE: run keys per lane during a cut (rcap <= 64 * RE)
     static_assert(G == 1 || G == 2 || G == 4, "G");
-    static_assert(P >= 1, "rows of at least 128 bytes");
+    static_assert(P >= 1 && P * U == 8, "rows of at least 128 bytes");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int CH = a.chunk;
-    const int cut_at = a.rcap - CH;  // a longer list could not take another chunk
-    uint32_t *keys32 = smem;
-    uint64_t *run = reinterpret_cast<uint64_t *>(smem + G * CH);
-    uint32_t *hist = smem + G * CH + 2 * G * a.rcap + wave * 320;
-    uint4 *qs = reinterpret_cast<uint4 *>(smem + G * CH + 2 * G * a.rcap + 4 * 320);  // [G][RB/16]
+    const int cut_at = a.rcap - CH;  // a longer list might not take another chunk
+    uint64_t *run = reinterpret_cast<uint64_t *>(smem);
+    uint32_t *hist = smem + 2 * G * a.rcap + wave * 320;
+    uint4 *qs = reinterpret_cast<uint4 *>(smem + 2 * G * a.rcap + 4 * 320);
+    uint32_t *rcnt = smem + 2 * G * a.rcap + 4 * 320 + G * RB / 4;
+    uint32_t *thr_s = rcnt + G;
     const int64_t nvec = (int64_t)a.g * a.nq;  // query vectors per KV head
-    const int s = lane & 7;
-    // After the 8-lane reduction the even lanes own one query's score each: query
-    // 2*bit2 + bit1 of the lane (G == 4); lanes 0 and 4 of 8 own queries 0 and 1 (G == 2);
-    // lane 0 of 8 owns query 0 (G == 1).
-    const int my_t = (G == 4) ? (((lane >> 2) & 1) * 2 + ((lane >> 1) & 1)) : (G == 2) ? ((lane >> 2) & 1) : 0;
-    const bool writer = (G == 4) ? ((lane & 1) == 0) : (G == 2) ? ((lane & 3) == 0) : ((lane & 7) == 0);
+    const int sl = lane % LPR;
+    // After the row reduction lane sl of a row holds the score of query sl / (LPR / G); the
+    // first lane of each such run writes it.
+    const bool writer = sl % (LPR / G) == 0;
+    const int my_t = sl / (LPR / G);
+    uint64_t qmask[G];  // writer lanes of each query
+#pragma unroll
+    for (int t = 0; t < G; ++t) qmask[t] = __ballot(writer && my_t == t);
+    uint64_t my_mask = qmask[0];  // writer lanes of this lane's query
+#pragma unroll
+    for (int t = 1; t < G; ++t) my_mask = (my_t == t) ? qmask[t] : my_mask;
 
     const bool shared_unit = a.wpu > 1;
     const int member = shared_unit ? (int)(blockIdx.x % a.wpu) : 0;
@@ -123,10 +158,11 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const T *__restrict__ q
             }
             qs[t * (RB / 16) + w16] = v;
         }
+        if (tid < G) { rcnt[tid] = 0u; thr_s[tid] = 0u; }
         __syncthreads();
-        int64_t my_rlast = rlast[0];
+        int my_rlast = (int)rlast[0];
 #pragma unroll
-        for (int t = 1; t < G; ++t) my_rlast = (my_t == t) ? rlast[t] : my_rlast;
+        for (int t = 1; t < G; ++t) my_rlast = (my_t == t) ? (int)rlast[t] : my_rlast;
         // Wavefront t owns query t of the unit: its running list and thresholds.
         const int64_t w_idx = grp * G + wave;
         const bool w_query = wave < G && w_idx < nvec;
@@ -137,11 +173,11 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const T *__restrict__ q
         uint64_t *w_run = run + (size_t)(wave < G ? wave : 0) * a.rcap;
         uint32_t *w_tau = a.tau + w_qv * a.wpu;
         uint32_t *w_top = a.top + w_qv * a.wpu;
-        // The first kq workgroups' best keys are kq distinct candidates: their minimum is a
-        // lower bound of the k-th key once all of them have published.
-        const bool use_min_bound = shared_unit && kq >= 1 && kq <= 64 && kq <= nread;
-        int rc = 0;             // keys in the running list
-        uint32_t tau_loc = 0u;  // high word of its k-th key once it has been cut back
+        // Published best keys are distinct candidates: once at least kq workgroups have
+        // published one, the smallest of them is a lower bound of the k-th key.
+        const bool use_min_bound = shared_unit && kq >= 1 && kq <= nread;
+        int rc_seen = 0;        // list entries already scanned for the best key
+        uint32_t tau_loc = 0u;  // high word of the list's k-th key once it has been cut back
         uint32_t tau_pub = 0u;  // k-th key published
         uint32_t best_loc = 0u; // best key seen
         uint32_t top_pub = 0u;  // best key published
@@ -149,30 +185,31 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const T *__restrict__ q
         const uint4 *kbase = reinterpret_cast<const uint4 *>(k + (int64_t)bk * a.n * D);
         int64_t c = member;
         while (1 + c * CH <= rl_max) {
-            const int64_t row0 = 1 + c * CH;
-            const int64_t rows_end = (row0 + CH < rl_max + 1) ? row0 + CH : rl_max + 1;
-            const int nrows = (int)(rows_end - row0);
-            const int64_t cn = c + a.wpu;
+            const int row0 = (int)(1 + c * CH);
+            const int rows_end = (int)((row0 + CH < rl_max + 1) ? row0 + CH : rl_max + 1);
             // Published bounds: requested now, reduced after the chunk's stream.
-            uint32_t sl0 = 0u, sl1 = 0u, sb = 0xFFFFFFFFu;
+            uint32_t sl0 = 0u, sl1 = 0u, sb0 = 0u, sb1 = 0u;
             if (w_query && shared_unit) {
                 if (lane < nread) sl0 = load_slot(w_tau + lane);
                 if (lane + 64 < nread) sl1 = load_slot(w_tau + lane + 64);
-                if (use_min_bound && lane < kq) sb = load_slot(w_top + lane);
+                if (use_min_bound && lane < nread) sb0 = load_slot(w_top + lane);
+                if (use_min_bound && lane + 64 < nread) sb1 = load_slot(w_top + lane + 64);
             }
-
+            const uint32_t my_thr = thr_s[my_t];
+            const bool direct = c == member;
             uint4 qr[G][P];  // this lane's slices of the queries
 #pragma unroll
             for (int t = 0; t < G; ++t)
 #pragma unroll
-                for (int p = 0; p < P; ++p) qr[t][p] = qs[t * (RB / 16) + p * 8 + s];
-            const int ngroups = (nrows + 7) >> 3;  // 8 rows per wavefront step
+                for (int p = 0; p < P; ++p) qr[t][p] = qs[t * (RB / 16) + p * LPR + sl];
+            const int ngroups = (rows_end - row0 + RPG - 1) / RPG;  // RPG rows per wavefront load
             for (int gi0 = wave; gi0 < ngroups; gi0 += 4 * U) {
                 uint4 kr[U][P];
-                load_round<P, U>(kbase, (int)row0, (int)rows_end, gi0, lane, kr);
+                load_round<LPR, P, U>(kbase, row0, rows_end, gi0, lane, kr);
+                uint32_t keyv[U];
+                int rowv[U];
 #pragma unroll
                 for (int uu = 0; uu < U; ++uu) {
-                    const int gi = gi0 + 4 * uu;
                     float acc[G];
 #pragma unroll
                     for (int t = 0; t < G; ++t) {
@@ -181,110 +218,70 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const T *__restrict__ q
                         for (int p = 0; p < P; ++p) x = dot16(kr[uu][p], qr[t][p], x, T());
                         acc[t] = x;
                     }
-                    // Sum over the 8 lanes of the row, halving the queries per lane at each
-                    // exchange while there are several.
-                    float score;
-                    if constexpr (G == 4) {
-                        const bool hi = (lane & 4) != 0;
-                        const float k0 = hi ? acc[2] : acc[0], s0 = hi ? acc[0] : acc[2];
-                        const float k1 = hi ? acc[3] : acc[1], s1 = hi ? acc[1] : acc[3];
-                        const float a0 = k0 + dpp_half_mirror(s0);
-                        const float a1 = k1 + dpp_half_mirror(s1);
-                        const bool hi1 = (lane & 2) != 0;
-                        const float kk = hi1 ? a1 : a0, ss = hi1 ? a0 : a1;
-                        const float b0 = kk + dpp_xor2(ss);
-                        score = b0 + dpp_xor1(b0);
-                    } else if constexpr (G == 2) {
-                        const bool hi = (lane & 4) != 0;
-                        const float kk = hi ? acc[1] : acc[0], ss = hi ? acc[0] : acc[1];
-                        float a0 = kk + dpp_half_mirror(ss);
-                        a0 += dpp_xor2(a0);
-                        score = a0 + dpp_xor1(a0);
-                    } else {
-                        float a0 = acc[0] + dpp_half_mirror(acc[0]);
-                        a0 += dpp_xor2(a0);
-                        score = a0 + dpp_xor1(a0);
-                    }
-                    const int rr = gi * 8 + (lane >> 3);
-                    if (writer && rr < nrows)
-                        keys32[my_t * CH + rr] = (row0 + rr <= my_rlast) ? score_key(score) : 0u;
+                    keyv[uu] = score_key(reduce_row<LPR, G>(acc, lane));
+                    rowv[uu] = row0 + (gi0 + 4 * uu) * RPG + lane / LPR;
                 }
+                emit_keys<G, U>(keyv, rowv, direct, my_thr, writer, my_t, my_rlast, row0, rows_end,
+                                qmask, my_mask, rcnt, run, a.rcap, lane);
             }
             __syncthreads();
 
-            // Running-list update of query `wave`.
+            // End of chunk: query `wave`'s list.
             if (w_query) {
-                const int64_t vend = (rows_end < w_rlast + 1) ? rows_end : w_rlast + 1;
-                const int nvalid = vend > row0 ? (int)(vend - row0) : 0;
-                if (nvalid > 0) {
-                    uint32_t thr = wave_max_u32_dpp(sl0 > sl1 ? sl0 : sl1);
-                    thr = thr > tau_loc ? thr : tau_loc;
-                    if (use_min_bound) {
-                        const uint32_t mb = wave_min_u32_dpp(sb);
+                uint32_t thr = wave_max_u32_dpp(sl0 > sl1 ? sl0 : sl1);
+                if (use_min_bound) {
+                    int np;
+                    (void)wave_excl_scan((sb0 != 0u) + (sb1 != 0u), &np);
+                    if (np >= kq) {
+                        const uint32_t m0 = sb0 ? sb0 : 0xFFFFFFFFu, m1 = sb1 ? sb1 : 0xFFFFFFFFu;
+                        const uint32_t mb = wave_min_u32_dpp(m0 < m1 ? m0 : m1);
                         thr = thr > mb ? thr : mb;
                     }
-                    const uint32_t *kq32 = keys32 + wave * CH;
-                    int cnt = 0;
-                    uint32_t bmax = 0u;
-                    for (int e0 = 4 * lane; e0 < nvalid; e0 += 256) {
-                        const uint4 v = *reinterpret_cast<const uint4 *>(kq32 + e0);
-                        const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                        for (int t4 = 0; t4 < 4; ++t4) {
-                            const bool ok = e0 + t4 < nvalid && kv[t4] >= thr && kv[t4] != 0u;
-                            cnt += ok;
-                            bmax = (ok && kv[t4] > bmax) ? kv[t4] : bmax;
-                        }
-                    }
-                    int tot;
-                    int pos = rc + wave_excl_scan(cnt, &tot);
-                    if (tot > 0) {
-                        for (int e0 = 4 * lane; e0 < nvalid; e0 += 256) {
-                            const uint4 v = *reinterpret_cast<const uint4 *>(kq32 + e0);
-                            const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                            for (int t4 = 0; t4 < 4; ++t4) {
-                                if (e0 + t4 < nvalid && kv[t4] >= thr && kv[t4] != 0u) {
-                                    w_run[pos] = make_rank_key(kv[t4], (uint32_t)(row0 + e0 + t4));
-                                    ++pos;
-                                }
-                            }
-                        }
-                        rc += tot;
-                        bmax = wave_max_u32_dpp(bmax);
-                        best_loc = bmax > best_loc ? bmax : best_loc;
-                        if (rc > cut_at) {  // cut back to the exact top-k
-                            wave_sync();
-                            uint64_t kk[RE];
-#pragma unroll
-                            for (int e = 0; e < RE; ++e) {
-                                const int f = lane + 64 * e;
-                                kk[e] = f < rc ? w_run[f] : 0ull;
-                            }
-                            tau_loc = wave_keep_top_u64(kk, a.topk, hist, w_run);
-                            rc = a.topk;
-                        }
-                        if (shared_unit && lane == 0) {
-                            if (tau_loc > tau_pub)
-                                __hip_atomic_store(w_tau + member, tau_loc, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-                            if (best_loc > top_pub)
-                                __hip_atomic_store(w_top + member, best_loc, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                        tau_pub = tau_loc > tau_pub ? tau_loc : tau_pub;
-                        top_pub = best_loc > top_pub ? best_loc : top_pub;
-                    }
                 }
+                int rc = direct ? rows_end - row0 : (int)rcnt[wave];
+                if (rc > rc_seen) {
+                    uint32_t bmax = 0u;
+                    for (int f = rc_seen + lane; f < rc; f += 64) {
+                        const uint32_t hi = (uint32_t)(w_run[f] >> 32);
+                        bmax = hi > bmax ? hi : bmax;
+                    }
+                    bmax = wave_max_u32_dpp(bmax);
+                    best_loc = bmax > best_loc ? bmax : best_loc;
+                    if (rc > cut_at) {  // thin the list to about its top-k
+                        uint64_t kk[RE];
+#pragma unroll
+                        for (int e = 0; e < RE; ++e) {
+                            const int f = lane + 64 * e;
+                            kk[e] = f < rc ? w_run[f] : 0ull;
+                        }
+                        uint32_t tk;
+                        rc = wave_thin_u64(kk, a.topk, cut_at, hist, w_run, &tk);
+                        tau_loc = tk > tau_loc ? tk : tau_loc;
+                    }
+                    if (lane == 0) rcnt[wave] = (uint32_t)rc;
+                    rc_seen = rc;
+                    if (shared_unit && lane == 0) {
+                        if (tau_loc > tau_pub)
+                            __hip_atomic_store(w_tau + member, tau_loc, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                        if (best_loc > top_pub)
+                            __hip_atomic_store(w_top + member, best_loc, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    tau_pub = tau_loc > tau_pub ? tau_loc : tau_pub;
+                    top_pub = best_loc > top_pub ? best_loc : top_pub;
+                }
+                thr = thr > tau_loc ? thr : tau_loc;
+                if (lane == 0) thr_s[wave] = thr;
             }
-            __syncthreads();  // keys32 is rewritten for the next chunk
-            c = cn;
+            __syncthreads();  // lengths and thresholds are read by every wavefront
+            c += a.wpu;
         }
 
         // Leave the keys that reach the best visible bound (at most k of them), and their
         // count, in this workgroup's segment of the query.
         if (w_query) {
-            wave_sync();
+            int rc = (int)rcnt[wave];
             uint32_t thr = tau_loc;
             if (shared_unit) {
                 uint32_t t0 = 0u, t1 = 0u;
@@ -310,6 +307,8 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const T *__restrict__ q
                     thr = thr > tb ? thr : tb;
                 }
             }
+            // (0 entries are rows that are no candidate of the query: their high word is 0.)
+            thr = thr > 1u ? thr : 1u;
             int cnt = 0;
             for (int f = lane; f < rc; f += 64) cnt += (uint32_t)(w_run[f] >> 32) >= thr;
             int tot;
@@ -337,7 +336,6 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const T *__restrict__ q
                 }
             }
             if (lane == 0) a.cnt[w_qv * a.wpu + member] = (uint32_t)(tot < a.topk ? tot : a.topk);
-            // A later unit of this workgroup rereads the slots of another query only.
         }
         __syncthreads();  // LDS is reused by the next unit
     }
@@ -346,8 +344,8 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const T *__restrict__ q
 }  // namespace
 
 size_t topk_lds_bytes(const Plan &pl) {
-    return (size_t)pl.G * pl.chunk * sizeof(uint32_t) + (size_t)pl.G * pl.rcap * sizeof(uint64_t) +
-           4 * 320 * sizeof(uint32_t) + (size_t)pl.G * pl.d * (pl.dtype == 1 ? 2 : 4);
+    return (size_t)pl.G * pl.rcap * sizeof(uint64_t) + 4 * 320 * sizeof(uint32_t) +
+           (size_t)pl.G * pl.d * (pl.dtype == 1 ? 2 : 4) + 2 * (size_t)pl.G * sizeof(uint32_t);
 }
 
 hipError_t launch_score_select(const Plan &pl, const void *q, const void *k, void *ws,
