@@ -35,12 +35,14 @@ struct Plan {
     size_t lists_offset;  // byte offset of the lists in the workspace
     size_t ws_bytes;      // total workspace
     // Decode path (score_keys + filter): key rows per unit, blocks of 256 rows per unit, and
-    // the offsets of the key buffer [units][rstride][G] and block maxima [units][nblk][G]. The
-    // segments are then filter splits of 1024 rows (wpu per query).
+    // the offsets of the key buffer [units][G][rstride], the block maxima [units][nblk][G] and
+    // the tile maxima [units][G][rstride / tile_rows]. The segments are then filter splits of
+    // 1024 rows (wpu per query).
     bool stream;
     int64_t rstride;
     int nblk;
-    size_t keys_offset, bmax_offset;
+    int tile_rows;  // rows per key tile (one best key per tile and query)
+    size_t keys_offset, bmax_offset, tmax_offset;
 };
 
 // Launchers (enqueue only; return the hipError_t of the last launch).

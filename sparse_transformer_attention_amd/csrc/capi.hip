@@ -145,13 +145,14 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     // that buffer stays within kStreamKeysMax; others use the fused score_topk kernel.
     P.stream = false;
     if (P.candidates) {
-        const int64_t nblk = (P.rmax + kStreamBlockRows - 1) / kStreamBlockRows;
-        const double kb = (double)P.units * (double)(1 + nblk * kStreamBlockRows) * P.G * 4.0;
+        // Blocks of 256 rows from row 0 cover rows 1..rmax.
+        const int64_t nblk = (P.rmax + kStreamBlockRows) / kStreamBlockRows;
+        const double kb = (double)P.units * (double)(nblk * kStreamBlockRows) * P.G * 4.0;
         if (kb <= kStreamKeysMax) {
             P.stream = true;
             P.nblk = (int)nblk;
-            P.rstride = 1 + nblk * kStreamBlockRows;
-            P.wpu = (int)((P.rmax + kStreamSplitRows - 1) / kStreamSplitRows);
+            P.rstride = nblk * kStreamBlockRows;
+            P.wpu = (int)((P.rmax + kStreamSplitRows) / kStreamSplitRows);
             P.nwg = P.units * P.nblk;
             if (P.nwg > (int64_t)UINT32_MAX / 256 || P.units * P.wpu > (int64_t)UINT32_MAX / 256)
                 return fail(CA_ERR_UNSUPPORTED, "problem too large for one launch");
@@ -162,7 +163,12 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
             P.keys_offset = P.lists_offset + list_bytes;
             const size_t keys_bytes = (ca::stream_keys_bytes(P) + 255) & ~(size_t)255;
             P.bmax_offset = P.keys_offset + keys_bytes;
-            P.ws_bytes = P.bmax_offset + (size_t)P.units * P.nblk * P.G * sizeof(uint32_t);
+            const size_t bmax_bytes = ((size_t)P.units * P.nblk * P.G * sizeof(uint32_t) + 255) & ~(size_t)255;
+            // Tiles of 4 rows-per-load: 16 rows with 16 lanes per row (rows of >= 256 bytes),
+            // else 32.
+            P.tile_rows = row_bytes >= 256 ? 16 : 32;
+            P.tmax_offset = P.bmax_offset + bmax_bytes;
+            P.ws_bytes = P.tmax_offset + (size_t)P.units * P.G * (P.rstride / P.tile_rows) * sizeof(uint32_t);
             return CA_OK;
         }
     }

@@ -49,6 +49,29 @@ __device__ __forceinline__ float dpp_mirror16(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
 }
 
+// Maximum of x over lanes l and l ^ 8 (within rows of 16: DPP row_ror:8), l ^ 16 and l ^ 32
+// (gfx950 permlane swaps: the pair they return holds both partners of every lane).
+__device__ __forceinline__ uint32_t lane_max_xor8(uint32_t x) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
+    return o > x ? o : x;
+}
+__device__ __forceinline__ uint32_t lane_max_xor16(uint32_t x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return r[0] > r[1] ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_max_xor32(uint32_t x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return r[0] > r[1] ? r[0] : r[1];
+}
+// Maximum over the lanes l, l + off, l + 2 off, ... (mod 64) for off = 8, 16 or 32.
+template <int OFF>
+__device__ __forceinline__ uint32_t lane_max_stride(uint32_t x) {
+    static_assert(OFF == 8 || OFF == 16 || OFF == 32, "stride");
+    if constexpr (OFF == 8) x = lane_max_xor8(x);
+    if constexpr (OFF <= 16) x = lane_max_xor16(x);
+    return lane_max_xor32(x);
+}
+
 // Order-preserving map of a float32 score to uint32 (larger score -> larger key); -0 is
 // folded onto +0 so that equal scores give equal keys. Every finite score maps to a key
 // >= 0x00800000, so 0 is free to mean "no candidate".

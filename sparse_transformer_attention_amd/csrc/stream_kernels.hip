@@ -4,11 +4,17 @@
 // R_i = {1..i-W} outside the anchor and the window).
 //
 // score_keys: one workgroup per (unit, block of 256 key rows), where a unit is (batch, KV head,
-// query group) with up to G query vectors reading the same KV head. It streams the block's K
-// rows once (the only large HBM traffic of the path), computes the fp32 scores of its G
-// queries, and writes one order-preserving 32-bit key per (row, query) plus the block's best key
-// per query. No LDS lists, no barriers in the stream, no atomics: the grid is one-shot and the
-// hardware dispatcher balances it.
+// query group) with up to G query vectors reading the same KV head. Each wavefront requests its
+// 64 rows at once, then computes the fp32 scores of the G queries; the block's K rows are read
+// once (the only large HBM traffic of the path). It writes one order-preserving 32-bit key per
+// (row, query), the best key of every tile of rows, and the block's best key per query. Small workgroups in a one-shot grid let the
+// hardware dispatcher balance the stream across the CUs; no LDS lists, no atomics.
+//
+// Key buffer: [units][G][rstride] words, query-major. Rows are grouped in tiles of 4*RPG rows
+// (RPG = rows one wavefront load covers); after 4 loads a lane holds its query's keys of rows
+// r, r+RPG, r+2RPG, r+3RPG and stores them as one 16-byte word, so position p of a tile holds
+// row RPG*(p%4) + p/4 of the tile. Block b covers rows [256b, 256b+256); row 0 (the anchor) and
+// rows that are no candidate of the query hold key 0.
 //
 // filter: one workgroup per (unit, split of 1024 rows). The blocks are disjoint, so any value
 // that at least k' of a query's block maxima reach (k' = min(k, |R_i|)) is reached by k'
@@ -34,21 +40,22 @@ struct KeysArgs {
     int64_t groups, units;
     int64_t rstride;  // key rows per unit in the key buffer
     int nblk;         // blocks per unit
-    uint32_t *keys;   // [units][rstride][G]
+    uint32_t *keys;   // [units][G][rstride], tiles as described above
     uint32_t *bmax;   // [units][nblk][G]
+    uint32_t *tmax;   // [units][G][rstride / (4*RPG)]: best key of each tile
 };
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void score_keys_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                         KeysArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 5 : 4))) void score_keys_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, KeysArgs a) {
     constexpr int EB = sizeof(T);
     constexpr int RB = D * EB;               // bytes per key row
     constexpr int LPR = RB >= 256 ? 16 : 8;  // lanes per row
     constexpr int RPG = 64 / LPR;            // rows per wavefront load
     constexpr int P = RB / (16 * LPR);       // 16-byte loads per lane per row
-    constexpr int NG = 64 / RPG;             // row groups per wavefront (64 rows)
-    constexpr int U = 8 / P < NG ? 8 / P : NG;  // row groups per round (<= 8 loads per lane)
-    static_assert(P >= 1 && NG % U == 0, "layout");
+    constexpr int NG = 64 / RPG;             // row groups of a wavefront's 64 rows
+    constexpr int U = 16 / P < NG ? 16 / P : NG;  // row groups per round (<= 16 loads per lane)
+    static_assert(P >= 1 && NG % U == 0 && U % 4 == 0, "layout");
     __shared__ uint32_t red[4][G];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -73,40 +80,41 @@ __global__ __launch_bounds__(256) void score_keys_kernel(const T *__restrict__ q
         rl_max = rlast[t] > rl_max ? rlast[t] : rl_max;
     }
     uint32_t *bout = a.bmax + ((size_t)u * a.nblk + bi) * G;
-    const int row0 = 1 + bi * kBlockRows;
+    const int row0 = bi * kBlockRows;
     if (row0 > rl_max) {  // no candidate row of the unit in this block
         if (tid < G) bout[tid] = 0u;
         return;
     }
     const int rows_end = (int)((row0 + kBlockRows < rl_max + 1) ? row0 + kBlockRows : rl_max + 1);
+    const int rlo = row0 > 1 ? row0 : 1;  // row 0 (the anchor) is no candidate
     int my_rlast = (int)rlast[0];
 #pragma unroll
     for (int t = 1; t < G; ++t) my_rlast = (my_t == t) ? (int)rlast[t] : my_rlast;
 
-    uint4 qr[G][P];  // this lane's slices of the queries (zero past the last query vector)
-#pragma unroll
-    for (int t = 0; t < G; ++t) {
-        const int64_t idx = grp * G + t;
-        if (idx < nvec) {
-            const int h = kvh * a.g + (int)(idx % a.g);
-            const uint4 *src = reinterpret_cast<const uint4 *>(q + (((int64_t)b * a.Hq + h) * a.nq + idx / a.g) * D);
-#pragma unroll
-            for (int p = 0; p < P; ++p) qr[t][p] = src[p * LPR + sl];
-        } else {
-#pragma unroll
-            for (int p = 0; p < P; ++p) qr[t][p] = make_uint4(0, 0, 0, 0);
-        }
-    }
-
     const uint4 *kbase = reinterpret_cast<const uint4 *>(k + (int64_t)bk * a.n * D);
-    uint32_t *kout = a.keys + (size_t)u * a.rstride * G;
+    uint32_t *kout = a.keys + ((size_t)u * G + my_t) * a.rstride;
+    uint32_t *tout = a.tmax + ((size_t)u * G + my_t) * (a.rstride / (4 * RPG));
     const int wrow0 = row0 + wave * 64;  // this wavefront's 64 rows
     uint32_t best = 0u;
     if (wrow0 < rows_end) {
+        uint4 qr[G][P];  // this lane's slices of the queries (zero past the last query vector)
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+            const int64_t idx = grp * G + t;
+            if (idx < nvec) {
+                const int h = kvh * a.g + (int)(idx % a.g);
+                const uint4 *src = reinterpret_cast<const uint4 *>(q + (((int64_t)b * a.Hq + h) * a.nq + idx / a.g) * D);
+#pragma unroll
+                for (int p = 0; p < P; ++p) qr[t][p] = src[p * LPR + sl];
+            } else {
+#pragma unroll
+                for (int p = 0; p < P; ++p) qr[t][p] = make_uint4(0, 0, 0, 0);
+            }
+        }
 #pragma unroll
         for (int r = 0; r < NG / U; ++r) {
+            // Row groups r*U .. r*U+U-1 of the wavefront's rows, RPG rows each, all in flight.
             uint4 kr[U][P];
-            // Row groups r*U*... of the wavefront's rows, RPG rows per load.
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
                 int row = wrow0 + (r * U + uu) * RPG + lane / LPR;
@@ -116,31 +124,40 @@ __global__ __launch_bounds__(256) void score_keys_kernel(const T *__restrict__ q
                 for (int p = 0; p < P; ++p) kr[uu][p] = src[p * LPR + sl];
             }
 #pragma unroll
-            for (int uu = 0; uu < U; ++uu) {
-                float acc[G];
+            for (int u4 = 0; u4 < U; u4 += 4) {
+                uint32_t kv4[4];
 #pragma unroll
-                for (int t = 0; t < G; ++t) {
-                    float x = 0.f;
+                for (int gg = 0; gg < 4; ++gg) {
+                    const int uu = u4 + gg;
+                    float acc[G];
 #pragma unroll
-                    for (int p = 0; p < P; ++p) x = dot16(kr[uu][p], qr[t][p], x, T());
-                    acc[t] = x;
+                    for (int t = 0; t < G; ++t) {
+                        float x = 0.f;
+#pragma unroll
+                        for (int p = 0; p < P; ++p) x = dot16(kr[uu][p], qr[t][p], x, T());
+                        acc[t] = x;
+                    }
+                    const uint32_t key = score_key(reduce_row<LPR, G>(acc, lane));
+                    const int row = wrow0 + (r * U + uu) * RPG + lane / LPR;
+                    kv4[gg] = (row >= rlo && row < rows_end && row <= my_rlast) ? key : 0u;
+                    best = kv4[gg] > best ? kv4[gg] : best;
                 }
-                const uint32_t key = score_key(reduce_row<LPR, G>(acc, lane));
-                const int row = wrow0 + (r * U + uu) * RPG + lane / LPR;
-                if (writer && row < rows_end) {
-                    const uint32_t kv = row <= my_rlast ? key : 0u;
-                    kout[(size_t)row * G + my_t] = kv;
-                    best = kv > best ? kv : best;
-                }
+                // Tile of 4*RPG rows starting at the first of these row groups, and its best key
+                // (over the lanes of the query's rows: LPR apart).
+                const int tile0 = wrow0 + (r * U + u4) * RPG;
+                if (writer)
+                    *reinterpret_cast<uint4 *>(kout + tile0 + 4 * (lane / LPR)) =
+                        make_uint4(kv4[0], kv4[1], kv4[2], kv4[3]);
+                uint32_t tm = kv4[0] > kv4[1] ? kv4[0] : kv4[1];
+                tm = kv4[2] > tm ? kv4[2] : tm;
+                tm = kv4[3] > tm ? kv4[3] : tm;
+                tm = lane_max_stride<LPR>(tm);
+                if (writer && lane < LPR) tout[tile0 / (4 * RPG)] = tm;
             }
         }
     }
-    // Best key per query over the block: lanes of the same query are LPR apart.
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) {
-        const uint32_t o = (uint32_t)__shfl_xor((int)best, off);
-        best = o > best ? o : best;
-    }
+    // Best key per query over the block: lanes of the same query are LPR apart, then the waves.
+    best = lane_max_stride<LPR>(best);
     if (lane < LPR && writer) red[wave][my_t] = best;
     __syncthreads();
     if (tid < G) {
@@ -157,8 +174,10 @@ struct FilterArgs {
     int64_t groups, units;
     int64_t rstride;
     int nblk, nsplit;
-    const uint32_t *keys;  // [units][rstride][G]
+    int rpg;               // rows per load of score_keys (tile = 4*rpg rows)
+    const uint32_t *keys;  // [units][G][rstride]
     const uint32_t *bmax;  // [units][nblk][G]
+    const uint32_t *tmax;  // [units][G][rstride / (4*rpg)]
     uint32_t *cnt;         // [nqv][nsplit]
     uint64_t *lists;       // [nqv][nsplit][topk]
 };
@@ -170,7 +189,6 @@ __global__ __launch_bounds__(256) void filter_kernel(FilterArgs a) {
     __shared__ uint32_t hist_all[4][320];
     __shared__ uint32_t lcnt[G], thr_s[G];
     constexpr int E = kMaxBound / 64;
-    constexpr int RPT = kSplitRows / 256;  // rows per thread
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t u = blockIdx.x / a.nsplit;
@@ -191,28 +209,22 @@ __global__ __launch_bounds__(256) void filter_kernel(FilterArgs a) {
         rlast[t] = (int)rl;
         rl_max = rl > rl_max ? rl : rl_max;
     }
-    // The split's keys, requested first so that they arrive while the bounds are computed.
-    const int row0 = 1 + sp * kSplitRows;
+    // The split's tile maxima, requested first so that they arrive while the bounds are
+    // computed: entry i of the loop below is query i / tps, tile i % tps of the split.
+    const int row0 = sp * kSplitRows;
     const int rows_end = (int)((row0 + kSplitRows < rl_max + 1) ? row0 + kSplitRows : rl_max + 1);
-    const uint32_t *kin = a.keys + (size_t)u * a.rstride * G;
-    uint32_t kv[RPT][G];
+    const int trows = 4 * a.rpg;              // rows per tile
+    const int tps = kSplitRows / trows;       // tiles per split
+    const int64_t ntq = a.rstride / trows;    // tiles per (unit, query)
+    constexpr int TPT = (G * kSplitRows / 16 + 255) / 256;  // entries per thread (at most)
+    uint32_t tmv[TPT];
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-        const int row = row0 + tid + 256 * j;
-        if (row < rows_end) {
-            if constexpr (G == 4) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(kin + (size_t)row * 4);
-                kv[j][0] = v.x; kv[j][1] = v.y; kv[j][2] = v.z; kv[j][3] = v.w;
-            } else if constexpr (G == 2) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(kin + (size_t)row * 2);
-                kv[j][0] = v.x; kv[j][1] = v.y;
-            } else {
-                kv[j][0] = kin[row];
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < G; ++t) kv[j][t] = 0u;
-        }
+    for (int e = 0; e < TPT; ++e) {
+        const int i = tid + 256 * e;
+        const int t = i / tps, tile0 = row0 + (i % tps) * trows;
+        // A tile that starts below rows_end was written by score_keys.
+        tmv[e] = (t < G && tile0 < rows_end)
+                     ? a.tmax[((size_t)u * G + t) * ntq + tile0 / trows] : 0u;
     }
 
     // Wavefront t: the bound of query t, near the k'-th largest block maximum.
@@ -248,22 +260,27 @@ __global__ __launch_bounds__(256) void filter_kernel(FilterArgs a) {
     }
     __syncthreads();
 
-    // Keys of the split that reach their query's bound.
-    uint32_t thr[G];
+    // Keys of the split that reach their query's bound: only tiles whose best key does are read
+    // (position p of a tile holds row rpg*(p%4) + p/4 of the tile).
 #pragma unroll
-    for (int t = 0; t < G; ++t) thr[t] = thr_s[t];
+    for (int e = 0; e < TPT; ++e) {
+        const int i = tid + 256 * e;
+        const int t = i / tps;
+        if (t < G && tmv[e] >= thr_s[t]) {
+            const uint32_t th = thr_s[t];
+            const int tile0 = row0 + (i % tps) * trows;
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.keys + ((size_t)u * G + t) * a.rstride + tile0);
+            for (int w4 = 0; w4 < trows / 4; ++w4) {
+                const uint4 v = src[w4];
+                const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-        const int row = row0 + tid + 256 * j;
-#pragma unroll
-        for (int t = 0; t < G; ++t) {
-            const bool pass = row < rows_end && row <= rlast[t] && kv[j][t] >= thr[t];
-            const uint64_t m = __ballot(pass);
-            if (m != 0ull) {
-                uint32_t base = 0u;
-                if (lane == 0) base = atomicAdd(&lcnt[t], (uint32_t)__popcll(m));
-                base = __builtin_amdgcn_readlane(base, 0);
-                if (pass) lst[t][base + lanes_below(m)] = make_rank_key(kv[j][t], (uint32_t)row);
+                for (int c = 0; c < 4; ++c) {
+                    const int row = tile0 + a.rpg * c + w4;  // position 4*w4 + c
+                    if (kv[c] >= th && row >= 1 && row < rows_end && row <= rlast[t]) {
+                        const uint32_t at = atomicAdd(&lcnt[t], 1u);
+                        lst[t][at] = make_rank_key(kv[c], (uint32_t)row);
+                    }
+                }
             }
         }
     }
@@ -307,6 +324,7 @@ hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void 
     a.groups = pl.groups; a.units = pl.units; a.rstride = pl.rstride; a.nblk = pl.nblk;
     a.keys = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.keys_offset);
     a.bmax = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.bmax_offset);
+    a.tmax = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.tmax_offset);
     dim3 grid((unsigned)(pl.units * pl.nblk)), block(256);
 #define CA_LAUNCH_SK(T, D, G) \
     hipLaunchKernelGGL((score_keys_kernel<T, D, G>), grid, block, 0, s, static_cast<const T *>(q), \
@@ -332,8 +350,10 @@ hipError_t launch_filter(const Plan &pl, void *ws, hipStream_t s) {
     a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g; a.W = pl.W; a.topk = pl.topk;
     a.groups = pl.groups; a.units = pl.units; a.rstride = pl.rstride; a.nblk = pl.nblk;
     a.nsplit = pl.wpu;
+    a.rpg = pl.tile_rows / 4;
     a.keys = reinterpret_cast<const uint32_t *>(static_cast<char *>(ws) + pl.keys_offset);
     a.bmax = reinterpret_cast<const uint32_t *>(static_cast<char *>(ws) + pl.bmax_offset);
+    a.tmax = reinterpret_cast<const uint32_t *>(static_cast<char *>(ws) + pl.tmax_offset);
     a.cnt = reinterpret_cast<uint32_t *>(ws) + 2 * pl.nqv * pl.wpu;
     a.lists = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + pl.lists_offset);
     dim3 grid((unsigned)(pl.units * pl.wpu)), block(256);
