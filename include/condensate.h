@@ -112,7 +112,7 @@ int ca_attention_on_subset(const ca_params *p, const void *q, const void *k, con
  * kernel name (launches, summed milliseconds) into out[0..capacity), setting *count to the
  * number of kernels seen. Not meant to be used from several threads at once. */
 typedef struct {
-    const char *kernel;  /* static name: "score_select", "filter", "finish" or "attend" */
+    const char *kernel;  /* static name: "score_select", "finish" or "attend" */
     int64_t launches;
     double total_ms;
 } ca_kernel_time;

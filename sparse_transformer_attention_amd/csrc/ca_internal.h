@@ -34,10 +34,9 @@ struct Plan {
     int64_t lmax;         // candidate slots per query (wpu * topk)
     size_t lists_offset;  // byte offset of the lists in the workspace
     size_t ws_bytes;      // total workspace
-    // Decode path (score_keys + filter): key rows per unit, blocks of 256 rows per unit, and
-    // the offsets of the key buffer [units][G][rstride], the block maxima [units][nblk][G] and
-    // the tile maxima [units][G][rstride / tile_rows]. The segments are then filter splits of
-    // 1024 rows (wpu per query).
+    // Decode path (score_keys, then finish reading the key buffer): key rows per unit, blocks
+    // of 256 rows per unit, and the offsets of the key buffer [units][G][rstride], the block
+    // maxima [units][nblk][G] and the tile maxima [units][G][rstride / tile_rows].
     bool stream;
     int64_t rstride;
     int nblk;
@@ -57,7 +56,6 @@ hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k
                                     const int32_t *idx, float *out, hipStream_t s);
 size_t topk_lds_bytes(const Plan &pl);
 hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s);
-hipError_t launch_filter(const Plan &pl, void *ws, hipStream_t s);
 size_t stream_keys_bytes(const Plan &pl);
 
 }  // namespace ca

@@ -13,8 +13,8 @@
 namespace {
 
 // ---- measurement hooks: HIP events around each launch while profiling is on ----------------
-enum { K_SCORE = 0, K_FILTER = 1, K_FINISH = 2, K_ATTEND = 3, K_COUNT = 4 };
-const char *const kKernelNames[K_COUNT] = {"score_select", "filter", "finish", "attend"};
+enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_COUNT = 3 };
+const char *const kKernelNames[K_COUNT] = {"score_select", "finish", "attend"};
 
 struct Profiler {
     std::mutex mu;
@@ -82,7 +82,6 @@ constexpr int kMinChunk = 256, kMaxChunk = 1024, kDefaultChunk = 256;
 constexpr int kMaxTopk = 512;            // running lists hold topk + chunk <= 1024 keys
 constexpr int64_t kTargetBlocks = 1024;  // score_topk workgroups to aim for (4 per CU)
 constexpr int kStreamBlockRows = 256;    // score_keys rows per workgroup
-constexpr int kStreamSplitRows = 1024;   // filter rows per workgroup
 constexpr double kStreamKeysMax = 1024.0 * 1024 * 1024;  // key buffer budget (bytes)
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -141,8 +140,9 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         if (ca::topk_lds_bytes(P) <= 64 * 1024 || chunk <= kMinChunk) break;
         chunk /= 2;
     }
-    // Decode-shaped problems stream K once into a key buffer (score_keys, then filter) when
-    // that buffer stays within kStreamKeysMax; others use the fused score_topk kernel.
+    // Decode-shaped problems stream K once into a key buffer (score_keys; the finish kernel
+    // reads it) when that buffer stays within kStreamKeysMax; others use the fused score_topk
+    // kernel.
     P.stream = false;
     if (P.candidates) {
         // Blocks of 256 rows from row 0 cover rows 1..rmax.
@@ -152,21 +152,19 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
             P.stream = true;
             P.nblk = (int)nblk;
             P.rstride = nblk * kStreamBlockRows;
-            P.wpu = (int)((P.rmax + kStreamSplitRows) / kStreamSplitRows);
+            P.wpu = 1;
             P.nwg = P.units * P.nblk;
-            if (P.nwg > (int64_t)UINT32_MAX / 256 || P.units * P.wpu > (int64_t)UINT32_MAX / 256)
+            if (P.nwg > (int64_t)UINT32_MAX / 256)
                 return fail(CA_ERR_UNSUPPORTED, "problem too large for one launch");
-            P.lmax = (int64_t)P.wpu * P.topk;
-            const size_t slot_bytes = ((size_t)(3 * P.nqv * P.wpu) * sizeof(uint32_t) + 255) & ~(size_t)255;
-            P.lists_offset = slot_bytes;
-            const size_t list_bytes = ((size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) + 255) & ~(size_t)255;
-            P.keys_offset = P.lists_offset + list_bytes;
-            const size_t keys_bytes = (ca::stream_keys_bytes(P) + 255) & ~(size_t)255;
-            P.bmax_offset = P.keys_offset + keys_bytes;
-            const size_t bmax_bytes = ((size_t)P.units * P.nblk * P.G * sizeof(uint32_t) + 255) & ~(size_t)255;
+            P.lmax = 0;
+            P.lists_offset = 0;
             // Tiles of 4 rows-per-load: 16 rows with 16 lanes per row (rows of >= 256 bytes),
             // else 32.
             P.tile_rows = row_bytes >= 256 ? 16 : 32;
+            P.keys_offset = 0;
+            const size_t keys_bytes = (ca::stream_keys_bytes(P) + 255) & ~(size_t)255;
+            P.bmax_offset = P.keys_offset + keys_bytes;
+            const size_t bmax_bytes = ((size_t)P.units * P.nblk * P.G * sizeof(uint32_t) + 255) & ~(size_t)255;
             P.tmax_offset = P.bmax_offset + bmax_bytes;
             P.ws_bytes = P.tmax_offset + (size_t)P.units * P.G * (P.rstride / P.tile_rows) * sizeof(uint32_t);
             return CA_OK;
@@ -210,10 +208,6 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
         e = ca::launch_score_keys(pl, q, k, ws, s);
         ps.done();
         if (e != hipSuccess) return hip_fail(e, "score_keys launch");
-        ProfScope pfl(K_FILTER, s);
-        e = ca::launch_filter(pl, ws, s);
-        pfl.done();
-        if (e != hipSuccess) return hip_fail(e, "filter launch");
     } else if (pl.candidates) {
         ProfScope ps(K_SCORE, s);
         e = ca::launch_score_select(pl, q, k, ws, s);

@@ -1,6 +1,7 @@
 // The end of the condensate-attention path on gfx950, one workgroup per query vector:
-//   merge    exact top-k' of the candidates score_topk left in the query's segments (ranking
-//            keys (score_key << 32) | ~position; k' = min(k, |R_i|));
+//   merge    exact top-k' of the query's candidates (ranking keys (score_key << 32) | ~position;
+//            k' = min(k, |R_i|)): from the segments score_topk left, or from the key buffer of
+//            score_keys, reading only the tiles whose best key reaches the query's bound;
 //   assemble C_i = {0} u top-k' u {i-W+1..i} in ascending order, written to out_idx (pages of
 //            "The Condensate Theorem", metaphor-xennon blog, section 2.1 Definition 1);
 //   attend   (optional) the restricted softmax times V on that set, straight from LDS.
@@ -20,6 +21,12 @@ struct FinishArgs {
     float scale_log2e;
     const uint32_t *cnt;    // [nqv][wpu] keys in each segment
     const uint64_t *lists;  // [nqv][wpu][topk] segments of candidate ranking keys
+    // Key-buffer path (score_keys): units of G query vectors, blocks and tiles of key rows.
+    int G, nblk, tile_rows;
+    int64_t groups, rstride;
+    const uint32_t *keys;   // [units][G][rstride]
+    const uint32_t *bmax;   // [units][nblk][G]
+    const uint32_t *tmax;   // [units][G][rstride / tile_rows]
 };
 
 constexpr int kGather = 1024;  // candidates gathered into LDS for the one-wavefront select
@@ -48,34 +55,17 @@ __device__ __forceinline__ uint64_t wave_min_u64_dpp(uint64_t x) {
     return ((uint64_t)hmin << 32) | lmin;
 }
 
-// Exact top-kp of one query's candidates: the first cnt[w] keys of each segment w of
-// lists[w][0..topk) (distinct, non-zero; at least kp of them). The kp positions go to
-// js[0..kp), ascending (js needs room for 2*kp). Up to kGather candidates are gathered into
-// LDS by wavefront 0, which then selects alone with the keys in registers; more are selected by
-// the whole workgroup, re-reading the segments on every radix pass.
-template <int NT>
-__device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt,
-                                                const uint64_t *__restrict__ lists, int wpu,
-                                                int topk, int kp, int32_t *js, uint64_t *sel,
-                                                uint64_t *gathered, SelectShared<NT> &sh) {
+// Exact top-kp of one query's candidates, given as n keys gathered in LDS (gathered[0..n) when
+// n <= kGather) and as key_at(f) over f in [0, slots) (0 = no candidate): the distinct,
+// non-zero ranking keys. The kp positions go to js[0..kp), ascending (js needs room for 2*kp).
+// Up to kGather candidates are selected by wavefront 0 alone with the keys in registers; more
+// by the whole workgroup, calling key_at on every radix pass.
+template <int NT, typename KeyAt>
+__device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at, int kp, int32_t *js,
+                                             uint64_t *sel, const uint64_t *gathered,
+                                             SelectShared<NT> &sh) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (wave == 0) {
-        int base = 0;
-        for (int j0 = 0; j0 < wpu; j0 += 64) {
-            const int w = j0 + lane;
-            const int c = w < wpu ? (int)cnt[w] : 0;
-            int tot;
-            const int off = base + wave_excl_scan(c, &tot);
-            for (int e = 0; e < c; ++e)
-                if (off + e < kGather) gathered[off + e] = lists[(size_t)w * topk + e];
-            base += tot;
-        }
-        if (lane == 0) sh.sel_count = base;
-    }
-    __syncthreads();
-    const int n = sh.sel_count;
-    __syncthreads();
     if (n <= kGather) {
         if (wave == 0) {
             uint64_t kk[kMaxKeysPerThread];
@@ -89,12 +79,6 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
         __syncthreads();
         for (int t = tid; t < kp; t += NT) js[t] = rank_key_pos(sel[t]);
     } else {
-        const int64_t slots = (int64_t)wpu * topk;
-        auto key_at = [&](int64_t f) -> uint64_t {
-            const int w = (int)(f / topk);
-            const int e = (int)(f - (int64_t)w * topk);
-            return e < (int)cnt[w] ? lists[f] : 0ull;
-        };
         uint64_t kmax = 0ull, kmin = ~0ull;
         for (int64_t f = tid; f < slots; f += NT) {
             const uint64_t x = key_at(f);
@@ -186,7 +170,173 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
     __syncthreads();
 }
 
-template <typename T, int D, int NT, bool ATTEND>
+// Candidates from the segments score_topk left (the first cnt[w] keys of each segment w of
+// lists[w][0..topk)), gathered into LDS by wavefront 0; then the exact top-kp.
+template <int NT>
+__device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt,
+                                                const uint64_t *__restrict__ lists, int wpu,
+                                                int topk, int kp, int32_t *js, uint64_t *sel,
+                                                uint64_t *gathered, SelectShared<NT> &sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (wave == 0) {
+        int base = 0;
+        for (int j0 = 0; j0 < wpu; j0 += 64) {
+            const int w = j0 + lane;
+            const int c = w < wpu ? (int)cnt[w] : 0;
+            int tot;
+            const int off = base + wave_excl_scan(c, &tot);
+            for (int e = 0; e < c; ++e)
+                if (off + e < kGather) gathered[off + e] = lists[(size_t)w * topk + e];
+            base += tot;
+        }
+        if (lane == 0) sh.sel_count = base;
+    }
+    __syncthreads();
+    const int n = sh.sel_count;
+    __syncthreads();
+    auto key_at = [&](int64_t f) -> uint64_t {
+        const int w = (int)(f / topk);
+        const int e = (int)(f - (int64_t)w * topk);
+        return e < (int)cnt[w] ? lists[f] : 0ull;
+    };
+    select_exact<NT>(n, (int64_t)wpu * topk, key_at, kp, js, sel, gathered, sh);
+}
+
+// Candidates from the key buffer (score_keys): the query's bound is the lower edge of the radix
+// bin that holds the k'-th largest of its block (or tile) maxima (k' distinct candidates reach
+// it, so it is a lower bound of its k-th key); the keys of every tile whose best key reaches the
+// bound are gathered into LDS; then the exact top-kp. keys/tmax point at the query's rows, bm at
+// its first block maximum (stride G); the query's candidate rows are 1..rl. tiles is LDS for
+// kTileCap tile indices.
+constexpr int kTileCap = 1024;
+constexpr int kRankSelectMax = 256;  // candidates selected by rank counting (else radix select)
+
+template <int NT>
+__device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ keys,
+                                             const uint32_t *__restrict__ tmax,
+                                             const uint32_t *__restrict__ bm, int G, int nblk,
+                                             int tile_rows, int64_t rl, int kp, int32_t *js,
+                                             uint64_t *sel, uint64_t *gathered, int32_t *tiles,
+                                             SelectShared<NT> &sh) {
+    constexpr int E = 8;   // block maxima per lane: at most 512 (merged in groups beyond)
+    constexpr int TU = 8;  // tile maxima in flight per thread
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rpg = tile_rows / 4;
+    const int64_t ntiles = (rl + tile_rows) / tile_rows;  // tiles covering rows 0..rl
+    // First tile maxima requested before the bound is known.
+    uint32_t tm[TU];
+#pragma unroll
+    for (int e = 0; e < TU; ++e) {
+        const int64_t j = tid + (int64_t)NT * e;
+        tm[e] = j < ntiles ? tmax[j] : 0u;
+    }
+    if (wave == 0) {
+        // Maxima of disjoint groups of rows: the blocks (256 rows), or the tiles when there are
+        // fewer than 2k' blocks; merged into at most 64*E groups of consecutive ones.
+        const bool by_tile = (int64_t)nblk < 2 * (int64_t)kp;
+        const uint32_t *src = by_tile ? tmax : bm;
+        const int64_t stride = by_tile ? 1 : G;
+        const int64_t count = by_tile ? ntiles : nblk;
+        const int per = (int)((count + 64 * E - 1) / (64 * E));
+        const int64_t ngr = (count + per - 1) / per;
+        uint32_t m[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) m[e] = 0u;
+        for (int jj = 0; jj < per; ++jj) {  // E independent loads per pass
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int64_t gi = lane + 64 * e, grp = gi * per + jj;
+                if (gi < ngr && grp < count) {
+                    const uint32_t x = src[grp * stride];
+                    m[e] = x > m[e] ? x : m[e];
+                }
+            }
+        }
+        const uint32_t thr = wave_bound_u32(m, kp, &sh.hist[0][0]);
+        if (lane == 0) { sh.pick[0] = thr > 1u ? thr : 1u; sh.pick[1] = 0u; sh.sel_count = 0; }
+    }
+    __syncthreads();
+    const uint32_t thr = sh.pick[0];
+    // Tiles whose best key reaches the bound, compacted into tiles[].
+    for (int64_t j0 = tid;; j0 += (int64_t)NT * TU) {
+#pragma unroll
+        for (int e = 0; e < TU; ++e) {
+            if (tm[e] >= thr) {
+                const uint32_t at = atomicAdd(&sh.pick[1], 1u);
+                if (at < (uint32_t)kTileCap) tiles[at] = (int32_t)(j0 + (int64_t)NT * e);
+            }
+        }
+        if (j0 + (int64_t)NT * TU >= ntiles) break;
+#pragma unroll
+        for (int e = 0; e < TU; ++e) {
+            const int64_t j = j0 + (int64_t)NT * (TU + e);
+            tm[e] = j < ntiles ? tmax[j] : 0u;
+        }
+    }
+    __syncthreads();
+    const int nt = (int)sh.pick[1];
+    if (nt <= kTileCap) {
+        // Their keys, one 16-byte word per thread (position p of a tile holds row
+        // rpg*(p%4) + p/4 of the tile), the ones that reach the bound gathered.
+        const int wpt = tile_rows / 4;
+        for (int x = tid; x < nt * wpt; x += NT) {
+            const int64_t tile0 = (int64_t)tiles[x / wpt] * tile_rows;
+            const int w4 = x % wpt;
+            const uint4 v = *reinterpret_cast<const uint4 *>(keys + tile0 + 4 * w4);
+            const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t row = tile0 + rpg * c + w4;
+                if (kv[c] >= thr && row >= 1 && row <= rl) {
+                    const int pos = atomicAdd(&sh.sel_count, 1);
+                    if (pos < kGather) gathered[pos] = make_rank_key(kv[c], (uint32_t)row);
+                }
+            }
+        }
+    } else if (tid == 0) {
+        sh.sel_count = kGather + 1;  // too many tiles: select over the whole key buffer
+    }
+    __syncthreads();
+    const int n = sh.sel_count;
+    __syncthreads();
+    if (n <= kRankSelectMax && n >= kp) {
+        // Few candidates: a key is selected when fewer than kp keys beat it; the selected
+        // positions are then placed by their rank among the selected ones (ascending).
+        uint64_t x = 0ull;
+        bool chosen = false;
+        if (tid < n) {
+            x = gathered[tid];
+            int above = 0;
+            for (int f = 0; f < n; ++f) above += gathered[f] > x;
+            chosen = above < kp;
+        }
+        __syncthreads();
+        if (tid < n) gathered[kGather - 1 - tid] = chosen ? x : 0ull;  // selected keys (0 = not)
+        __syncthreads();
+        if (chosen) {
+            const int32_t pos = rank_key_pos(x);
+            int rank = 0;
+            for (int f = 0; f < n; ++f) {
+                const uint64_t y = gathered[kGather - 1 - f];
+                rank += y != 0ull && rank_key_pos(y) < pos;
+            }
+            js[rank] = pos;
+        }
+        __syncthreads();
+        return;
+    }
+    // More than kGather candidates (ties at the bound): every key of rows 1..rl that reaches it.
+    auto key_at = [&](int64_t f) -> uint64_t {
+        const int64_t tile0 = f - f % tile_rows;
+        const int p = (int)(f - tile0);
+        const int64_t row = tile0 + rpg * (p % 4) + p / 4;
+        const uint32_t kv = keys[f];
+        return (row >= 1 && row <= rl && kv >= thr) ? make_rank_key(kv, (uint32_t)row) : 0ull;
+    };
+    select_exact<NT>(n, ntiles * tile_rows, key_at, kp, js, sel, gathered, sh);
+}
+
+template <typename T, int D, int NT, bool ATTEND, bool TILES>
 __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                     const T *__restrict__ v,
                                                     int32_t *__restrict__ out_idx,
@@ -199,6 +349,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     SelectShared<NT> &ssh = shu.sel;
     AttendShared<NT, D, T> &ash = shu.att;
     __shared__ uint64_t gathered[kGather];
+    __shared__ int32_t tile_idx[TILES ? kTileCap : 1];
     int32_t *js = fsm;
     float *sc = reinterpret_cast<float *>(fsm + 2 * a.cap);
     uint64_t *sel = reinterpret_cast<uint64_t *>(fsm + 3 * a.cap + (a.cap & 1));
@@ -214,9 +365,26 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
 
     // js layout: [0 if the anchor is separate][top-k' ascending][window ascending]
     const int base = wlo > 0 ? 1 : 0;
-    if (kp > 0)
-        select_segments<NT>(a.cnt + qv * a.wpu, a.lists + qv * a.wpu * a.topk, a.wpu, a.topk, kp,
-                            js + base, sel, gathered, ssh);
+    if (kp > 0) {
+        if constexpr (TILES) {
+            // Unit and slot of this query vector: vector index r*g + (h - kvh*g) of its KV head.
+            const int64_t bh = qv / a.nq;
+            const int h = (int)(bh % a.Hq);
+            const int b = (int)(bh / a.Hq);
+            const int kvh = h / a.g;
+            const int64_t idx = r * a.g + (h - kvh * a.g);
+            const int64_t u = ((int64_t)b * a.Hkv + kvh) * a.groups + idx / a.G;
+            const int t = (int)(idx % a.G);
+            const int64_t ntq = a.rstride / a.tile_rows;
+            select_tiles<NT>(a.keys + ((size_t)u * a.G + t) * a.rstride,
+                             a.tmax + ((size_t)u * a.G + t) * ntq,
+                             a.bmax + (size_t)u * a.nblk * a.G + t, a.G, a.nblk, a.tile_rows, rl,
+                             kp, js + base, sel, gathered, tile_idx, ssh);
+        } else {
+            select_segments<NT>(a.cnt + qv * a.wpu, a.lists + qv * a.wpu * a.topk, a.wpu, a.topk,
+                                kp, js + base, sel, gathered, ssh);
+        }
+    }
     const int wcount = (int)(i - wlo + 1);
     const int count = base + kp + wcount;
     if (tid == 0 && base) js[0] = 0;
@@ -287,6 +455,11 @@ FinishArgs finish_args(const Plan &pl, const void *ws) {
     a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
     a.cnt = ws ? static_cast<const uint32_t *>(ws) + 2 * pl.nqv * pl.wpu : nullptr;
     a.lists = ws ? reinterpret_cast<const uint64_t *>(static_cast<const char *>(ws) + pl.lists_offset) : nullptr;
+    a.G = pl.G; a.nblk = pl.nblk; a.tile_rows = pl.tile_rows; a.groups = pl.groups; a.rstride = pl.rstride;
+    const char *wb = static_cast<const char *>(ws);
+    a.keys = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.keys_offset) : nullptr;
+    a.bmax = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.bmax_offset) : nullptr;
+    a.tmax = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.tmax_offset) : nullptr;
     return a;
 }
 
@@ -304,10 +477,16 @@ hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const 
                              (sizeof(SelectShared<1024>) > sizeof(AttendShared<1024, D, T>)
                                   ? sizeof(SelectShared<1024>) : sizeof(AttendShared<1024, D, T>));
     const bool wide = pl.nqv < kWideBelow && shmem + fixed1024 <= 64 * 1024;
-    if (wide)
-        hipLaunchKernelGGL((finish_kernel<T, D, 1024, ATTEND>), grid, dim3(1024), shmem, s, qt, kt, vt, out_idx, out, a);
-    else
-        hipLaunchKernelGGL((finish_kernel<T, D, 256, ATTEND>), grid, dim3(256), shmem, s, qt, kt, vt, out_idx, out, a);
+#define CA_LAUNCH_FIN(NT, TILES)                                                                  \
+    hipLaunchKernelGGL((finish_kernel<T, D, NT, ATTEND, TILES>), grid, dim3(NT), shmem, s, qt, kt, vt, \
+                       out_idx, out, a)
+    const bool tiles = pl.stream && ws != nullptr;
+    if (wide) {
+        if (tiles) CA_LAUNCH_FIN(1024, true); else CA_LAUNCH_FIN(1024, false);
+    } else {
+        if (tiles) CA_LAUNCH_FIN(256, true); else CA_LAUNCH_FIN(256, false);
+    }
+#undef CA_LAUNCH_FIN
     return hipGetLastError();
 }
 
