@@ -148,7 +148,8 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         // Blocks of 256 rows from row 0 cover rows 1..rmax.
         const int64_t nblk = (P.rmax + kStreamBlockRows) / kStreamBlockRows;
         const double kb = (double)P.units * (double)(nblk * kStreamBlockRows) * P.G * 4.0;
-        if (kb <= kStreamKeysMax) {
+        // (Index math of score_keys in 32 bits.)
+        if (kb <= kStreamKeysMax && P.units * nblk < ((int64_t)1 << 31) && nvec < ((int64_t)1 << 31)) {
             P.stream = true;
             P.nblk = (int)nblk;
             P.rstride = nblk * kStreamBlockRows;

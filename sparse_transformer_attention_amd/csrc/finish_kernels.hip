@@ -307,6 +307,7 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ keys,
         if (tid < n) {
             x = gathered[tid];
             int above = 0;
+#pragma unroll 8
             for (int f = 0; f < n; ++f) above += gathered[f] > x;
             chosen = above < kp;
         }
@@ -316,6 +317,7 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ keys,
         if (chosen) {
             const int32_t pos = rank_key_pos(x);
             int rank = 0;
+#pragma unroll 8
             for (int f = 0; f < n; ++f) {
                 const uint64_t y = gathered[kGather - 1 - f];
                 rank += y != 0ull && rank_key_pos(y) < pos;

@@ -32,6 +32,8 @@ struct KeysArgs {
     int64_t groups, units;
     int64_t rstride;  // key rows per unit in the key buffer
     int nblk;         // blocks per unit
+    uint32_t nvec;    // query vectors per KV head (g * nq)
+    int row_base;     // n - nq - W: the last candidate row of query vector idx is row_base + idx / g
     uint32_t *keys;   // [units][G][rstride], tiles as described above
     uint32_t *bmax;   // [units][nblk][G]
     uint32_t *tmax;   // [units][G][rstride / (4*RPG)]: best key of each tile
@@ -52,36 +54,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t u = blockIdx.x / a.nblk;
-    const int bi = (int)(blockIdx.x - u * a.nblk);
-    const int bk = (int)(u / a.groups);  // b * Hkv + kvh
-    const int64_t grp = u - (int64_t)bk * a.groups;
-    const int kvh = bk % a.Hkv;
-    const int b = bk / a.Hkv;
-    const int64_t nvec = (int64_t)a.g * a.nq;
+    // Workgroup (unit, block), units ordered (batch * Hkv + KV head, query group); 32-bit math.
+    const uint32_t wg = blockIdx.x, nb = (uint32_t)a.nblk, ng = (uint32_t)a.groups;
+    const uint32_t uu32 = wg / nb;
+    const int bi = (int)(wg - uu32 * nb);
+    const uint32_t bk = uu32 / ng;
+    const uint32_t grp = uu32 - bk * ng;
+    const int64_t u = (int64_t)bk * a.groups + grp;
+    const uint32_t g = (uint32_t)a.g;
     const int sl = lane % LPR;
     const bool writer = sl % (LPR / G) == 0;
     const int my_t = sl / (LPR / G);
-
-    int64_t rlast[G];
-    int64_t rl_max = 0;
-#pragma unroll
-    for (int t = 0; t < G; ++t) {
-        const int64_t idx = grp * G + t;
-        rlast[t] = idx < nvec ? (a.n - a.nq + idx / a.g) - a.W : 0;
-        rl_max = rlast[t] > rl_max ? rlast[t] : rl_max;
-    }
+    // Last candidate row of the unit: that of its last query vector (rows grow with idx).
+    const uint32_t idx0 = grp * G;
+    const uint32_t idx_last = (idx0 + G - 1 < a.nvec ? idx0 + G - 1 : a.nvec - 1);
+    const int rl_max = a.row_base + (int)(idx_last / g);
     uint32_t *bout = a.bmax + ((size_t)u * a.nblk + bi) * G;
     const int row0 = bi * kBlockRows;
     if (row0 > rl_max) {  // no candidate row of the unit in this block
         if (tid < G) bout[tid] = 0u;
         return;
     }
-    const int rows_end = (int)((row0 + kBlockRows < rl_max + 1) ? row0 + kBlockRows : rl_max + 1);
+    const int rows_end = (row0 + kBlockRows < rl_max + 1) ? row0 + kBlockRows : rl_max + 1;
     const int rlo = row0 > 1 ? row0 : 1;  // row 0 (the anchor) is no candidate
-    int my_rlast = (int)rlast[0];
-#pragma unroll
-    for (int t = 1; t < G; ++t) my_rlast = (my_t == t) ? (int)rlast[t] : my_rlast;
 
     const uint4 *kbase = reinterpret_cast<const uint4 *>(k + (int64_t)bk * a.n * D);
     uint32_t *kout = a.keys + ((size_t)u * G + my_t) * a.rstride;
@@ -89,15 +84,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     const int wrow0 = row0 + wave * 64;  // this wavefront's 64 rows
     uint32_t best = 0u;
     if (wrow0 < rows_end) {
+        // The queries (vector idx of the KV head: head bk*g + idx % g, row idx / g) and the last
+        // candidate row of this lane's query.
         uint4 qr[G][P];  // this lane's slices of the queries (zero past the last query vector)
+        int my_rlast = 0;
 #pragma unroll
         for (int t = 0; t < G; ++t) {
-            const int64_t idx = grp * G + t;
-            if (idx < nvec) {
-                const int h = kvh * a.g + (int)(idx % a.g);
-                const uint4 *src = reinterpret_cast<const uint4 *>(q + (((int64_t)b * a.Hq + h) * a.nq + idx / a.g) * D);
+            const uint32_t idx = idx0 + t;
+            if (idx < a.nvec) {
+                const uint32_t qh = idx / g, hh = idx - qh * g;
+                const uint4 *src = reinterpret_cast<const uint4 *>(q + (((int64_t)bk * g + hh) * a.nq + qh) * D);
 #pragma unroll
                 for (int p = 0; p < P; ++p) qr[t][p] = src[p * LPR + sl];
+                if (my_t == t) my_rlast = a.row_base + (int)qh;
             } else {
 #pragma unroll
                 for (int p = 0; p < P; ++p) qr[t][p] = make_uint4(0, 0, 0, 0);
@@ -170,6 +169,8 @@ hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void 
     KeysArgs a;
     a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g; a.W = pl.W;
     a.groups = pl.groups; a.units = pl.units; a.rstride = pl.rstride; a.nblk = pl.nblk;
+    a.nvec = (uint32_t)(pl.g * pl.nq);
+    a.row_base = (int)(pl.n - pl.nq - pl.W);
     a.keys = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.keys_offset);
     a.bmax = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.bmax_offset);
     a.tmax = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.tmax_offset);
