@@ -28,9 +28,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "condensate-attn decode queries/sec + achieved HBM GB/s at 131K ctx (1 GPU)"
 HBM_PEAK_GBPS = 8000.0
-COUNTERS = os.path.join(ROOT, "profiles", "score_select_decode_131k_counters.md")
+# HBM bytes per launch of the score stage's kernel (score_keys on this workload) from rocprofv3
+# FETCH_SIZE / WRITE_SIZE counters, valid while the kernel's sources hash to the recorded value.
+COUNTERS = os.path.join(ROOT, "profiles", "score_keys_decode_131k_gqa_bf16_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_transformer_attention_amd", "csrc", f)
-                  for f in ("select_kernels.hip", "device_utils.h", "ca_internal.h")]
+                  for f in ("stream_kernels.hip", "score_core.h", "device_utils.h", "ca_internal.h")]
 
 
 def kernel_sources_sha() -> str:
@@ -41,7 +43,7 @@ def kernel_sources_sha() -> str:
 
 
 def recorded_traffic(workload: str):
-    """HBM bytes per score_select launch from the committed counter summary, or None when the
+    """HBM bytes per score-stage launch from the committed counter summary, or None when the
     summary is absent, is for another workload, or predates the current kernel sources."""
     if not os.path.exists(COUNTERS):
         return None

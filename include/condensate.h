@@ -67,9 +67,13 @@ typedef struct {
     int32_t W;         /* local window length, >= 1 (the window includes position i) */
     int32_t topk;      /* dynamic top-k size, >= 0 */
     int32_t dtype;     /* ca_dtype of q, k, v */
-    int32_t chunk;     /* key rows per unit of work of the scoring pass; 0 = automatic (256),
-                          else 256, 512 or 1024 (a hint: lowered to 512 when topk + chunk
-                          would exceed 1024). Results do not depend on it. */
+    int32_t chunk;     /* scoring strategy. 0 = automatic: when its key buffer stays within
+                          1 GiB (decode-shaped problems) the library streams K once into
+                          per-row score keys and selects from them, else it uses the chunked
+                          select below with 256-row chunks. 256, 512 or 1024 = always the
+                          chunked select (one pass that keeps running top-k lists per chunk of
+                          that many key rows; a hint: halved while its buffers would exceed
+                          64 KiB of LDS). Results do not depend on it. */
 } ca_params;
 
 /* The one-call form, as the method is usually stated: float32 q/k/v, batch 1, every position

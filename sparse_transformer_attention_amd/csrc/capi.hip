@@ -144,7 +144,7 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     // reads it) when that buffer stays within kStreamKeysMax; others use the fused score_topk
     // kernel.
     P.stream = false;
-    if (P.candidates) {
+    if (P.candidates && p->chunk == 0) {
         // Blocks of 256 rows from row 0 cover rows 1..rmax.
         const int64_t nblk = (P.rmax + kStreamBlockRows) / kStreamBlockRows;
         const double kb = (double)P.units * (double)(nblk * kStreamBlockRows) * P.G * 4.0;
