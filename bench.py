@@ -2,16 +2,16 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--chunk C] [--rotate R]
 
-A step is one call of ca_condensate_attention_ex: scores over every causal key, anchor/window
-masks, chunk-local exact top-k, global merge and set assembly, then the restricted softmax
-times V -- the whole path, on one batch of synthetic inputs already resident in HBM. The
-default workload is the 131,072-token GQA decode step (32 query heads, 8 KV heads, d=128,
-bf16, W=256, k=64). Distinct KV buffer sets are rotated between steps so that the key stream
-comes from HBM and not from the 256 MB last-level cache.
+A step is one call of ca_condensate_attention_ex: scores over every causal key, the anchor /
+window / exact top-k set, and the restricted softmax times V -- the whole path, on one batch of
+synthetic inputs already resident in HBM. The default workload is the 131,072-token GQA decode
+step (32 query heads, 8 KV heads, d=128, bf16, W=256, k=64). Distinct KV buffer sets are rotated
+between steps so that the key stream comes from HBM and not from the 256 MB last-level cache.
 
-Prints one JSON line with queries/s (query vectors per second), the step's algorithmic HBM
-GB/s, the roofline of the dominant kernel (score_select; durations from HIP events the library
-records around its own launches on the stream it uses) and the CPU oracle timed on the host.
+Prints one JSON line: query vectors/s from a clean timed loop, the step's algorithmic HBM GB/s,
+the roofline of the dominant kernel (the score stage; durations from HIP events the library
+records around its own launches on the stream it uses, in a second pass over the same steps),
+and the CPU oracle timed on the host.
 """
 from __future__ import annotations
 
@@ -191,7 +191,7 @@ def main():
         "ms_per_step_profiled": ms_per_step_profiled,
         "kernels": kernels,
         "roofline": {
-            "kernel": "score_select",
+            "kernel": "score_keys (score stage)" if not args.chunk else "score_topk (score stage)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,

@@ -1,6 +1,6 @@
 // Restricted softmax times V for one query vector, executed by one workgroup of NT threads
 // (pages of "The Condensate Theorem", metaphor-xennon blog: section 2.3, Theorem 1's
-// Attention_C; section 3.2.4, the output computed only on C_i).
+// Attention_C; section 3.2.4, the output evaluated over C_i alone).
 //
 // The set is given as `count` positions js[0..count) in LDS. Every gathered row is loaded
 // with 16-byte loads: K rows 4 lanes per row (P loads each) for the fp32 dot products, V rows
