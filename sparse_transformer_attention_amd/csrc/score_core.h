@@ -11,7 +11,16 @@ namespace ca {
 
 // Loads the K rows of one streaming round: row groups gi0 + 4*uu (RPG = 64/LPR rows each, LPR
 // lanes per row) of the chunk [r0, rend). Rows past the chunk's end are clamped to its last row
-// (loaded, never used), so every load is unconditional.
+// (loaded, never used), so every load is unconditional. Non-temporal loads.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load of a key-row slice that is read once: non-temporal, so the stream does not
+// evict what the kernels write meanwhile.
+__device__ __forceinline__ uint4 load_row16_nt(const uint4 *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int LPR, int P, int U>
 __device__ __forceinline__ void load_round(const uint4 *__restrict__ kbase, int r0, int rend, int gi0,
                                            int lane, uint4 (&dst)[U][P]) {
@@ -24,7 +33,7 @@ __device__ __forceinline__ void load_round(const uint4 *__restrict__ kbase, int 
         row = row < rend ? row : rend - 1;
         const uint4 *src = kbase + (int64_t)row * RQ;
 #pragma unroll
-        for (int p = 0; p < P; ++p) dst[uu][p] = src[p * LPR + sl];
+        for (int p = 0; p < P; ++p) dst[uu][p] = load_row16_nt(src + p * LPR + sl);
     }
 }
 

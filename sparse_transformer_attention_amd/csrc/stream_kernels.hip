@@ -24,7 +24,9 @@
 namespace ca {
 namespace {
 
-constexpr int kBlockRows = 256;   // rows per score_keys workgroup (block of the bound)
+constexpr int kBlockRows = 256;   // rows per block of the bound (4 wavefronts of score_keys)
+constexpr int kKeysBW = 2;        // blocks per score_keys workgroup
+constexpr bool kKeysNT = true;    // non-temporal key-row loads
 
 struct KeysArgs {
     int64_t n, nq;
@@ -39,8 +41,17 @@ struct KeysArgs {
     uint32_t *tmax;   // [units][G][rstride / (4*RPG)]: best key of each tile
 };
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 5 : 4))) void score_keys_kernel(
+// 16-byte load of a key-row slice; NTL: non-temporal (streamed once, kept out of the caches so
+// that the key buffer written meanwhile stays there).
+template <bool NTL>
+__device__ __forceinline__ uint4 load_row16(const uint4 *p) {
+    if constexpr (NTL) return load_row16_nt(p);
+    else return *p;
+}
+
+// BW blocks of 256 rows per workgroup (4 wavefronts each).
+template <typename T, int D, int G, int BW, bool NTL>
+__global__ __launch_bounds__(256 * BW) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 5 : 4))) void score_keys_kernel(
     const T *__restrict__ q, const T *__restrict__ k, KeysArgs a) {
     constexpr int EB = sizeof(T);
     constexpr int RB = D * EB;               // bytes per key row
@@ -50,14 +61,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     constexpr int NG = 64 / RPG;             // row groups of a wavefront's 64 rows
     constexpr int U = 16 / P < NG ? 16 / P : NG;  // row groups per round (<= 16 loads per lane)
     static_assert(P >= 1 && NG % U == 0 && U % 4 == 0, "layout");
-    __shared__ uint32_t red[4][G];
+    __shared__ uint32_t red[4 * BW][G];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Workgroup (unit, block), units ordered (batch * Hkv + KV head, query group); 32-bit math.
-    const uint32_t wg = blockIdx.x, nb = (uint32_t)a.nblk, ng = (uint32_t)a.groups;
-    const uint32_t uu32 = wg / nb;
-    const int bi = (int)(wg - uu32 * nb);
+    // Workgroup (unit, BW blocks), units ordered (batch * Hkv + KV head, query group); 32-bit
+    // math. Wavefronts 4b..4b+3 take block b of the workgroup.
+    const uint32_t wpb = ((uint32_t)a.nblk + BW - 1) / BW;  // workgroups per unit
+    const uint32_t wg = blockIdx.x, ng = (uint32_t)a.groups;
+    const uint32_t uu32 = wg / wpb;
+    const int bi = (int)(wg - uu32 * wpb) * BW + wave / 4;
     const uint32_t bk = uu32 / ng;
     const uint32_t grp = uu32 - bk * ng;
     const int64_t u = (int64_t)bk * a.groups + grp;
@@ -69,21 +82,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     const uint32_t idx0 = grp * G;
     const uint32_t idx_last = (idx0 + G - 1 < a.nvec ? idx0 + G - 1 : a.nvec - 1);
     const int rl_max = a.row_base + (int)(idx_last / g);
-    uint32_t *bout = a.bmax + ((size_t)u * a.nblk + bi) * G;
     const int row0 = bi * kBlockRows;
-    if (row0 > rl_max) {  // no candidate row of the unit in this block
-        if (tid < G) bout[tid] = 0u;
-        return;
-    }
+    const bool live = bi < a.nblk && row0 <= rl_max;  // the block has candidate rows
     const int rows_end = (row0 + kBlockRows < rl_max + 1) ? row0 + kBlockRows : rl_max + 1;
     const int rlo = row0 > 1 ? row0 : 1;  // row 0 (the anchor) is no candidate
 
     const uint4 *kbase = reinterpret_cast<const uint4 *>(k + (int64_t)bk * a.n * D);
     uint32_t *kout = a.keys + ((size_t)u * G + my_t) * a.rstride;
     uint32_t *tout = a.tmax + ((size_t)u * G + my_t) * (a.rstride / (4 * RPG));
-    const int wrow0 = row0 + wave * 64;  // this wavefront's 64 rows
+    const int wrow0 = row0 + (wave % 4) * 64;  // this wavefront's 64 rows
     uint32_t best = 0u;
-    if (wrow0 < rows_end) {
+    if (live && wrow0 < rows_end) {
         // The queries (vector idx of the KV head: head bk*g + idx % g, row idx / g) and the last
         // candidate row of this lane's query.
         uint4 qr[G][P];  // this lane's slices of the queries (zero past the last query vector)
@@ -112,7 +121,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
                 row = row < rows_end ? row : rows_end - 1;
                 const uint4 *src = kbase + (int64_t)row * (P * LPR);
 #pragma unroll
-                for (int p = 0; p < P; ++p) kr[uu][p] = src[p * LPR + sl];
+                for (int p = 0; p < P; ++p) kr[uu][p] = load_row16<NTL>(src + p * LPR + sl);
             }
 #pragma unroll
             for (int u4 = 0; u4 < U; u4 += 4) {
@@ -147,15 +156,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
             }
         }
     }
-    // Best key per query over the block: lanes of the same query are LPR apart, then the waves.
+    // Best key per query over each block: lanes of the same query are LPR apart, then the
+    // block's 4 wavefronts (0 for a block without candidate rows).
     best = lane_max_stride<LPR>(best);
     if (lane < LPR && writer) red[wave][my_t] = best;
     __syncthreads();
-    if (tid < G) {
-        uint32_t m = 0u;
+    if (tid < BW * G) {
+        const int b2 = tid / G, t = tid % G;
+        const int bi2 = (int)(wg - uu32 * wpb) * BW + b2;
+        if (bi2 < a.nblk) {
+            uint32_t m = 0u;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) m = red[w][tid] > m ? red[w][tid] : m;
-        bout[tid] = m;
+            for (int w = 0; w < 4; ++w) m = red[4 * b2 + w][t] > m ? red[4 * b2 + w][t] : m;
+            a.bmax[((size_t)u * a.nblk + bi2) * G + t] = m;
+        }
     }
 }
 
@@ -174,10 +188,10 @@ hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void 
     a.keys = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.keys_offset);
     a.bmax = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.bmax_offset);
     a.tmax = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.tmax_offset);
-    dim3 grid((unsigned)(pl.units * pl.nblk)), block(256);
+    dim3 grid((unsigned)(pl.units * ((pl.nblk + kKeysBW - 1) / kKeysBW))), block(256 * kKeysBW);
 #define CA_LAUNCH_SK(T, D, G) \
-    hipLaunchKernelGGL((score_keys_kernel<T, D, G>), grid, block, 0, s, static_cast<const T *>(q), \
-                       static_cast<const T *>(k), a)
+    hipLaunchKernelGGL((score_keys_kernel<T, D, G, kKeysBW, kKeysNT>), grid, block, 0, s,       \
+                       static_cast<const T *>(q), static_cast<const T *>(k), a)
 #define CA_LAUNCH_SK_G(T, D)                          \
     do {                                              \
         if (pl.G == 4) CA_LAUNCH_SK(T, D, 4);         \
