@@ -357,8 +357,13 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     uint64_t *sel = reinterpret_cast<uint64_t *>(fsm + 3 * a.cap + (a.cap & 1));
 
     const int tid = threadIdx.x;
+    // Query vector qv = (b*Hq + h)*nq + r (32-bit math: the plan keeps qv below 2^24).
     const int64_t qv = blockIdx.x;
-    const int64_t r = qv % a.nq;
+    const uint32_t nq32 = (uint32_t)a.nq, hq32 = (uint32_t)a.Hq, g32 = (uint32_t)a.g;
+    const uint32_t bh = (uint32_t)qv / nq32;
+    const int64_t r = (uint32_t)qv - bh * nq32;
+    const uint32_t b = bh / hq32, h = bh - b * hq32;
+    const uint32_t kvh = h / g32;
     const int64_t i = a.n - a.nq + r;
     const int64_t wlo = (i - a.W + 1 > 0) ? i - a.W + 1 : 0;
     const int64_t rl = i - a.W;
@@ -370,13 +375,10 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     if (kp > 0) {
         if constexpr (TILES) {
             // Unit and slot of this query vector: vector index r*g + (h - kvh*g) of its KV head.
-            const int64_t bh = qv / a.nq;
-            const int h = (int)(bh % a.Hq);
-            const int b = (int)(bh / a.Hq);
-            const int kvh = h / a.g;
-            const int64_t idx = r * a.g + (h - kvh * a.g);
-            const int64_t u = ((int64_t)b * a.Hkv + kvh) * a.groups + idx / a.G;
-            const int t = (int)(idx % a.G);
+            const uint32_t idx = (uint32_t)r * g32 + (h - kvh * g32);
+            const uint32_t gq = idx / (uint32_t)a.G;
+            const int64_t u = ((int64_t)b * a.Hkv + kvh) * a.groups + gq;
+            const int t = (int)(idx - gq * (uint32_t)a.G);
             const int64_t ntq = a.rstride / a.tile_rows;
             select_tiles<NT>(a.keys + ((size_t)u * a.G + t) * a.rstride,
                              a.tmax + ((size_t)u * a.G + t) * ntq,
@@ -395,10 +397,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     int32_t *row = out_idx + qv * a.cap;
     for (int t = tid; t < a.cap; t += NT) row[t] = t < count ? js[t] : -1;
     if constexpr (ATTEND) {
-        const int64_t bh = qv / a.nq;
-        const int h = (int)(bh % a.Hq);
-        const int b = (int)(bh / a.Hq);
-        const size_t kv0 = ((size_t)b * a.Hkv + h / a.g) * (size_t)a.n * D;
+        const size_t kv0 = ((size_t)b * a.Hkv + kvh) * (size_t)a.n * D;
         attend_set<NT, D, T>(q + qv * D, k + kv0, v + kv0, js, sc, count, a.n, a.scale_log2e,
                              out + qv * D, ash);
     }
@@ -416,11 +415,11 @@ __global__ __launch_bounds__(NT) void attend_kernel(const T *__restrict__ q, con
     int32_t *js = asm_;
     float *sc = reinterpret_cast<float *>(asm_ + a.cap);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t qv = blockIdx.x;
-    const int64_t r = qv % a.nq;
-    const int64_t bh = qv / a.nq;
-    const int h = (int)(bh % a.Hq);
-    const int b = (int)(bh / a.Hq);
+    const int64_t qv = blockIdx.x;  // (b*Hq + h)*nq + r, below 2^24
+    const uint32_t nq32 = (uint32_t)a.nq, hq32 = (uint32_t)a.Hq;
+    const uint32_t bh = (uint32_t)qv / nq32;
+    const int64_t r = (uint32_t)qv - bh * nq32;
+    const uint32_t b = bh / hq32, h = bh - b * hq32;
     const int64_t i = a.n - a.nq + r;
     const int32_t *row = idx + qv * a.cap;
 
