@@ -1,38 +1,35 @@
-// Restricted softmax times V for one query vector, executed by one workgroup of NT threads
-// (pages of "The Condensate Theorem", metaphor-xennon blog: section 2.3, Theorem 1's
-// Attention_C; section 3.2.4, the output evaluated over C_i alone).
+// Restricted softmax times V for one query vector on gfx950 (pages of "The Condensate Theorem",
+// metaphor-xennon blog: section 2.3, Theorem 1's Attention_C; section 3.2.4, the output
+// evaluated over C_i alone).
 //
-// The set is given as `count` positions js[0..count) in LDS. Every gathered row is loaded
-// with 16-byte loads: K rows 4 lanes per row (P loads each) for the fp32 dot products, V rows
-// LPR lanes per row for the accumulation. The V rows of the first block are requested before
-// the scores are reduced, so the two gathers overlap. Softmax in fp32: m = max s, w = exp(s-m),
-// l = sum w; out = sum w v / l. All reductions run in a fixed order (deterministic output).
+// The rows of a set are spread over wavefronts. A wavefront requests the K and V slices of its
+// rows together (16-byte loads, LPR = row bytes / 16 lanes per row, RPW = 64 / LPR rows per
+// load), computes the fp32 scores s = q . k_j, and keeps a partial result over its rows: the
+// largest score m, l = sum of exp2((s - m) * scale * log2 e) and acc = the sum of those
+// weights times the V rows. Partials of disjoint row subsets combine exactly: with M the largest
+// m_p and f_p = exp2((m_p - M) * scale * log2 e), out = sum f_p acc_p / sum f_p l_p, the softmax
+// over the union. Every sum runs in a fixed order (deterministic output, no atomics).
 #pragma once
 
 #include "device_utils.h"
 
 namespace ca {
 
-template <int NT, int D, typename T>
+template <int D, typename T>
 struct AttendShape {
-    static constexpr int NW = NT / 64;
-    static constexpr int EB = sizeof(T);
-    static constexpr int RB = D * EB;     // bytes per row
-    static constexpr int P = RB / 64;     // scoring: 16-byte loads per lane, 4 lanes per row
-    static constexpr int KSTEP = 16 * NW; // rows scored per workgroup step
-    static constexpr int KU = P >= 8 ? 1 : 2;  // scoring steps in flight
-    static constexpr int LPR = RB / 16;   // accumulation: lanes per row
-    static constexpr int RPW = 64 / LPR;  // accumulation: rows per wavefront load
-    static constexpr int EPL = 16 / EB;   // elements per 16-byte slice
-    static constexpr int VU = NT >= 1024 ? 8 : 16;  // V loads in flight per lane
-    static constexpr int VBLOCK = VU * NW * RPW;    // V rows per block
+    static constexpr int RB = D * (int)sizeof(T);  // bytes per row
+    static constexpr int LPR = RB / 16;            // lanes per row, one 16-byte slice each
+    static constexpr int RPW = 64 / LPR;           // rows per wavefront load
+    static constexpr int EPL = 16 / (int)sizeof(T);  // elements per slice
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row size");
 };
 
-// LDS the attend core needs besides js[] and sc[] (both sized by the caller).
-template <int NT, int D, typename T>
-struct AttendShared {
-    float red[AttendShape<NT, D, T>::NW];
-    float part[AttendShape<NT, D, T>::NW][D];
+// NP partial results in LDS: acc[p][0..D), the largest score m[p] (-inf: no rows) and the weight
+// sum l[p]; f[p] is the merge factor.
+template <int D, int NP>
+struct SoftmaxPartials {
+    float acc[NP][D];
+    float m[NP], l[NP], f[NP];
 };
 
 __device__ __forceinline__ void accumulate16(float *acc, const uint4 &v, float w, __bf16) {
@@ -50,119 +47,164 @@ __device__ __forceinline__ void accumulate16(float *acc, const uint4 &v, float w
     acc[3] = fmaf(w, __uint_as_float(v.w), acc[3]);
 }
 
-// qrow: this query's row; kbase/vbase: row 0 of its KV head in K and V (nrows rows); js/sc:
-// LDS arrays of >= count entries (sc is overwritten); positions are clamped into [0, nrows) for
-// addressing. Must be called by all NT threads, count uniform and >= 1.
-template <int NT, int D, typename T>
-__device__ __forceinline__ void attend_set(const T *__restrict__ qrow, const T *__restrict__ kbase,
-                           const T *__restrict__ vbase, const int32_t *js, float *sc, int count,
-                           int64_t nrows, float scale_log2e, float *__restrict__ out,
-                           AttendShared<NT, D, T> &sh) {
-    auto row_of = [&](int c) -> size_t {
-        const uint32_t j = (uint32_t)js[c];
-        return (size_t)(j < (uint64_t)nrows ? j : (uint32_t)(nrows - 1));
-    };
-    using S = AttendShape<NT, D, T>;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int s4 = lane & 3;
-    const int slot = lane / S::LPR, cs = lane % S::LPR;
-
-    uint4 qr[S::P];
-    {
-        const uint4 *qsrc = reinterpret_cast<const uint4 *>(qrow);
-#pragma unroll
-        for (int p = 0; p < S::P; ++p) qr[p] = qsrc[p * 4 + s4];
+// Sum over the LPR lanes of a row (every lane of the row gets it): DPP mirrors and quad
+// exchanges inside rows of 16 lanes, the gfx950 permlane16 swap across two of them.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+    if constexpr (LPR >= 16) x += dpp_mirror16(x);
+    x += dpp_half_mirror(x);
+    x += dpp_xor2(x);
+    x += dpp_xor1(x);
+    if constexpr (LPR == 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
-    // V rows of the first block, requested now so that they arrive while scores are computed.
-    uint4 vr[S::VU];
-#pragma unroll
-    for (int u = 0; u < S::VU; ++u) {
-        const int c = (u * S::NW + wave) * S::RPW + slot;
-        if (c < count) vr[u] = reinterpret_cast<const uint4 *>(vbase + row_of(c) * D)[cs];
-    }
+    return x;
+}
 
-    // Scores: raw fp32 dot products, 4 lanes per row.
-    for (int c0 = 0; c0 < count; c0 += S::KSTEP * S::KU) {
-        uint4 kr[S::KU][S::P];
+// K and V slices of U rows per lane: rows c = c0 + u*step + slot (slot = lane / LPR) of a row
+// list row_at(c), c in [0, count); rows past the end are clamped to the last one (loaded,
+// ignored). Issued together, consumed by accumulate_rows.
+template <int D, typename T, int U>
+struct RowSlices {
+    uint4 k[U], v[U];
+};
+
+template <int D, typename T, int U, typename RowAt>
+__device__ __forceinline__ void load_rows(RowSlices<D, T, U> &rs, const T *__restrict__ kbase,
+                                          const T *__restrict__ vbase, RowAt row_at, int count,
+                                          int c0, int step) {
+    using S = AttendShape<D, T>;
+    const int lane = threadIdx.x & 63, slot = lane / S::LPR, cs = lane % S::LPR;
 #pragma unroll
-        for (int u = 0; u < S::KU; ++u) {
-            int c = c0 + u * S::KSTEP + wave * 16 + (lane >> 2);
-            c = c < count ? c : count - 1;
-            const uint4 *src = reinterpret_cast<const uint4 *>(kbase + row_of(c) * D);
+    for (int u = 0; u < U; ++u) {
+        int c = c0 + u * step + slot;
+        c = c < count ? c : count - 1;
+        const size_t row = row_at(c);
+        rs.k[u] = reinterpret_cast<const uint4 *>(kbase + row * D)[cs];
+        rs.v[u] = reinterpret_cast<const uint4 *>(vbase + row * D)[cs];
+    }
+}
+
+// Running softmax state of one row slot of a wavefront.
+template <int D, typename T>
+struct SlotState {
+    float m = -INFINITY, l = 0.f, acc[AttendShape<D, T>::EPL] = {};
+};
+
+// Adds the rows of rs whose index passes use(c) to the slot state.
+template <int D, typename T, int U, typename Use>
+__device__ __forceinline__ void accumulate_rows(SlotState<D, T> &st, const RowSlices<D, T, U> &rs,
+                                                const uint4 &qs, Use use, int c0, int step,
+                                                float scale_log2e) {
+    using S = AttendShape<D, T>;
+    const int slot = (threadIdx.x & 63) / S::LPR;
+    float s[U];
+    bool ok[U];
+    float mr = st.m;
 #pragma unroll
-            for (int p = 0; p < S::P; ++p) kr[u][p] = src[p * 4 + s4];
+    for (int u = 0; u < U; ++u) {
+        s[u] = row_sum<S::LPR>(dot16(rs.k[u], qs, 0.f, T()));
+        ok[u] = use(c0 + u * step + slot);
+        if (ok[u]) mr = fmaxf(mr, s[u]);
+    }
+    // Rescale what the slot holds to the new maximum (nothing held: m = -inf).
+    const float f = st.m == -INFINITY ? 0.f : exp2f((st.m - mr) * scale_log2e);
+    st.l *= f;
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) st.acc[e] *= f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (ok[u]) {
+            const float w = exp2f((s[u] - mr) * scale_log2e);
+            st.l += w;
+            accumulate16(st.acc, rs.v[u], w, T());
         }
-#pragma unroll
-        for (int u = 0; u < S::KU; ++u) {
-            float x = 0.f;
-#pragma unroll
-            for (int p = 0; p < S::P; ++p) x = dot16(kr[u][p], qr[p], x, T());
-            x += dpp_xor2(x);
-            x += dpp_xor1(x);
-            const int c = c0 + u * S::KSTEP + wave * 16 + (lane >> 2);
-            if (s4 == 0 && c < count) sc[c] = x;
-        }
     }
-    __syncthreads();
+    st.m = mr;
+}
 
-    // Softmax weights over the set.
-    float m = -INFINITY;
-    for (int c = tid; c < count; c += NT) m = fmaxf(m, sc[c]);
-    m = wave_max_f32(m);
-    if (lane == 0) sh.red[wave] = m;
-    __syncthreads();
-    m = sh.red[0];
-#pragma unroll
-    for (int w2 = 1; w2 < S::NW; ++w2) m = fmaxf(m, sh.red[w2]);
-    __syncthreads();
-    float l = 0.f;
-    for (int c = tid; c < count; c += NT) {
-        const float w = exp2f((sc[c] - m) * scale_log2e);
-        sc[c] = w;
-        l += w;
-    }
-    l = wave_sum_f32(l);
-    if (lane == 0) sh.red[wave] = l;
-    __syncthreads();
-    l = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < S::NW; ++w2) l += sh.red[w2];
-
-    // sum_c w_c v_c, lane = (row slot, 16-byte column slice).
+// Merges the row slots of a wavefront (lanes LPR apart) and writes the result to partial p
+// (m = -inf, l = 0, acc = 0 when the wavefront had no rows). All 64 lanes, p uniform.
+template <int D, typename T, int NP>
+__device__ __forceinline__ void store_wave_partial(SlotState<D, T> st, float scale_log2e,
+                                                   SoftmaxPartials<D, NP> &out, int p) {
+    using S = AttendShape<D, T>;
+    const int lane = threadIdx.x & 63, cs = lane % S::LPR;
+    float mw = st.m;
+    if constexpr (S::LPR <= 8) mw = lane_pair_max<8>(mw);
+    if constexpr (S::LPR <= 16) mw = lane_pair_max<16>(mw);
+    mw = lane_pair_max<32>(mw);
+    const float f = st.m == -INFINITY ? 0.f : exp2f((st.m - mw) * scale_log2e);
+    float l = st.l * f;
     float acc[S::EPL];
 #pragma unroll
-    for (int e = 0; e < S::EPL; ++e) acc[e] = 0.f;
+    for (int e = 0; e < S::EPL; ++e) acc[e] = st.acc[e] * f;
+    if constexpr (S::LPR <= 8) {
+        l = lane_pair_sum<8>(l);
 #pragma unroll
-    for (int u = 0; u < S::VU; ++u) {
-        const int c = (u * S::NW + wave) * S::RPW + slot;
-        if (c < count) accumulate16(acc, vr[u], sc[c], T());
+        for (int e = 0; e < S::EPL; ++e) acc[e] = lane_pair_sum<8>(acc[e]);
     }
-    for (int vb = S::VBLOCK; vb < count; vb += S::VBLOCK) {
+    if constexpr (S::LPR <= 16) {
+        l = lane_pair_sum<16>(l);
 #pragma unroll
-        for (int u = 0; u < S::VU; ++u) {
-            const int c = vb + (u * S::NW + wave) * S::RPW + slot;
-            if (c < count) vr[u] = reinterpret_cast<const uint4 *>(vbase + row_of(c) * D)[cs];
-        }
-#pragma unroll
-        for (int u = 0; u < S::VU; ++u) {
-            const int c = vb + (u * S::NW + wave) * S::RPW + slot;
-            if (c < count) accumulate16(acc, vr[u], sc[c], T());
-        }
+        for (int e = 0; e < S::EPL; ++e) acc[e] = lane_pair_sum<16>(acc[e]);
     }
+    l = lane_pair_sum<32>(l);
 #pragma unroll
-    for (int off = S::LPR; off < 64; off <<= 1)
+    for (int e = 0; e < S::EPL; ++e) acc[e] = lane_pair_sum<32>(acc[e]);
+    if (lane < S::LPR) {
 #pragma unroll
-        for (int e = 0; e < S::EPL; ++e) acc[e] += __shfl_xor(acc[e], off);
-    if (slot == 0)
-#pragma unroll
-        for (int e = 0; e < S::EPL; ++e) sh.part[wave][cs * S::EPL + e] = acc[e];
+        for (int e = 0; e < S::EPL; ++e) out.acc[p][cs * S::EPL + e] = acc[e];
+    }
+    if (lane == 0) { out.m[p] = mw; out.l[p] = l; }
+}
+
+// Partial result of wavefront wv of nw over the rows row_at(c), c in [0, count): it takes rows
+// c = wv*RPW + slot + r*nw*RPW, U of them per lane in flight (K and V requested together). qs is
+// this lane's slice of the query (slice lane % LPR). kbase/vbase: row 0 of the KV head. The
+// result goes to partial p of *out. Must be called by all 64 lanes, wv and p uniform.
+template <int D, typename T, int U, int NP, typename RowAt>
+__device__ __forceinline__ void wave_partial(const uint4 &qs, const T *__restrict__ kbase,
+                                             const T *__restrict__ vbase, RowAt row_at, int count,
+                                             int wv, int nw, float scale_log2e,
+                                             SoftmaxPartials<D, NP> &out, int p) {
+    using S = AttendShape<D, T>;
+    SlotState<D, T> st;
+    const int step = nw * S::RPW;
+    auto use = [&](int c) { return c < count; };
+    for (int c0 = wv * S::RPW; c0 < count; c0 += U * step) {
+        RowSlices<D, T, U> rs;
+        load_rows<D, T, U>(rs, kbase, vbase, row_at, count, c0, step);
+        accumulate_rows<D, T, U>(st, rs, qs, use, c0, step, scale_log2e);
+    }
+    store_wave_partial<D, T>(st, scale_log2e, out, p);
+}
+
+// out[0..D) from partials p0..p1-1 (at most 64 of them, all written, at least one row in all),
+// combined in index order: wavefront 0 turns their m[p], l[p] into normalised factors
+// f[p] = exp2((m[p] - M) * scale_log2e) / L, then each column sums f[p] acc[p][t]. Called by all
+// NT threads after the partials are visible.
+template <int NT, int D, int NP>
+__device__ __forceinline__ void merge_partials(SoftmaxPartials<D, NP> &ps, int p0, int p1,
+                                               float scale_log2e, float *__restrict__ out) {
+    static_assert(NP <= 64, "partials");
+    const int tid = threadIdx.x, lane = tid & 63;
+    if (tid < 64) {
+        const int p = p0 + lane;
+        const float m = p < p1 ? ps.m[p] : -INFINITY;
+        const float l = p < p1 ? ps.l[p] : 0.f;
+        const float mx = wave_max_f32_dpp(m);
+        const float f = m == -INFINITY ? 0.f : exp2f((m - mx) * scale_log2e);
+        const float lsum = wave_sum_f32_dpp(l * f);
+        if (p < p1) ps.f[p] = f / lsum;
+    }
     __syncthreads();
-    const float inv_l = 1.0f / l;
     for (int t = tid; t < D; t += NT) {
-        float sum = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < S::NW; ++w2) sum += sh.part[w2][t];
-        out[t] = sum * inv_l;
+        float o = 0.f;
+#pragma unroll 8
+        for (int p = p0; p < p1; ++p) o = fmaf(ps.acc[p][t], ps.f[p], o);
+        out[t] = o;
     }
 }
 

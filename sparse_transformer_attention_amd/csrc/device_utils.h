@@ -72,6 +72,37 @@ __device__ __forceinline__ uint32_t lane_max_stride(uint32_t x) {
     return lane_max_xor32(x);
 }
 
+// x(lane) op x(lane ^ OFF) for OFF = 8 (DPP row_ror:8 inside rows of 16 lanes), 16 or 32
+// (gfx950 permlane swaps); every lane gets the result.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float x, float &a, float &b) {
+    static_assert(OFF == 8 || OFF == 16 || OFF == 32, "offset");
+    if constexpr (OFF == 8) {
+        a = x;
+        b = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    } else if constexpr (OFF == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    }
+}
+template <int OFF>
+__device__ __forceinline__ float lane_pair_sum(float x) {
+    float a, b;
+    lane_pair<OFF>(x, a, b);
+    return a + b;
+}
+template <int OFF>
+__device__ __forceinline__ float lane_pair_max(float x) {
+    float a, b;
+    lane_pair<OFF>(x, a, b);
+    return fmaxf(a, b);
+}
+
 // Order-preserving map of a float32 score to uint32 (larger score -> larger key); -0 is
 // folded onto +0 so that equal scores give equal keys. Every finite score maps to a key
 // >= 0x00800000, so 0 is free to mean "no candidate".
@@ -163,6 +194,31 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
     return x;
+}
+
+// Maximum / sum of a float over the 64 lanes (result uniform): DPP rotations inside rows of 16,
+// then the 4 row results.
+__device__ __forceinline__ float wave_max_f32_dpp(float x) {
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_sum_f32_dpp(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // Orders LDS traffic between the lanes of one wavefront (no workgroup barrier).

@@ -22,11 +22,12 @@ struct FinishArgs {
     const uint32_t *cnt;    // [nqv][wpu] keys in each segment
     const uint64_t *lists;  // [nqv][wpu][topk] segments of candidate ranking keys
     // Key-buffer path (score_keys): units of G query vectors, blocks and tiles of key rows.
-    int G, nblk, tile_rows;
+    int G, nblk, tile_shift;  // rows per tile: 1 << tile_shift
     int64_t groups, rstride;
     const uint32_t *keys;   // [units][G][rstride]
     const uint32_t *bmax;   // [units][nblk][G]
     const uint32_t *tmax;   // [units][G][rstride / tile_rows]
+    const float *wpart;     // [nqv][D + 4]: anchor-and-window partials (m, l, -, -, acc[D])
 };
 
 constexpr int kGather = 1024;  // candidates gathered into LDS for the one-wavefront select
@@ -171,12 +172,14 @@ __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at,
 }
 
 // Candidates from the segments score_topk left (the first cnt[w] keys of each segment w of
-// lists[w][0..topk)), gathered into LDS by wavefront 0; then the exact top-kp.
-template <int NT>
+// lists[w][0..topk)), gathered into LDS by wavefront 0 while the other wavefronts run
+// overlap(); then the exact top-kp.
+template <int NT, typename Overlap>
 __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt,
                                                 const uint64_t *__restrict__ lists, int wpu,
                                                 int topk, int kp, int32_t *js, uint64_t *sel,
-                                                uint64_t *gathered, SelectShared<NT> &sh) {
+                                                uint64_t *gathered, SelectShared<NT> &sh,
+                                                Overlap overlap) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (wave == 0) {
         int base = 0;
@@ -190,6 +193,8 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
             base += tot;
         }
         if (lane == 0) sh.sel_count = base;
+    } else {
+        overlap();
     }
     __syncthreads();
     const int n = sh.sel_count;
@@ -207,70 +212,78 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
 // it, so it is a lower bound of its k-th key); the keys of every tile whose best key reaches the
 // bound are gathered into LDS; then the exact top-kp. keys/tmax point at the query's rows, bm at
 // its first block maximum (stride G); the query's candidate rows are 1..rl. tiles is LDS for
-// kTileCap tile indices.
+// kTileCap tile indices. The other wavefronts run overlap() while wavefront 0 takes the bound.
 constexpr int kTileCap = 1024;
 constexpr int kRankSelectMax = 256;  // candidates selected by rank counting (else radix select)
 
-template <int NT>
+template <int NT, typename Overlap>
 __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ keys,
                                              const uint32_t *__restrict__ tmax,
                                              const uint32_t *__restrict__ bm, int G, int nblk,
-                                             int tile_rows, int64_t rl, int kp, int32_t *js,
+                                             int tile_shift, int rl, int kp, int32_t *js,
                                              uint64_t *sel, uint64_t *gathered, int32_t *tiles,
-                                             SelectShared<NT> &sh) {
+                                             SelectShared<NT> &sh, Overlap overlap) {
     constexpr int E = 8;   // block maxima per lane: at most 512 (merged in groups beyond)
     constexpr int TU = 8;  // tile maxima in flight per thread
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rpg = tile_rows / 4;
-    const int64_t ntiles = (rl + tile_rows) / tile_rows;  // tiles covering rows 0..rl
+    // 32-bit indices: a query's key rows are fewer than 2^31.
+    const int tile_rows = 1 << tile_shift, rpg = tile_rows >> 2;
+    const int ntiles = (rl + tile_rows) >> tile_shift;  // tiles covering rows 0..rl
     // First tile maxima requested before the bound is known.
     uint32_t tm[TU];
 #pragma unroll
     for (int e = 0; e < TU; ++e) {
-        const int64_t j = tid + (int64_t)NT * e;
-        tm[e] = j < ntiles ? tmax[j] : 0u;
+        const int j = tid + NT * e;
+        tm[e] = tmax[j < ntiles ? j : 0];
     }
     if (wave == 0) {
         // Maxima of disjoint groups of rows: the blocks (256 rows), or the tiles when there are
         // fewer than 2k' blocks; merged into at most 64*E groups of consecutive ones.
-        const bool by_tile = (int64_t)nblk < 2 * (int64_t)kp;
+        const bool by_tile = nblk < 2 * kp;
         const uint32_t *src = by_tile ? tmax : bm;
-        const int64_t stride = by_tile ? 1 : G;
-        const int64_t count = by_tile ? ntiles : nblk;
-        const int per = (int)((count + 64 * E - 1) / (64 * E));
-        const int64_t ngr = (count + per - 1) / per;
+        const int stride = by_tile ? 1 : G;
+        const int count = by_tile ? ntiles : nblk;
+        const int per = (count + 64 * E - 1) / (64 * E);
+        const int ngr = per == 1 ? count : (int)(((uint32_t)count + per - 1) / (uint32_t)per);
         uint32_t m[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) m[e] = 0u;
-        for (int jj = 0; jj < per; ++jj) {  // E independent loads per pass
+        for (int jj = 0; jj < per; ++jj) {  // E independent loads per pass, all issued first
+            uint32_t x[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const int64_t gi = lane + 64 * e, grp = gi * per + jj;
-                if (gi < ngr && grp < count) {
-                    const uint32_t x = src[grp * stride];
-                    m[e] = x > m[e] ? x : m[e];
-                }
+                const int gi = lane + 64 * e, grp = gi * per + jj;
+                x[e] = src[(gi < ngr && grp < count ? grp : 0) * stride];
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int gi = lane + 64 * e, grp = gi * per + jj;
+                if (gi < ngr && grp < count) m[e] = x[e] > m[e] ? x[e] : m[e];
             }
         }
         const uint32_t thr = wave_bound_u32(m, kp, &sh.hist[0][0]);
         if (lane == 0) { sh.pick[0] = thr > 1u ? thr : 1u; sh.pick[1] = 0u; sh.sel_count = 0; }
+    } else {
+        overlap();
     }
     __syncthreads();
     const uint32_t thr = sh.pick[0];
-    // Tiles whose best key reaches the bound, compacted into tiles[].
-    for (int64_t j0 = tid;; j0 += (int64_t)NT * TU) {
+    // Tiles whose best key reaches the bound, compacted into tiles[] (in any order: the
+    // selection does not depend on it). jb is uniform.
+    for (int jb = 0;; jb += NT * TU) {
+        const int j0 = jb + tid;
 #pragma unroll
         for (int e = 0; e < TU; ++e) {
-            if (tm[e] >= thr) {
+            if (tm[e] >= thr && j0 + NT * e < ntiles) {
                 const uint32_t at = atomicAdd(&sh.pick[1], 1u);
-                if (at < (uint32_t)kTileCap) tiles[at] = (int32_t)(j0 + (int64_t)NT * e);
+                if (at < (uint32_t)kTileCap) tiles[at] = j0 + NT * e;
             }
         }
-        if (j0 + (int64_t)NT * TU >= ntiles) break;
+        if (jb + NT * TU >= ntiles) break;
 #pragma unroll
         for (int e = 0; e < TU; ++e) {
-            const int64_t j = j0 + (int64_t)NT * (TU + e);
-            tm[e] = j < ntiles ? tmax[j] : 0u;
+            const int j = j0 + NT * (TU + e);
+            tm[e] = tmax[j < ntiles ? j : 0];
         }
     }
     __syncthreads();
@@ -278,15 +291,15 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ keys,
     if (nt <= kTileCap) {
         // Their keys, one 16-byte word per thread (position p of a tile holds row
         // rpg*(p%4) + p/4 of the tile), the ones that reach the bound gathered.
-        const int wpt = tile_rows / 4;
-        for (int x = tid; x < nt * wpt; x += NT) {
-            const int64_t tile0 = (int64_t)tiles[x / wpt] * tile_rows;
-            const int w4 = x % wpt;
+        const int wshift = tile_shift - 2;  // words per tile: tile_rows / 4
+        for (int x = tid; x < (nt << wshift); x += NT) {
+            const int tile0 = tiles[x >> wshift] << tile_shift;
+            const int w4 = x & (rpg - 1);
             const uint4 v = *reinterpret_cast<const uint4 *>(keys + tile0 + 4 * w4);
             const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int64_t row = tile0 + rpg * c + w4;
+                const int row = tile0 + rpg * c + w4;
                 if (kv[c] >= thr && row >= 1 && row <= rl) {
                     const int pos = atomicAdd(&sh.sel_count, 1);
                     if (pos < kGather) gathered[pos] = make_rank_key(kv[c], (uint32_t)row);
@@ -301,62 +314,72 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ keys,
     __syncthreads();
     if (n <= kRankSelectMax && n >= kp) {
         // Few candidates: a key is selected when fewer than kp keys beat it; the selected
-        // positions are then placed by their rank among the selected ones (ascending).
-        uint64_t x = 0ull;
-        bool chosen = false;
-        if (tid < n) {
-            x = gathered[tid];
-            int above = 0;
-#pragma unroll 8
-            for (int f = 0; f < n; ++f) above += gathered[f] > x;
-            chosen = above < kp;
+        // positions are then placed by their rank among the selected ones (ascending). S lanes
+        // per candidate (S*n <= NT, S <= 16): lane s compares against keys s, s+S, ..., and the S
+        // counts are summed.
+        int lg = 4;
+        while (lg > 0 && (n << lg) > NT) --lg;
+        const int S = 1 << lg, c = tid >> lg, sl = tid & (S - 1);
+        const bool mine = c < n;
+        const uint64_t x = gathered[mine ? c : 0];
+        int above = 0;
+        if (mine) {
+#pragma unroll 4
+            for (int f = sl; f < n; f += S) above += gathered[f] > x;
         }
+        for (int off = 1; off < S; off <<= 1) above += __shfl_xor(above, off);
+        const bool chosen = mine && above < kp;
+        // Selected keys (0 = not) in the tail of gathered[], clear of [0, n).
+        if (mine && sl == 0) gathered[kGather - 1 - c] = chosen ? x : 0ull;
         __syncthreads();
-        if (tid < n) gathered[kGather - 1 - tid] = chosen ? x : 0ull;  // selected keys (0 = not)
-        __syncthreads();
+        const int32_t pos = rank_key_pos(x);
+        int rank = 0;
         if (chosen) {
-            const int32_t pos = rank_key_pos(x);
-            int rank = 0;
-#pragma unroll 8
-            for (int f = 0; f < n; ++f) {
+#pragma unroll 4
+            for (int f = sl; f < n; f += S) {
                 const uint64_t y = gathered[kGather - 1 - f];
                 rank += y != 0ull && rank_key_pos(y) < pos;
             }
-            js[rank] = pos;
         }
+        for (int off = 1; off < S; off <<= 1) rank += __shfl_xor(rank, off);
+        if (chosen && sl == 0) js[rank] = pos;
         __syncthreads();
         return;
     }
     // More than kGather candidates (ties at the bound): every key of rows 1..rl that reaches it.
-    auto key_at = [&](int64_t f) -> uint64_t {
-        const int64_t tile0 = f - f % tile_rows;
-        const int p = (int)(f - tile0);
-        const int64_t row = tile0 + rpg * (p % 4) + p / 4;
+    auto key_at = [&](int64_t f64) -> uint64_t {
+        const int f = (int)f64;
+        const int tile0 = f & ~(tile_rows - 1);
+        const int p = f - tile0;
+        const int row = tile0 + rpg * (p & 3) + (p >> 2);
         const uint32_t kv = keys[f];
         return (row >= 1 && row <= rl && kv >= thr) ? make_rank_key(kv, (uint32_t)row) : 0ull;
     };
-    select_exact<NT>(n, ntiles * tile_rows, key_at, kp, js, sel, gathered, sh);
+    select_exact<NT>(n, (int64_t)ntiles << tile_shift, key_at, kp, js, sel, gathered, sh);
 }
+
+// Rows per lane in flight for the window part and for the top-k part of the attend phase.
+constexpr int kWindowU = 8;
+constexpr int kTopU = 2;
 
 template <typename T, int D, int NT, bool ATTEND, bool TILES>
 __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                     const T *__restrict__ v,
                                                     int32_t *__restrict__ out_idx,
                                                     float *__restrict__ out, FinishArgs a) {
-    extern __shared__ int32_t fsm[];  // js[2*cap] positions, sc[cap] scores, sel[topk] keys
-    __shared__ union {
-        SelectShared<NT> sel;
-        AttendShared<NT, D, T> att;
-    } shu;  // the select and the attend phases never overlap
-    SelectShared<NT> &ssh = shu.sel;
-    AttendShared<NT, D, T> &ash = shu.att;
+    constexpr int NW = NT / 64;
+    extern __shared__ int32_t fsm[];  // js[2*cap] positions, then sel[topk] keys
+    __shared__ SelectShared<NT> ssh;
     __shared__ uint64_t gathered[kGather];
     __shared__ int32_t tile_idx[TILES ? kTileCap : 1];
+    // Softmax partials: [0, NW) the anchor and window rows (wavefronts 1..NW-1 when wavefront 0
+    // takes the bound; NW-1 alone when precomputed), [NW, 2NW) the top-k rows.
+    __shared__ SoftmaxPartials<D, ATTEND ? 2 * NW : 1> part;
     int32_t *js = fsm;
-    float *sc = reinterpret_cast<float *>(fsm + 2 * a.cap);
-    uint64_t *sel = reinterpret_cast<uint64_t *>(fsm + 3 * a.cap + (a.cap & 1));
+    uint64_t *sel = reinterpret_cast<uint64_t *>(fsm + 2 * a.cap);
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // Query vector qv = (b*Hq + h)*nq + r (32-bit math: the plan keeps qv below 2^24).
     const int64_t qv = blockIdx.x;
     const uint32_t nq32 = (uint32_t)a.nq, hq32 = (uint32_t)a.Hq, g32 = (uint32_t)a.g;
@@ -369,27 +392,51 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     const int64_t rl = i - a.W;
     const int64_t n_r = rl >= 1 ? rl : 0;
     const int kp = (int)(a.topk < n_r ? a.topk : n_r);
-
     // js layout: [0 if the anchor is separate][top-k' ascending][window ascending]
     const int base = wlo > 0 ? 1 : 0;
+    const int wcount = (int)(i - wlo + 1);
+
+    // Attend over the anchor and the window: the rows are known from the start, so they are
+    // processed by the wavefronts that do not take the bound (all of them when there is no
+    // top-k part). With the key buffer, the scoring kernel has computed this part already: one
+    // wavefront copies it into partial NW-1.
+    const size_t kv0 = ((size_t)b * a.Hkv + kvh) * (size_t)a.n * D;
+    const T *kb = k + kv0, *vb = v + kv0;
+    uint4 qs = make_uint4(0, 0, 0, 0);
+    if constexpr (ATTEND) qs = reinterpret_cast<const uint4 *>(q + qv * D)[lane % AttendShape<D, T>::LPR];
+    auto window_part = [&](int wv, int nw) {
+        if constexpr (ATTEND && TILES) {
+            if (wv == 0) {
+                const float *src = a.wpart + qv * (D + 4);
+                for (int t = lane; t < D; t += 64) part.acc[NW - 1][t] = src[4 + t];
+                if (lane == 0) { part.m[NW - 1] = src[0]; part.l[NW - 1] = src[1]; }
+            }
+        } else if constexpr (ATTEND) {
+            auto row_at = [&](int c) -> size_t { return c < base ? 0 : (size_t)(wlo - base + c); };
+            wave_partial<D, T, kWindowU>(qs, kb, vb, row_at, base + wcount, wv, nw, a.scale_log2e,
+                                         part, wave);
+        }
+    };
     if (kp > 0) {
+        auto overlap = [&]() { window_part(wave - 1, NW - 1); };
         if constexpr (TILES) {
             // Unit and slot of this query vector: vector index r*g + (h - kvh*g) of its KV head.
             const uint32_t idx = (uint32_t)r * g32 + (h - kvh * g32);
             const uint32_t gq = idx / (uint32_t)a.G;
             const int64_t u = ((int64_t)b * a.Hkv + kvh) * a.groups + gq;
             const int t = (int)(idx - gq * (uint32_t)a.G);
-            const int64_t ntq = a.rstride / a.tile_rows;
+            const int64_t ntq = a.rstride >> a.tile_shift;
             select_tiles<NT>(a.keys + ((size_t)u * a.G + t) * a.rstride,
                              a.tmax + ((size_t)u * a.G + t) * ntq,
-                             a.bmax + (size_t)u * a.nblk * a.G + t, a.G, a.nblk, a.tile_rows, rl,
-                             kp, js + base, sel, gathered, tile_idx, ssh);
+                             a.bmax + (size_t)u * a.nblk * a.G + t, a.G, a.nblk, a.tile_shift,
+                             (int)rl, kp, js + base, sel, gathered, tile_idx, ssh, overlap);
         } else {
             select_segments<NT>(a.cnt + qv * a.wpu, a.lists + qv * a.wpu * a.topk, a.wpu, a.topk,
-                                kp, js + base, sel, gathered, ssh);
+                                kp, js + base, sel, gathered, ssh, overlap);
         }
+    } else {
+        window_part(wave, NW);
     }
-    const int wcount = (int)(i - wlo + 1);
     const int count = base + kp + wcount;
     if (tid == 0 && base) js[0] = 0;
     for (int t = tid; t < wcount; t += NT) js[base + kp + t] = (int32_t)(wlo + t);
@@ -397,9 +444,16 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     int32_t *row = out_idx + qv * a.cap;
     for (int t = tid; t < a.cap; t += NT) row[t] = t < count ? js[t] : -1;
     if constexpr (ATTEND) {
-        const size_t kv0 = ((size_t)b * a.Hkv + kvh) * (size_t)a.n * D;
-        attend_set<NT, D, T>(q + qv * D, k + kv0, v + kv0, js, sc, count, a.n, a.scale_log2e,
-                             out + qv * D, ash);
+        if (kp > 0) {
+            const int32_t *top = js + base;
+            auto row_at = [&](int c) -> size_t { return (size_t)(uint32_t)top[c]; };
+            wave_partial<D, T, kTopU>(qs, kb, vb, row_at, kp, wave, NW, a.scale_log2e, part, NW + wave);
+        }
+        __syncthreads();
+        // Window partials: NW-1 (precomputed), 1..NW-1 (wavefront 0 took the bound) or 0..NW-1;
+        // top-k partials NW..2NW-1.
+        const int p0 = TILES ? NW - 1 : (kp > 0 ? 1 : 0);
+        merge_partials<NT, D>(part, p0, kp > 0 ? 2 * NW : NW, a.scale_log2e, out + qv * D);
     }
 }
 
@@ -409,12 +463,12 @@ __global__ __launch_bounds__(NT) void attend_kernel(const T *__restrict__ q, con
                                                     const T *__restrict__ v,
                                                     const int32_t *__restrict__ idx,
                                                     float *__restrict__ out, FinishArgs a) {
-    extern __shared__ int32_t asm_[];  // js[cap], then sc[cap]
-    __shared__ int wave_cnt[NT / 64];
-    __shared__ AttendShared<NT, D, T> ash;
-    int32_t *js = asm_;
-    float *sc = reinterpret_cast<float *>(asm_ + a.cap);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NW = NT / 64;
+    extern __shared__ int32_t js[];  // js[cap]
+    __shared__ int wave_cnt[NW];
+    __shared__ SoftmaxPartials<D, NW> part;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t qv = blockIdx.x;  // (b*Hq + h)*nq + r, below 2^24
     const uint32_t nq32 = (uint32_t)a.nq, hq32 = (uint32_t)a.Hq;
     const uint32_t bh = (uint32_t)qv / nq32;
@@ -445,8 +499,13 @@ __global__ __launch_bounds__(NT) void attend_kernel(const T *__restrict__ q, con
         for (int t = tid; t < D; t += NT) o[t] = 0.f;
         return;
     }
-    const size_t kv0 = ((size_t)b * a.Hkv + h / a.g) * (size_t)a.n * D;
-    attend_set<NT, D, T>(q + qv * D, k + kv0, v + kv0, js, sc, count, a.n, a.scale_log2e, o, ash);
+    // Every listed position lies in [0, i], so it addresses a row of the KV head.
+    const size_t kv0 = ((size_t)b * a.Hkv + h / (uint32_t)a.g) * (size_t)a.n * D;
+    const uint4 qs = reinterpret_cast<const uint4 *>(q + qv * D)[lane % AttendShape<D, T>::LPR];
+    auto row_at = [&](int c) -> size_t { return (size_t)(uint32_t)js[c]; };
+    wave_partial<D, T, kTopU>(qs, k + kv0, v + kv0, row_at, count, wave, NW, a.scale_log2e, part, wave);
+    __syncthreads();
+    merge_partials<NT, D>(part, 0, NW, a.scale_log2e, o);
 }
 
 FinishArgs finish_args(const Plan &pl, const void *ws) {
@@ -456,11 +515,12 @@ FinishArgs finish_args(const Plan &pl, const void *ws) {
     a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
     a.cnt = ws ? static_cast<const uint32_t *>(ws) + 2 * pl.nqv * pl.wpu : nullptr;
     a.lists = ws ? reinterpret_cast<const uint64_t *>(static_cast<const char *>(ws) + pl.lists_offset) : nullptr;
-    a.G = pl.G; a.nblk = pl.nblk; a.tile_rows = pl.tile_rows; a.groups = pl.groups; a.rstride = pl.rstride;
+    a.G = pl.G; a.nblk = pl.nblk; a.tile_shift = pl.tile_rows == 32 ? 5 : 4; a.groups = pl.groups; a.rstride = pl.rstride;
     const char *wb = static_cast<const char *>(ws);
     a.keys = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.keys_offset) : nullptr;
     a.bmax = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.bmax_offset) : nullptr;
     a.tmax = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.tmax_offset) : nullptr;
+    a.wpart = (ws && pl.stream) ? reinterpret_cast<const float *>(wb + pl.wpart_offset) : nullptr;
     return a;
 }
 
@@ -471,12 +531,11 @@ template <typename T, int D, bool ATTEND>
 hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const void *k,
                            const void *v, int32_t *out_idx, float *out, hipStream_t s) {
     const FinishArgs a = finish_args(pl, ws);
-    const size_t shmem = (size_t)pl.cap * (3 * sizeof(int32_t)) + 8 + (size_t)pl.topk * sizeof(uint64_t);
+    const size_t shmem = (size_t)pl.cap * (2 * sizeof(int32_t)) + (size_t)pl.topk * sizeof(uint64_t);
     const dim3 grid((unsigned)pl.nqv);
     const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v);
-    const size_t fixed1024 = kGather * sizeof(uint64_t) +
-                             (sizeof(SelectShared<1024>) > sizeof(AttendShared<1024, D, T>)
-                                  ? sizeof(SelectShared<1024>) : sizeof(AttendShared<1024, D, T>));
+    const size_t fixed1024 = kGather * sizeof(uint64_t) + sizeof(SelectShared<1024>) +
+                             kTileCap * sizeof(int32_t) + sizeof(SoftmaxPartials<D, 32>);
     const bool wide = pl.nqv < kWideBelow && shmem + fixed1024 <= 64 * 1024;
 #define CA_LAUNCH_FIN(NT, TILES)                                                                  \
     hipLaunchKernelGGL((finish_kernel<T, D, NT, ATTEND, TILES>), grid, dim3(NT), shmem, s, qt, kt, vt, \
@@ -495,10 +554,10 @@ template <typename T, int D>
 hipError_t launch_attend_t(const Plan &pl, const void *q, const void *k, const void *v,
                            const int32_t *idx, float *out, hipStream_t s) {
     const FinishArgs a = finish_args(pl, nullptr);
-    const size_t shmem = (size_t)pl.cap * (sizeof(int32_t) + sizeof(float));
+    const size_t shmem = (size_t)pl.cap * sizeof(int32_t);
     const dim3 grid((unsigned)pl.nqv);
     const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v);
-    const bool wide = pl.nqv < kWideBelow && shmem + sizeof(AttendShared<1024, D, T>) <= 64 * 1024;
+    const bool wide = pl.nqv < kWideBelow && shmem + sizeof(SoftmaxPartials<D, 16>) <= 64 * 1024;
     if (wide)
         hipLaunchKernelGGL((attend_kernel<T, D, 1024>), grid, dim3(1024), shmem, s, qt, kt, vt, idx, out, a);
     else
