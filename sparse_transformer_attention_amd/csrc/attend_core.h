@@ -64,7 +64,8 @@ __device__ __forceinline__ float row_sum(float x) {
 
 // K and V slices of U rows per lane: rows c = c0 + u*step + slot (slot = lane / LPR) of a row
 // list row_at(c), c in [0, count); rows past the end are clamped to the last one (loaded,
-// ignored). Issued together, consumed by accumulate_rows.
+// ignored: every load is unconditional, so that all are in flight together). Issued together,
+// consumed by accumulate_rows.
 template <int D, typename T, int U>
 struct RowSlices {
     uint4 k[U], v[U];

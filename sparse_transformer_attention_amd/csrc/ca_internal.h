@@ -36,13 +36,12 @@ struct Plan {
     size_t ws_bytes;      // total workspace
     // Decode path (score_keys, then finish reading the key buffer): key rows per unit, blocks
     // of 256 rows per unit, and the offsets of the key buffer [units][G][rstride], the block
-    // maxima [units][nblk][G], the tile maxima [units][G][rstride / tile_rows] and the
-    // anchor-and-window softmax partials [nqv][d + 4] floats (m, l, -, -, acc[d]).
+    // maxima [units][nblk][G] and the tile maxima [units][G][rstride / tile_rows].
     bool stream;
     int64_t rstride;
     int nblk;
     int tile_rows;  // rows per key tile (one best key per tile and query)
-    size_t keys_offset, bmax_offset, tmax_offset, wpart_offset;
+    size_t keys_offset, bmax_offset, tmax_offset;
 };
 
 // Launchers (enqueue only; return the hipError_t of the last launch).
@@ -56,10 +55,7 @@ hipError_t launch_finish(const Plan &pl, const void *ws, const void *q, const vo
 hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k, const void *v,
                                     const int32_t *idx, float *out, hipStream_t s);
 size_t topk_lds_bytes(const Plan &pl);
-// Scores into the key buffer; with v != nullptr, also the anchor-and-window softmax partial of
-// every query vector (extra workgroups of the same grid).
-hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
-                             hipStream_t s);
+hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s);
 size_t stream_keys_bytes(const Plan &pl);
 
 }  // namespace ca

@@ -167,12 +167,7 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
             P.bmax_offset = P.keys_offset + keys_bytes;
             const size_t bmax_bytes = ((size_t)P.units * P.nblk * P.G * sizeof(uint32_t) + 255) & ~(size_t)255;
             P.tmax_offset = P.bmax_offset + bmax_bytes;
-            const size_t tmax_bytes = ((size_t)P.units * P.G * (P.rstride / P.tile_rows) * sizeof(uint32_t) + 255) & ~(size_t)255;
-            // Softmax partial over the anchor and the window of every query vector.
-            P.wpart_offset = P.tmax_offset + tmax_bytes;
-            P.ws_bytes = P.wpart_offset + (size_t)P.nqv * (P.d + 4) * sizeof(float);
-            if (P.nwg + P.units > (int64_t)UINT32_MAX / 256)
-                return fail(CA_ERR_UNSUPPORTED, "problem too large for one launch");
+            P.ws_bytes = P.tmax_offset + (size_t)P.units * P.G * (P.rstride / P.tile_rows) * sizeof(uint32_t);
             return CA_OK;
         }
     }
@@ -211,7 +206,7 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
     hipError_t e;
     if (pl.candidates && pl.stream) {
         ProfScope ps(K_SCORE, s);
-        e = ca::launch_score_keys(pl, q, k, out ? v : nullptr, ws, s);
+        e = ca::launch_score_keys(pl, q, k, ws, s);
         ps.done();
         if (e != hipSuccess) return hip_fail(e, "score_keys launch");
     } else if (pl.candidates) {

@@ -27,7 +27,6 @@ struct FinishArgs {
     const uint32_t *keys;   // [units][G][rstride]
     const uint32_t *bmax;   // [units][nblk][G]
     const uint32_t *tmax;   // [units][G][rstride / tile_rows]
-    const float *wpart;     // [nqv][D + 4]: anchor-and-window partials (m, l, -, -, acc[D])
 };
 
 constexpr int kGather = 1024;  // candidates gathered into LDS for the one-wavefront select
@@ -358,9 +357,12 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ keys,
     select_exact<NT>(n, (int64_t)ntiles << tile_shift, key_at, kp, js, sel, gathered, sh);
 }
 
-// Rows per lane in flight for the window part and for the top-k part of the attend phase.
-constexpr int kWindowU = 8;
-constexpr int kTopU = 2;
+
+// Rows per lane in flight in the attend phase (rows past the set's end are loaded as clamped
+// duplicates, so these match the common sizes: 15 wavefronts x 4 rows x 5 cover the anchor and
+// a window of up to 299 rows of 256 bytes in one round, 16 x 4 x 1 a top-64 part).
+constexpr int kWindowU = 5;
+constexpr int kTopU = 1;
 
 template <typename T, int D, int NT, bool ATTEND, bool TILES>
 __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, const T *__restrict__ k,
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     __shared__ uint64_t gathered[kGather];
     __shared__ int32_t tile_idx[TILES ? kTileCap : 1];
     // Softmax partials: [0, NW) the anchor and window rows (wavefronts 1..NW-1 when wavefront 0
-    // takes the bound; NW-1 alone when precomputed), [NW, 2NW) the top-k rows.
+    // takes the bound), [NW, 2NW) the top-k rows.
     __shared__ SoftmaxPartials<D, ATTEND ? 2 * NW : 1> part;
     int32_t *js = fsm;
     uint64_t *sel = reinterpret_cast<uint64_t *>(fsm + 2 * a.cap);
@@ -398,20 +400,13 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
 
     // Attend over the anchor and the window: the rows are known from the start, so they are
     // processed by the wavefronts that do not take the bound (all of them when there is no
-    // top-k part). With the key buffer, the scoring kernel has computed this part already: one
-    // wavefront copies it into partial NW-1.
+    // top-k part).
     const size_t kv0 = ((size_t)b * a.Hkv + kvh) * (size_t)a.n * D;
     const T *kb = k + kv0, *vb = v + kv0;
     uint4 qs = make_uint4(0, 0, 0, 0);
     if constexpr (ATTEND) qs = reinterpret_cast<const uint4 *>(q + qv * D)[lane % AttendShape<D, T>::LPR];
     auto window_part = [&](int wv, int nw) {
-        if constexpr (ATTEND && TILES) {
-            if (wv == 0) {
-                const float *src = a.wpart + qv * (D + 4);
-                for (int t = lane; t < D; t += 64) part.acc[NW - 1][t] = src[4 + t];
-                if (lane == 0) { part.m[NW - 1] = src[0]; part.l[NW - 1] = src[1]; }
-            }
-        } else if constexpr (ATTEND) {
+        if constexpr (ATTEND) {
             auto row_at = [&](int c) -> size_t { return c < base ? 0 : (size_t)(wlo - base + c); };
             wave_partial<D, T, kWindowU>(qs, kb, vb, row_at, base + wcount, wv, nw, a.scale_log2e,
                                          part, wave);
@@ -450,9 +445,9 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
             wave_partial<D, T, kTopU>(qs, kb, vb, row_at, kp, wave, NW, a.scale_log2e, part, NW + wave);
         }
         __syncthreads();
-        // Window partials: NW-1 (precomputed), 1..NW-1 (wavefront 0 took the bound) or 0..NW-1;
-        // top-k partials NW..2NW-1.
-        const int p0 = TILES ? NW - 1 : (kp > 0 ? 1 : 0);
+        // Window partials: 1..NW-1 (wavefront 0 took the bound) or 0..NW-1; top-k partials
+        // NW..2NW-1.
+        const int p0 = kp > 0 ? 1 : 0;
         merge_partials<NT, D>(part, p0, kp > 0 ? 2 * NW : NW, a.scale_log2e, out + qv * D);
     }
 }
@@ -503,7 +498,7 @@ __global__ __launch_bounds__(NT) void attend_kernel(const T *__restrict__ q, con
     const size_t kv0 = ((size_t)b * a.Hkv + h / (uint32_t)a.g) * (size_t)a.n * D;
     const uint4 qs = reinterpret_cast<const uint4 *>(q + qv * D)[lane % AttendShape<D, T>::LPR];
     auto row_at = [&](int c) -> size_t { return (size_t)(uint32_t)js[c]; };
-    wave_partial<D, T, kTopU>(qs, k + kv0, v + kv0, row_at, count, wave, NW, a.scale_log2e, part, wave);
+    wave_partial<D, T, 2>(qs, k + kv0, v + kv0, row_at, count, wave, NW, a.scale_log2e, part, wave);
     __syncthreads();
     merge_partials<NT, D>(part, 0, NW, a.scale_log2e, o);
 }
@@ -520,7 +515,6 @@ FinishArgs finish_args(const Plan &pl, const void *ws) {
     a.keys = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.keys_offset) : nullptr;
     a.bmax = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.bmax_offset) : nullptr;
     a.tmax = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.tmax_offset) : nullptr;
-    a.wpart = (ws && pl.stream) ? reinterpret_cast<const float *>(wb + pl.wpart_offset) : nullptr;
     return a;
 }
 
@@ -532,6 +526,7 @@ hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const 
                            const void *v, int32_t *out_idx, float *out, hipStream_t s) {
     const FinishArgs a = finish_args(pl, ws);
     const size_t shmem = (size_t)pl.cap * (2 * sizeof(int32_t)) + (size_t)pl.topk * sizeof(uint64_t);
+    const bool tiles = pl.stream && ws != nullptr;
     const dim3 grid((unsigned)pl.nqv);
     const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v);
     const size_t fixed1024 = kGather * sizeof(uint64_t) + sizeof(SelectShared<1024>) +
@@ -540,7 +535,6 @@ hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const 
 #define CA_LAUNCH_FIN(NT, TILES)                                                                  \
     hipLaunchKernelGGL((finish_kernel<T, D, NT, ATTEND, TILES>), grid, dim3(NT), shmem, s, qt, kt, vt, \
                        out_idx, out, a)
-    const bool tiles = pl.stream && ws != nullptr;
     if (wide) {
         if (tiles) CA_LAUNCH_FIN(1024, true); else CA_LAUNCH_FIN(1024, false);
     } else {

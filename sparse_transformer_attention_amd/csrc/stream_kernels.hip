@@ -18,12 +18,6 @@
 //
 // The finish kernel then takes, per query, the bound from the block maxima and reads only the
 // tiles whose best key reaches it.
-//
-// window workgroups (the first nwin of the grid, when the output is wanted): the anchor and the
-// window rows of a query are known before any score, so their part of the restricted softmax
-// (section 2.3, Attention over C_i) is computed here, one workgroup per unit, while the scoring
-// workgroups stream K; the finish kernel merges it with the top-k part.
-#include "attend_core.h"
 #include "ca_internal.h"
 #include "score_core.h"
 
@@ -45,66 +39,7 @@ struct KeysArgs {
     uint32_t *keys;   // [units][G][rstride], tiles as described above
     uint32_t *bmax;   // [units][nblk][G]
     uint32_t *tmax;   // [units][G][rstride / (4*RPG)]: best key of each tile
-    // Window workgroups: one per unit (0 when there are none).
-    uint32_t nwin;
-    float scale_log2e;
-    float *wpart;     // [nwin][D + 4]: m, l, -, -, acc[D] (unnormalised)
 };
-
-// Softmax partials of the query vectors of unit u (up to G, same KV head) over their anchors
-// (row 0, when outside the window) and window rows max(0, i-W+1)..i. The NT/64 wavefronts form
-// G groups, one per query vector (the vectors of a unit share most window rows, which the
-// groups then read through the same CU); each group's wavefront partials are combined into one
-// by the group's first wavefront.
-template <typename T, int D, int G, int NT>
-__device__ __forceinline__ void window_partials(const T *__restrict__ q, const T *__restrict__ k,
-                                                const T *__restrict__ v, const KeysArgs &a,
-                                                uint32_t u, SoftmaxPartials<D, NT / 64> &part) {
-    constexpr int NW = NT / 64, NWQ = NW / G;  // wavefronts per query vector
-    static_assert(NWQ >= 1 && NW % G == 0, "groups");
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t = wave / NWQ, wq = wave - t * NWQ;
-    const uint32_t g32 = (uint32_t)a.g, ng = (uint32_t)a.groups;
-    const uint32_t bk = u / ng, grp = u - bk * ng;  // bk = batch * Hkv + KV head
-    const uint32_t b = bk / (uint32_t)a.Hkv, kvh = bk - b * (uint32_t)a.Hkv;
-    const size_t kv0 = (size_t)bk * (size_t)a.n * D;
-    // Vector index of the KV head: head kvh*g + idx % g, row idx / g.
-    const uint32_t idx = grp * G + t;
-    const bool has = idx < a.nvec;
-    const uint32_t r = has ? idx / g32 : 0u, h = kvh * g32 + (idx - r * g32);
-    const uint32_t qv = (b * (uint32_t)a.Hq + h) * (uint32_t)a.nq + r;
-    if (has) {
-        const int64_t i = a.n - a.nq + r;
-        const int64_t wlo = i - a.W + 1 > 0 ? i - a.W + 1 : 0;
-        const int base = wlo > 0 ? 1 : 0;
-        const int count = base + (int)(i - wlo + 1);
-        const uint4 qs = reinterpret_cast<const uint4 *>(q + (size_t)qv * D)[lane % AttendShape<D, T>::LPR];
-        auto row_at = [&](int c) -> size_t { return c < base ? 0 : (size_t)(wlo - base + c); };
-        wave_partial<D, T, 4>(qs, k + kv0, v + kv0, row_at, count, wq, NWQ, a.scale_log2e, part, wave);
-    }
-    __syncthreads();
-    if (has && wq == 0) {
-        const int p0 = t * NWQ;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int p = 0; p < NWQ; ++p) mx = fmaxf(mx, part.m[p0 + p]);
-        float f[NWQ], lsum = 0.f;
-#pragma unroll
-        for (int p = 0; p < NWQ; ++p) {
-            f[p] = part.m[p0 + p] == -INFINITY ? 0.f : exp2f((part.m[p0 + p] - mx) * a.scale_log2e);
-            lsum = fmaf(part.l[p0 + p], f[p], lsum);
-        }
-        float *dst = a.wpart + (size_t)qv * (D + 4);
-        if (lane == 0) { dst[0] = mx; dst[1] = lsum; }
-        for (int c = lane; c < D; c += 64) {
-            float o = 0.f;
-#pragma unroll
-            for (int p = 0; p < NWQ; ++p) o = fmaf(part.acc[p0 + p][c], f[p], o);
-            dst[4 + c] = o;
-        }
-    }
-}
 
 // 16-byte load of a key-row slice; NTL: non-temporal (streamed once, kept out of the caches so
 // that the key buffer written meanwhile stays there).
@@ -117,7 +52,7 @@ __device__ __forceinline__ uint4 load_row16(const uint4 *p) {
 // BW blocks of 256 rows per workgroup (4 wavefronts each).
 template <typename T, int D, int G, int BW, bool NTL>
 __global__ __launch_bounds__(256 * BW) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 5 : 4))) void score_keys_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, KeysArgs a) {
+    const T *__restrict__ q, const T *__restrict__ k, KeysArgs a) {
     constexpr int EB = sizeof(T);
     constexpr int RB = D * EB;               // bytes per key row
     constexpr int LPR = RB >= 256 ? 16 : 8;  // lanes per row
@@ -127,18 +62,13 @@ __global__ __launch_bounds__(256 * BW) __attribute__((amdgpu_waves_per_eu(sizeof
     constexpr int U = 16 / P < NG ? 16 / P : NG;  // row groups per round (<= 16 loads per lane)
     static_assert(P >= 1 && NG % U == 0 && U % 4 == 0, "layout");
     __shared__ uint32_t red[4 * BW][G];
-    if (blockIdx.x < a.nwin) {
-        __shared__ SoftmaxPartials<D, 4 * BW> wp;
-        window_partials<T, D, G, 256 * BW>(q, k, v, a, blockIdx.x, wp);
-        return;
-    }
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // Workgroup (unit, BW blocks), units ordered (batch * Hkv + KV head, query group); 32-bit
     // math. Wavefronts 4b..4b+3 take block b of the workgroup.
     const uint32_t wpb = ((uint32_t)a.nblk + BW - 1) / BW;  // workgroups per unit
-    const uint32_t wg = blockIdx.x - a.nwin, ng = (uint32_t)a.groups;
+    const uint32_t wg = blockIdx.x, ng = (uint32_t)a.groups;
     const uint32_t uu32 = wg / wpb;
     const int bi = (int)(wg - uu32 * wpb) * BW + wave / 4;
     const uint32_t bk = uu32 / ng;
@@ -249,8 +179,7 @@ size_t stream_keys_bytes(const Plan &pl) {
     return (size_t)pl.units * (size_t)pl.rstride * pl.G * sizeof(uint32_t);
 }
 
-hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
-                             hipStream_t s) {
+hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s) {
     KeysArgs a;
     a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g; a.W = pl.W;
     a.groups = pl.groups; a.units = pl.units; a.rstride = pl.rstride; a.nblk = pl.nblk;
@@ -259,13 +188,10 @@ hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, const
     a.keys = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.keys_offset);
     a.bmax = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.bmax_offset);
     a.tmax = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.tmax_offset);
-    a.nwin = v ? (uint32_t)pl.units : 0u;
-    a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
-    a.wpart = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.wpart_offset);
-    dim3 grid((unsigned)(a.nwin + pl.units * ((pl.nblk + kKeysBW - 1) / kKeysBW))), block(256 * kKeysBW);
+    dim3 grid((unsigned)(pl.units * ((pl.nblk + kKeysBW - 1) / kKeysBW))), block(256 * kKeysBW);
 #define CA_LAUNCH_SK(T, D, G) \
     hipLaunchKernelGGL((score_keys_kernel<T, D, G, kKeysBW, kKeysNT>), grid, block, 0, s,       \
-                       static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), a)
+                       static_cast<const T *>(q), static_cast<const T *>(k), a)
 #define CA_LAUNCH_SK_G(T, D)                          \
     do {                                              \
         if (pl.G == 4) CA_LAUNCH_SK(T, D, 4);         \
