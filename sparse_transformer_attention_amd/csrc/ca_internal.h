@@ -34,14 +34,17 @@ struct Plan {
     int64_t lmax;         // candidate slots per query (wpu * topk)
     size_t lists_offset;  // byte offset of the lists in the workspace
     size_t ws_bytes;      // total workspace
-    // Decode path (score_keys, then finish reading the key buffer): key rows per unit, blocks
-    // of 256 rows per unit, and the offsets of the key buffer [units][G][rstride], the block
-    // maxima [units][nblk][G] and the tile maxima [units][G][rstride / tile_rows].
+    // Decode path (score_keys, then finish reading its tile summaries): rows per unit covered
+    // (rstride = 256 nblk), blocks of 256 rows per unit, rows per tile, and the offsets of the
+    // summaries [units][G][rstride / tile_rows] (best key u32; second key, offsets and the
+    // third key's upper half as one 8-byte word), the block maxima [units][nblk][G] and the
+    // finish kernel's scratch keys
+    // [nqv][rstride] (written only when a query's candidates exceed what LDS holds).
     bool stream;
     int64_t rstride;
     int nblk;
-    int tile_rows;  // rows per key tile (one best key per tile and query)
-    size_t keys_offset, bmax_offset, tmax_offset;
+    int tile_rows;
+    size_t best1_offset, rest_offset, bmax_offset, scratch_offset;
 };
 
 // Launchers (enqueue only; return the hipError_t of the last launch).
@@ -56,6 +59,6 @@ hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k
                                     const int32_t *idx, float *out, hipStream_t s);
 size_t topk_lds_bytes(const Plan &pl);
 hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s);
-size_t stream_keys_bytes(const Plan &pl);
+
 
 }  // namespace ca

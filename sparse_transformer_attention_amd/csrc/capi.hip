@@ -162,12 +162,13 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
             // Tiles of 4 rows-per-load: 16 rows with 16 lanes per row (rows of >= 256 bytes),
             // else 32.
             P.tile_rows = row_bytes >= 256 ? 16 : 32;
-            P.keys_offset = 0;
-            const size_t keys_bytes = (ca::stream_keys_bytes(P) + 255) & ~(size_t)255;
-            P.bmax_offset = P.keys_offset + keys_bytes;
-            const size_t bmax_bytes = ((size_t)P.units * P.nblk * P.G * sizeof(uint32_t) + 255) & ~(size_t)255;
-            P.tmax_offset = P.bmax_offset + bmax_bytes;
-            P.ws_bytes = P.tmax_offset + (size_t)P.units * P.G * (P.rstride / P.tile_rows) * sizeof(uint32_t);
+            auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+            const size_t ntiles = (size_t)P.units * P.G * (P.rstride / P.tile_rows);
+            P.best1_offset = 0;
+            P.rest_offset = P.best1_offset + up(ntiles * sizeof(uint32_t));
+            P.bmax_offset = P.rest_offset + up(ntiles * 2 * sizeof(uint32_t));
+            P.scratch_offset = P.bmax_offset + up((size_t)P.units * P.nblk * P.G * sizeof(uint32_t));
+            P.ws_bytes = P.scratch_offset + (size_t)P.nqv * (size_t)P.rstride * sizeof(uint32_t);
             return CA_OK;
         }
     }

@@ -7,9 +7,12 @@
 //   attend   (optional) the restricted softmax times V on that set, straight from LDS.
 // Plus the standalone attend kernel for caller-supplied sets (flash_attention_on_subset of the
 // section 5.2.2 sketch).
+#include <type_traits>
+
 #include "attend_core.h"
 #include "ca_internal.h"
 #include "device_utils.h"
+#include "score_core.h"
 #include "select_core.h"
 
 namespace ca {
@@ -21,12 +24,14 @@ struct FinishArgs {
     float scale_log2e;
     const uint32_t *cnt;    // [nqv][wpu] keys in each segment
     const uint64_t *lists;  // [nqv][wpu][topk] segments of candidate ranking keys
-    // Key-buffer path (score_keys): units of G query vectors, blocks and tiles of key rows.
+    // Tile-summary path (score_keys): units of G query vectors, blocks and tiles of key rows.
     int G, nblk, tile_shift;  // rows per tile: 1 << tile_shift
     int64_t groups, rstride;
-    const uint32_t *keys;   // [units][G][rstride]
-    const uint32_t *bmax;   // [units][nblk][G]
-    const uint32_t *tmax;   // [units][G][rstride / tile_rows]
+    uint32_t nvec;            // query vectors per KV head (g * nq)
+    const uint32_t *best1;    // [units][G][rstride / tile_rows]
+    const uint2 *rest;        // second key; offsets of the best two (bits 0-15), third key's upper half
+    const uint32_t *bmax;     // [units][nblk][G]
+    uint32_t *scratch;        // [nqv][rstride]
 };
 
 constexpr int kGather = 1024;  // candidates gathered into LDS for the one-wavefront select
@@ -206,40 +211,51 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
     select_exact<NT>(n, (int64_t)wpu * topk, key_at, kp, js, sel, gathered, sh);
 }
 
-// Candidates from the key buffer (score_keys): the query's bound is the lower edge of the radix
-// bin that holds the k'-th largest of its block (or tile) maxima (k' distinct candidates reach
-// it, so it is a lower bound of its k-th key); the keys of every tile whose best key reaches the
-// bound are gathered into LDS; then the exact top-kp. keys/tmax point at the query's rows, bm at
-// its first block maximum (stride G); the query's candidate rows are 1..rl. tiles is LDS for
-// kTileCap tile indices. The other wavefronts run overlap() while wavefront 0 takes the bound.
+// Candidates from the tile summaries of score_keys. The query's bound thr is the lower edge of
+// the radix bin that holds the k'-th largest of its block maxima (or of its tile maxima when
+// there are fewer than 2k' blocks): k' distinct rows reach it, so it is a lower bound of the
+// query's k-th key. Every key that reaches thr lies in a tile whose best key reaches it; such a
+// tile contributes its one or two best rows that reach thr, and, when its third key may reach
+// thr too, all its rows, scored again by rescore (the same bits as score_keys). The candidates go to gathered[] as ranking keys;
+// then the exact top-kp. best1/rest point at the query's tiles, bm at its first block
+// maximum (stride G); its candidate rows are 1..rl. tiles is LDS for kTileCap tile indices,
+// ovf for kOvfCap. When the candidates do not fit (ties at the bound), every passing tile is
+// scored into scratch (the query's rows) and selected from there. The other wavefronts run
+// overlap() while wavefront 0 takes the bound.
+//
+// rescore(ntl, tile_at, emit): scores every row of the tiles tile_at(0..ntl) (-1: none) for
+// this query, calling emit(key, row) for each of its candidate rows. All threads.
 constexpr int kTileCap = 1024;
+constexpr int kOvfCap = 64;
 constexpr int kRankSelectMax = 256;  // candidates selected by rank counting (else radix select)
 
-template <int NT, typename Overlap>
-__device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ keys,
-                                             const uint32_t *__restrict__ tmax,
+template <int NT, typename Overlap, typename Rescore>
+__device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
+                                             const uint2 *__restrict__ rest,
                                              const uint32_t *__restrict__ bm, int G, int nblk,
                                              int tile_shift, int rl, int kp, int32_t *js,
                                              uint64_t *sel, uint64_t *gathered, int32_t *tiles,
-                                             SelectShared<NT> &sh, Overlap overlap) {
+                                             int32_t *ovf, uint32_t *scratch,
+                                             SelectShared<NT> &sh, Overlap overlap,
+                                             Rescore rescore) {
     constexpr int E = 8;   // block maxima per lane: at most 512 (merged in groups beyond)
     constexpr int TU = 8;  // tile maxima in flight per thread
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // 32-bit indices: a query's key rows are fewer than 2^31.
-    const int tile_rows = 1 << tile_shift, rpg = tile_rows >> 2;
+    const int tile_rows = 1 << tile_shift;
     const int ntiles = (rl + tile_rows) >> tile_shift;  // tiles covering rows 0..rl
     // First tile maxima requested before the bound is known.
     uint32_t tm[TU];
 #pragma unroll
     for (int e = 0; e < TU; ++e) {
         const int j = tid + NT * e;
-        tm[e] = tmax[j < ntiles ? j : 0];
+        tm[e] = best1[j < ntiles ? j : 0];
     }
     if (wave == 0) {
         // Maxima of disjoint groups of rows: the blocks (256 rows), or the tiles when there are
         // fewer than 2k' blocks; merged into at most 64*E groups of consecutive ones.
         const bool by_tile = nblk < 2 * kp;
-        const uint32_t *src = by_tile ? tmax : bm;
+        const uint32_t *src = by_tile ? best1 : bm;
         const int stride = by_tile ? 1 : G;
         const int count = by_tile ? ntiles : nblk;
         const int per = (count + 64 * E - 1) / (64 * E);
@@ -261,7 +277,7 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ keys,
             }
         }
         const uint32_t thr = wave_bound_u32(m, kp, &sh.hist[0][0]);
-        if (lane == 0) { sh.pick[0] = thr > 1u ? thr : 1u; sh.pick[1] = 0u; sh.sel_count = 0; }
+        if (lane == 0) { sh.pick[0] = thr > 1u ? thr : 1u; sh.pick[1] = 0u; sh.pick[2] = 0u; sh.sel_count = 0; }
     } else {
         overlap();
     }
@@ -282,34 +298,60 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ keys,
 #pragma unroll
         for (int e = 0; e < TU; ++e) {
             const int j = j0 + NT * (TU + e);
-            tm[e] = tmax[j < ntiles ? j : 0];
+            tm[e] = best1[j < ntiles ? j : 0];
         }
     }
     __syncthreads();
     const int nt = (int)sh.pick[1];
-    if (nt <= kTileCap) {
-        // Their keys, one 16-byte word per thread (position p of a tile holds row
-        // rpg*(p%4) + p/4 of the tile), the ones that reach the bound gathered.
-        const int wshift = tile_shift - 2;  // words per tile: tile_rows / 4
-        for (int x = tid; x < (nt << wshift); x += NT) {
-            const int tile0 = tiles[x >> wshift] << tile_shift;
-            const int w4 = x & (rpg - 1);
-            const uint4 v = *reinterpret_cast<const uint4 *>(keys + tile0 + 4 * w4);
-            const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int row = tile0 + rpg * c + w4;
-                if (kv[c] >= thr && row >= 1 && row <= rl) {
-                    const int pos = atomicAdd(&sh.sel_count, 1);
-                    if (pos < kGather) gathered[pos] = make_rank_key(kv[c], (uint32_t)row);
+    bool fallback = nt > kTileCap;
+    if (!fallback) {
+        // Each passing tile gives its best rows that reach the bound, or, when its third key may
+        // reach it as well (its upper half is kept: compared as the largest key with that
+        // half), goes to the list of tiles scored again.
+        for (int x = tid; x < nt; x += NT) {
+            const int tile = tiles[x];
+            const uint32_t k1 = best1[tile];
+            const uint2 rs = rest[tile];
+            // Both loads complete here (kept from being moved into the branches one by one).
+            asm volatile("" ::"v"(k1), "v"(rs.x), "v"(rs.y));
+            const uint32_t k2 = rs.x, o = rs.y, k3max = (rs.y & 0xFFFF0000u) | 0xFFFFu;
+            if ((rs.y & 0xFFFF0000u) != 0u && k3max >= thr) {
+                const uint32_t at = atomicAdd(&sh.pick[2], 1u);
+                if (at < (uint32_t)kOvfCap) ovf[at] = tile;
+            } else {
+                // (Increments of 1 only: the compiler turns those into one atomic per wavefront.)
+                const uint32_t row0 = (uint32_t)(tile << tile_shift);
+                const int p1 = atomicAdd(&sh.sel_count, 1);
+                if (p1 < kGather) gathered[p1] = make_rank_key(k1, row0 + (o & 0xFFu));
+                if (k2 >= thr) {
+                    const int p2 = atomicAdd(&sh.sel_count, 1);
+                    if (p2 < kGather) gathered[p2] = make_rank_key(k2, row0 + ((o >> 8) & 0xFFu));
                 }
             }
         }
-    } else if (tid == 0) {
-        sh.sel_count = kGather + 1;  // too many tiles: select over the whole key buffer
+        __syncthreads();
+        const int no = (int)sh.pick[2];
+        if (no > kOvfCap) {
+            fallback = true;
+        } else if (no > 0) {
+            rescore(no, [&](int i) { return ovf[i]; }, [&](uint32_t key, int row) {
+                if (key >= thr) {
+                    const int pos = atomicAdd(&sh.sel_count, 1);
+                    if (pos < kGather) gathered[pos] = make_rank_key(key, (uint32_t)row);
+                }
+            });
+            __syncthreads();
+        }
     }
-    __syncthreads();
-    const int n = sh.sel_count;
+    int n = fallback ? kGather + 1 : sh.sel_count;
+    if (n > kGather) {
+        // Too many candidates for LDS (exact ties at the bound): the keys of every passing tile
+        // into scratch, then the selection over them.
+        rescore(ntiles, [&](int i) { return best1[i] >= thr ? i : -1; },
+                [&](uint32_t key, int row) { scratch[row] = key; });
+        __threadfence_block();
+        n = kGather + 1;
+    }
     __syncthreads();
     if (n <= kRankSelectMax && n >= kp) {
         // Few candidates: a key is selected when fewer than kp keys beat it; the selected
@@ -345,18 +387,66 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ keys,
         __syncthreads();
         return;
     }
-    // More than kGather candidates (ties at the bound): every key of rows 1..rl that reaches it.
+    // Keys from scratch for rows of passing tiles (others hold none that reach the bound).
     auto key_at = [&](int64_t f64) -> uint64_t {
         const int f = (int)f64;
-        const int tile0 = f & ~(tile_rows - 1);
-        const int p = f - tile0;
-        const int row = tile0 + rpg * (p & 3) + (p >> 2);
-        const uint32_t kv = keys[f];
-        return (row >= 1 && row <= rl && kv >= thr) ? make_rank_key(kv, (uint32_t)row) : 0ull;
+        if (f < 1 || f > rl || best1[f >> tile_shift] < thr) return 0ull;
+        const uint32_t kv = scratch[f];
+        return kv >= thr ? make_rank_key(kv, (uint32_t)f) : 0ull;
     };
     select_exact<NT>(n, (int64_t)ntiles << tile_shift, key_at, kp, js, sel, gathered, sh);
 }
 
+// Scores every row of the tiles tile_at(0..ntl) (-1: none) for the query vector in slot t of
+// unit (b, kvh, group gq) with row_key over the unit's G query vectors, as score_keys does (the
+// same bits), and calls emit(key, row) for each row in [1, rl] (key 0 never reaches a bound). RPG
+// rows per wavefront load, LPR lanes per row; one pass per NW*RPG rows. All threads.
+template <typename T, int D, int NT, typename TileAt, typename Emit>
+__device__ __forceinline__ void rescore_tiles(const T *__restrict__ q, const T *__restrict__ kb,
+                                              const FinishArgs &a, uint32_t b, uint32_t kvh, uint32_t gq,
+                                              int t, int rl, int ntl, TileAt tile_at, Emit emit) {
+    constexpr int RB = D * (int)sizeof(T);
+    constexpr int LPR = RB >= 256 ? 16 : 8, RPG = 64 / LPR, P = RB / (16 * LPR);
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sl = lane % LPR;
+    const uint32_t g = (uint32_t)a.g, bk = b * (uint32_t)a.Hkv + kvh;
+    const int G = a.G;
+    auto body = [&](auto gc) {
+        constexpr int GC = decltype(gc)::value;
+        uint4 qr[GC][P];
+#pragma unroll
+        for (int tt = 0; tt < GC; ++tt) {
+            const uint32_t idx = gq * GC + tt;
+            if (idx < a.nvec) {
+                const uint32_t qh = idx / g, hh = idx - qh * g;
+                const uint4 *src = reinterpret_cast<const uint4 *>(q + (((size_t)bk * g + hh) * a.nq + qh) * D);
+#pragma unroll
+                for (int p = 0; p < P; ++p) qr[tt][p] = src[p * LPR + sl];
+            } else {
+#pragma unroll
+                for (int p = 0; p < P; ++p) qr[tt][p] = make_uint4(0, 0, 0, 0);
+            }
+        }
+        const bool mine = sl / (LPR / GC) == t && sl % (LPR / GC) == 0;
+        const int total = ntl << a.tile_shift;
+        for (int r0 = wave * RPG; r0 < total; r0 += NW * RPG) {
+            const int rr = r0 + lane / LPR;
+            const int tile = rr < total ? tile_at(rr >> a.tile_shift) : -1;
+            const int row = tile >= 0 ? (tile << a.tile_shift) + (rr & ((1 << a.tile_shift) - 1)) : 0;
+            const int lrow = row < a.n ? row : (int)a.n - 1;
+            const uint4 *src = reinterpret_cast<const uint4 *>(kb + (size_t)lrow * D);
+            uint4 kr[P];
+#pragma unroll
+            for (int p = 0; p < P; ++p) kr[p] = src[p * LPR + sl];
+            const uint32_t key = row_key<T, LPR, P, GC>(kr, qr, lane);
+            if (mine && tile >= 0 && row >= 1 && row <= rl) emit(key, row);
+        }
+    };
+    if (G == 4) body(std::integral_constant<int, 4>());
+    else if (G == 2) body(std::integral_constant<int, 2>());
+    else body(std::integral_constant<int, 1>());
+}
 
 // Rows per lane in flight in the attend phase (rows past the set's end are loaded as clamped
 // duplicates, so these match the common sizes: 15 wavefronts x 4 rows x 5 cover the anchor and
@@ -374,6 +464,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     __shared__ SelectShared<NT> ssh;
     __shared__ uint64_t gathered[kGather];
     __shared__ int32_t tile_idx[TILES ? kTileCap : 1];
+    __shared__ int32_t ovf_idx[TILES ? kOvfCap : 1];
     // Softmax partials: [0, NW) the anchor and window rows (wavefronts 1..NW-1 when wavefront 0
     // takes the bound), [NW, 2NW) the top-k rows.
     __shared__ SoftmaxPartials<D, ATTEND ? 2 * NW : 1> part;
@@ -420,11 +511,14 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
             const uint32_t gq = idx / (uint32_t)a.G;
             const int64_t u = ((int64_t)b * a.Hkv + kvh) * a.groups + gq;
             const int t = (int)(idx - gq * (uint32_t)a.G);
-            const int64_t ntq = a.rstride >> a.tile_shift;
-            select_tiles<NT>(a.keys + ((size_t)u * a.G + t) * a.rstride,
-                             a.tmax + ((size_t)u * a.G + t) * ntq,
+            const size_t qt = ((size_t)u * a.G + t) * (size_t)(a.rstride >> a.tile_shift);
+            select_tiles<NT>(a.best1 + qt, a.rest + qt,
                              a.bmax + (size_t)u * a.nblk * a.G + t, a.G, a.nblk, a.tile_shift,
-                             (int)rl, kp, js + base, sel, gathered, tile_idx, ssh, overlap);
+                             (int)rl, kp, js + base, sel, gathered, tile_idx, ovf_idx,
+                             a.scratch + qv * a.rstride, ssh, overlap,
+                             [&](int ntl, auto tile_at, auto emit) {
+                                 rescore_tiles<T, D, NT>(q, kb, a, b, kvh, gq, t, (int)rl, ntl, tile_at, emit);
+                             });
         } else {
             select_segments<NT>(a.cnt + qv * a.wpu, a.lists + qv * a.wpu * a.topk, a.wpu, a.topk,
                                 kp, js + base, sel, gathered, ssh, overlap);
@@ -512,9 +606,12 @@ FinishArgs finish_args(const Plan &pl, const void *ws) {
     a.lists = ws ? reinterpret_cast<const uint64_t *>(static_cast<const char *>(ws) + pl.lists_offset) : nullptr;
     a.G = pl.G; a.nblk = pl.nblk; a.tile_shift = pl.tile_rows == 32 ? 5 : 4; a.groups = pl.groups; a.rstride = pl.rstride;
     const char *wb = static_cast<const char *>(ws);
-    a.keys = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.keys_offset) : nullptr;
-    a.bmax = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.bmax_offset) : nullptr;
-    a.tmax = (ws && pl.stream) ? reinterpret_cast<const uint32_t *>(wb + pl.tmax_offset) : nullptr;
+    const bool sm = ws && pl.stream;
+    a.best1 = sm ? reinterpret_cast<const uint32_t *>(wb + pl.best1_offset) : nullptr;
+    a.rest = sm ? reinterpret_cast<const uint2 *>(wb + pl.rest_offset) : nullptr;
+    a.bmax = sm ? reinterpret_cast<const uint32_t *>(wb + pl.bmax_offset) : nullptr;
+    a.scratch = sm ? reinterpret_cast<uint32_t *>(const_cast<char *>(wb) + pl.scratch_offset) : nullptr;
+    a.nvec = (uint32_t)(pl.g * pl.nq);
     return a;
 }
 
@@ -530,7 +627,7 @@ hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const 
     const dim3 grid((unsigned)pl.nqv);
     const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v);
     const size_t fixed1024 = kGather * sizeof(uint64_t) + sizeof(SelectShared<1024>) +
-                             kTileCap * sizeof(int32_t) + sizeof(SoftmaxPartials<D, 32>);
+                             (kTileCap + kOvfCap) * sizeof(int32_t) + sizeof(SoftmaxPartials<D, 32>);
     const bool wide = pl.nqv < kWideBelow && shmem + fixed1024 <= 64 * 1024;
 #define CA_LAUNCH_FIN(NT, TILES)                                                                  \
     hipLaunchKernelGGL((finish_kernel<T, D, NT, ATTEND, TILES>), grid, dim3(NT), shmem, s, qt, kt, vt, \

@@ -86,6 +86,23 @@ __device__ __forceinline__ float reduce_row(const float (&acc)[G], int lane) {
     }
 }
 
+// Order-preserving key of one K row for the G queries of a unit: the lane's P slices of the row
+// dotted with the same slices of each query (fp32), summed over the row's LPR lanes, mapped by
+// score_key. The lanes of query (lane % LPR) / (LPR / G) hold its key. Every kernel that scores
+// rows uses this function, so a row's key has the same bits wherever it is computed.
+template <typename T, int LPR, int P, int G>
+__device__ __forceinline__ uint32_t row_key(const uint4 (&kr)[P], const uint4 (&qr)[G][P], int lane) {
+    float acc[G];
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+        float x = 0.f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) x = dot16(kr[p], qr[t][p], x, T());
+        acc[t] = x;
+    }
+    return score_key(reduce_row<LPR, G>(acc, lane));
+}
+
 // Adds the NS (key, row) results a lane holds to its query's running list. First chunk of a
 // unit (direct): the lists are empty and there is no threshold yet, so the key of row r goes to
 // position r - row0 (0 when r is no candidate of the query). Otherwise the keys that reach the

@@ -3,21 +3,21 @@
 // C_i = {0} u {i-W+1..i} u Top-k_i; section 2.2.3, the top-k part ranks the positions
 // R_i = {1..i-W} outside the anchor and the window).
 //
-// score_keys: one workgroup per (unit, block of 256 key rows), where a unit is (batch, KV head,
-// query group) with up to G query vectors reading the same KV head. Each wavefront requests its
-// 64 rows at once, then computes the fp32 scores of the G queries; the block's K rows are read
-// once (the only large HBM traffic of the path). It writes one order-preserving 32-bit key per
-// (row, query), the best key of every tile of rows, and the block's best key per query. Small workgroups in a one-shot grid let the
-// hardware dispatcher balance the stream across the CUs; no LDS lists, no atomics.
+// score_keys: one workgroup per (unit, BW blocks of 256 key rows), where a unit is (batch, KV
+// head, query group) with up to G query vectors reading the same KV head. Each wavefront
+// requests its 64 rows at once, then computes the fp32 scores of the G queries (row_key); the
+// K rows are read once (the only large HBM traffic of the path). The order-preserving 32-bit
+// keys (0 for rows that are no candidate of the query: the anchor, the window, past the query)
+// are staged in LDS; the workgroup's epilogue then writes, per tile of TR = 4*RPG rows (RPG =
+// rows one wavefront load covers) and query, only a summary: the two best keys with their row
+// offsets in the tile (ties: the smaller offset first) and the upper half of the third best key;
+// and per block and query the block's best key. Writing every key (16 MiB at 131K) cost the
+// stream more than its share of bandwidth; the summaries are ~1/5 of that. Small workgroups in a one-shot grid let the
+// hardware dispatcher balance the stream across the CUs.
 //
-// Key buffer: [units][G][rstride] words, query-major. Rows are grouped in tiles of 4*RPG rows
-// (RPG = rows one wavefront load covers); after 4 loads a lane holds its query's keys of rows
-// r, r+RPG, r+2RPG, r+3RPG and stores them as one 16-byte word, so position p of a tile holds
-// row RPG*(p%4) + p/4 of the tile. Block b covers rows [256b, 256b+256); row 0 (the anchor) and
-// rows that are no candidate of the query hold key 0.
-//
-// The finish kernel then takes, per query, the bound from the block maxima and reads only the
-// tiles whose best key reaches it.
+// The finish kernel takes, per query, a bound from the block maxima; a tile gives each of its two
+// best rows whose key reaches it as candidates, and a tile whose third key may reach it as well
+// is scored again there (row_key, the same bits).
 #include "ca_internal.h"
 #include "score_core.h"
 
@@ -32,17 +32,17 @@ struct KeysArgs {
     int64_t n, nq;
     int Hq, Hkv, g, W;
     int64_t groups, units;
-    int64_t rstride;  // key rows per unit in the key buffer
+    int64_t rstride;  // rows per unit covered by the summaries (nblk * 256)
     int nblk;         // blocks per unit
     uint32_t nvec;    // query vectors per KV head (g * nq)
     int row_base;     // n - nq - W: the last candidate row of query vector idx is row_base + idx / g
-    uint32_t *keys;   // [units][G][rstride], tiles as described above
+    uint32_t *best1;  // [units][G][rstride / TR]: best key of each tile
+    uint2 *rest;      // [units][G][rstride / TR]: second key; offsets of the best (bits 0-7) and
+                      // the second (bits 8-15), upper 16 bits of the third key (bits 16-31)
     uint32_t *bmax;   // [units][nblk][G]
-    uint32_t *tmax;   // [units][G][rstride / (4*RPG)]: best key of each tile
 };
 
-// 16-byte load of a key-row slice; NTL: non-temporal (streamed once, kept out of the caches so
-// that the key buffer written meanwhile stays there).
+// 16-byte load of a key-row slice; NTL: non-temporal (streamed once, kept out of the caches).
 template <bool NTL>
 __device__ __forceinline__ uint4 load_row16(const uint4 *p) {
     if constexpr (NTL) return load_row16_nt(p);
@@ -61,7 +61,10 @@ __global__ __launch_bounds__(256 * BW) __attribute__((amdgpu_waves_per_eu(sizeof
     constexpr int NG = 64 / RPG;             // row groups of a wavefront's 64 rows
     constexpr int U = 16 / P < NG ? 16 / P : NG;  // row groups per round (<= 16 loads per lane)
     static_assert(P >= 1 && NG % U == 0 && U % 4 == 0, "layout");
+    constexpr int TR = 4 * RPG;               // rows per tile
+    constexpr int WROWS = BW * kBlockRows;    // rows per workgroup
     __shared__ uint32_t red[4 * BW][G];
+    __shared__ uint32_t kst[G][WROWS];        // keys of the workgroup's rows, per query
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -70,7 +73,8 @@ __global__ __launch_bounds__(256 * BW) __attribute__((amdgpu_waves_per_eu(sizeof
     const uint32_t wpb = ((uint32_t)a.nblk + BW - 1) / BW;  // workgroups per unit
     const uint32_t wg = blockIdx.x, ng = (uint32_t)a.groups;
     const uint32_t uu32 = wg / wpb;
-    const int bi = (int)(wg - uu32 * wpb) * BW + wave / 4;
+    const int wg_row0 = (int)(wg - uu32 * wpb) * WROWS;
+    const int bi = wg_row0 / kBlockRows + wave / 4;
     const uint32_t bk = uu32 / ng;
     const uint32_t grp = uu32 - bk * ng;
     const int64_t u = (int64_t)bk * a.groups + grp;
@@ -88,8 +92,6 @@ __global__ __launch_bounds__(256 * BW) __attribute__((amdgpu_waves_per_eu(sizeof
     const int rlo = row0 > 1 ? row0 : 1;  // row 0 (the anchor) is no candidate
 
     const uint4 *kbase = reinterpret_cast<const uint4 *>(k + (int64_t)bk * a.n * D);
-    uint32_t *kout = a.keys + ((size_t)u * G + my_t) * a.rstride;
-    uint32_t *tout = a.tmax + ((size_t)u * G + my_t) * (a.rstride / (4 * RPG));
     const int wrow0 = row0 + (wave % 4) * 64;  // this wavefront's 64 rows
     uint32_t best = 0u;
     if (live && wrow0 < rows_end) {
@@ -129,55 +131,68 @@ __global__ __launch_bounds__(256 * BW) __attribute__((amdgpu_waves_per_eu(sizeof
 #pragma unroll
                 for (int gg = 0; gg < 4; ++gg) {
                     const int uu = u4 + gg;
-                    float acc[G];
-#pragma unroll
-                    for (int t = 0; t < G; ++t) {
-                        float x = 0.f;
-#pragma unroll
-                        for (int p = 0; p < P; ++p) x = dot16(kr[uu][p], qr[t][p], x, T());
-                        acc[t] = x;
-                    }
-                    const uint32_t key = score_key(reduce_row<LPR, G>(acc, lane));
+                    const uint32_t key = row_key<T, LPR, P, G>(kr[uu], qr, lane);
                     const int row = wrow0 + (r * U + uu) * RPG + lane / LPR;
                     kv4[gg] = (row >= rlo && row < rows_end && row <= my_rlast) ? key : 0u;
                     best = kv4[gg] > best ? kv4[gg] : best;
                 }
-                // Tile of 4*RPG rows starting at the first of these row groups, and its best key
-                // (over the lanes of the query's rows: LPR apart).
+                // Keys of rows tile0 + RPG*gg + lane/LPR, staged as one 16-byte word: position p
+                // of a staged tile holds row RPG*(p%4) + p/4 of the tile.
                 const int tile0 = wrow0 + (r * U + u4) * RPG;
                 if (writer)
-                    *reinterpret_cast<uint4 *>(kout + tile0 + 4 * (lane / LPR)) =
+                    *reinterpret_cast<uint4 *>(&kst[my_t][tile0 - wg_row0 + 4 * (lane / LPR)]) =
                         make_uint4(kv4[0], kv4[1], kv4[2], kv4[3]);
-                uint32_t tm = kv4[0] > kv4[1] ? kv4[0] : kv4[1];
-                tm = kv4[2] > tm ? kv4[2] : tm;
-                tm = kv4[3] > tm ? kv4[3] : tm;
-                tm = lane_max_stride<LPR>(tm);
-                if (writer && lane < LPR) tout[tile0 / (4 * RPG)] = tm;
             }
         }
+    } else {
+        // Rows without candidates: key 0.
+        for (int i = lane; i < G * 16; i += 64)
+            *reinterpret_cast<uint4 *>(&kst[i / 16][wrow0 - wg_row0 + 4 * (i % 16)]) = make_uint4(0, 0, 0, 0);
     }
     // Best key per query over each block: lanes of the same query are LPR apart, then the
     // block's 4 wavefronts (0 for a block without candidate rows).
     best = lane_max_stride<LPR>(best);
     if (lane < LPR && writer) red[wave][my_t] = best;
     __syncthreads();
+    const int nbw = (int)(a.nblk - wg_row0 / kBlockRows) < BW ? a.nblk - wg_row0 / kBlockRows : BW;
     if (tid < BW * G) {
         const int b2 = tid / G, t = tid % G;
-        const int bi2 = (int)(wg - uu32 * wpb) * BW + b2;
-        if (bi2 < a.nblk) {
+        if (b2 < nbw) {
             uint32_t m = 0u;
 #pragma unroll
             for (int w = 0; w < 4; ++w) m = red[4 * b2 + w][t] > m ? red[4 * b2 + w][t] : m;
-            a.bmax[((size_t)u * a.nblk + bi2) * G + t] = m;
+            a.bmax[((size_t)u * a.nblk + wg_row0 / kBlockRows + b2) * G + t] = m;
         }
+    }
+    // Tile summaries, one thread per (query, tile) of the workgroup's blocks: the two best
+    // (key, offset) in the ranking order (larger key, then smaller offset) and the third key.
+    const int nt = nbw * kBlockRows / TR;
+    for (int x = tid; x < G * nt; x += 256 * BW) {
+        const int t = x / nt, j = x - t * nt;
+        uint32_t k1 = 0u, o1 = 0u, k2 = 0u, o2 = 0u, k3 = 0u;
+#pragma unroll
+        for (int w4 = 0; w4 < TR / 4; ++w4) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(&kst[t][j * TR + 4 * w4]);
+            const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {  // staged position 4*w4 + c holds row offset RPG*c + w4
+                const uint32_t key = kv[c], off = (uint32_t)(RPG * c + w4);
+                const bool b1 = key > k1 || (key == k1 && off < o1);
+                const bool b2 = key > k2 || (key == k2 && off < o2);
+                k3 = b2 ? k2 : (key > k3 ? key : k3);
+                k2 = b1 ? k1 : (b2 ? key : k2);
+                o2 = b1 ? o1 : (b2 ? off : o2);
+                k1 = b1 ? key : k1;
+                o1 = b1 ? off : o1;
+            }
+        }
+        const size_t o = ((size_t)u * G + t) * (size_t)(a.rstride / TR) + wg_row0 / TR + j;
+        a.best1[o] = k1;
+        a.rest[o] = make_uint2(k2, o1 | (o2 << 8) | (k3 & 0xFFFF0000u));
     }
 }
 
 }  // namespace
-
-size_t stream_keys_bytes(const Plan &pl) {
-    return (size_t)pl.units * (size_t)pl.rstride * pl.G * sizeof(uint32_t);
-}
 
 hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s) {
     KeysArgs a;
@@ -185,9 +200,10 @@ hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void 
     a.groups = pl.groups; a.units = pl.units; a.rstride = pl.rstride; a.nblk = pl.nblk;
     a.nvec = (uint32_t)(pl.g * pl.nq);
     a.row_base = (int)(pl.n - pl.nq - pl.W);
-    a.keys = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.keys_offset);
-    a.bmax = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.bmax_offset);
-    a.tmax = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.tmax_offset);
+    char *w = static_cast<char *>(ws);
+    a.best1 = reinterpret_cast<uint32_t *>(w + pl.best1_offset);
+    a.rest = reinterpret_cast<uint2 *>(w + pl.rest_offset);
+    a.bmax = reinterpret_cast<uint32_t *>(w + pl.bmax_offset);
     dim3 grid((unsigned)(pl.units * ((pl.nblk + kKeysBW - 1) / kKeysBW))), block(256 * kKeysBW);
 #define CA_LAUNCH_SK(T, D, G) \
     hipLaunchKernelGGL((score_keys_kernel<T, D, G, kKeysBW, kKeysNT>), grid, block, 0, s,       \

@@ -153,6 +153,41 @@ def test_deterministic():
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
 
 
+def clustered_inputs(w, seed, start, length):
+    """Random q/k/v, then K rows [start, start+length) aligned with the sum of each KV head's
+    query rows, with distinct gains: the best scores of every query sit in that run, many per
+    tile of rows."""
+    x = synth.make_inputs(w, seed=seed)
+    q = x["q"].float()
+    k = x["k"].float().clone()
+    g = w.heads // w.kv_heads
+    j = torch.arange(length, dtype=torch.float32)
+    # Distinct gains; for long runs permuted, so that the best rows spread over many tiles.
+    gains = 1.0 + 0.5 * ((j * 7919.0) % length if length > 256 else j) / length
+    for kvh in range(w.kv_heads):
+        d = q[:, kvh * g:(kvh + 1) * g].sum(dim=(1, 2))  # [B][d]
+        d = d / d.norm(dim=-1, keepdim=True) * 24.0
+        k[:, kvh, start:start + length] = d[:, None, :] * gains[None, :, None]
+    x["k"] = k.to(w.torch_dtype)
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("length,topk", [(60, 48), (1500, 300)])
+def test_clustered_best_rows(dtype, length, topk):
+    """Best rows packed into consecutive tiles: with a few such tiles the decode path scores
+    them again (more than two keys of a tile reach the bound); with many (here > 64 tiles) it
+    scores every passing tile into its scratch keys and selects from there. Either way the
+    sets must match the oracle's."""
+    w = W_(dtype=dtype, heads=4, kv_heads=1, n=8000, nq=2, W=64, topk=topk)
+    x = clustered_inputs(w, seed=13, start=3001, length=length)
+    announce(f"clustered {dtype} {length} {topk}")
+    out, idx = run_gpu(w, x)
+    ref_idx, _, ref_diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    compare_sets(idx, ref_idx, ref_diag, x["q"], x["k"], w.W, w.topk)
+    assert_outputs(out, oracle.restricted(x["q"], x["k"], x["v"], idx), w.torch_dtype)
+
+
 def test_select_stage_alone_matches_full_call():
     w = SMALL["prefill_bf16_ragged"]
     x = synth.make_inputs(w, seed=4)
