@@ -212,7 +212,7 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
 }
 
 // Candidates from the tile summaries of score_keys. The query's bound thr is the lower edge of
-// the radix bin that holds the k'-th largest of its block maxima (or of its tile maxima when
+// the 10-bit radix bin that holds the k'-th largest of its block maxima (or of its tile maxima when
 // there are fewer than 2k' blocks): k' distinct rows reach it, so it is a lower bound of the
 // query's k-th key. Every key that reaches thr lies in a tile whose best key reaches it; such a
 // tile contributes its one or two best rows that reach thr, and, when its third key may reach
@@ -276,7 +276,7 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
                 if (gi < ngr && grp < count) m[e] = x[e] > m[e] ? x[e] : m[e];
             }
         }
-        const uint32_t thr = wave_bound_u32(m, kp, &sh.hist[0][0]);
+        const uint32_t thr = wave_bound_u32(m, kp);
         if (lane == 0) { sh.pick[0] = thr > 1u ? thr : 1u; sh.pick[1] = 0u; sh.pick[2] = 0u; sh.sel_count = 0; }
     } else {
         overlap();

@@ -131,13 +131,14 @@ __device__ __forceinline__ uint32_t wave_keep_top_u64(const uint64_t (&kr)[E], i
     return wave_min_u32_dpp(tmin);
 }
 
-// A high word that at least `keep` of the wavefront's non-zero values v[0..E) reach, close to
-// their keep-th largest: the lower edge of the 8-bit radix bin, over the highest bits where
-// the values differ, that holds the keep-th largest value (one histogram pass). 0 when there
-// are fewer than `keep` values.
+// A value that at least `keep` of the wavefront's non-zero values v[0..E) reach, close to their
+// keep-th largest: the largest P whose bits above the highest bit hb where the values differ are
+// theirs, whose bits below lb = hb - 9 are 0, and which `keep` values reach (the lower edge of the
+// 10-bit radix bin that holds the keep-th largest value). Found bit by bit from hb down, each
+// step a count of the values that reach the candidate (compares and one DPP sum: no LDS, no
+// atomics). 0 when there are fewer than `keep` values.
 template <int E>
-__device__ __forceinline__ uint32_t wave_bound_u32(const uint32_t (&v)[E], int keep, uint32_t *hist) {
-    const int lane = threadIdx.x & 63;
+__device__ __forceinline__ uint32_t wave_bound_u32(const uint32_t (&v)[E], int keep) {
     int nz = 0;
     uint32_t hmax = 0u, hmin = 0xFFFFFFFFu;
 #pragma unroll
@@ -151,29 +152,17 @@ __device__ __forceinline__ uint32_t wave_bound_u32(const uint32_t (&v)[E], int k
     hmin = wave_min_u32_dpp(hmin);
     if (hmax == hmin) return hmax;
     const int hb = 31 - __builtin_clz(hmax ^ hmin);
-    const int lb = hb >= 7 ? hb - 7 : 0;
-    const uint32_t dmask = (2u << (hb - lb)) - 1u;
-    reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0, 0, 0, 0);
-    wave_sync();
+    const int lb = hb >= 9 ? hb - 9 : 0;
+    uint32_t p = hb >= 31 ? 0u : (hmax >> (hb + 1)) << (hb + 1);
+    for (int bit = hb; bit >= lb; --bit) {
+        const uint32_t cand = p | (1u << bit);
+        uint32_t c = 0u;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-        if (v[e]) atomicAdd(&hist[(v[e] >> lb) & dmask], 1u);
-    wave_sync();
-    const uint4 h = reinterpret_cast<const uint4 *>(hist)[lane];  // bins 4l..4l+3
-    const uint32_t own = h.x + h.y + h.z + h.w;
-    const uint32_t pre = wave_incl_scan_u32(own);
-    const uint32_t all = __builtin_amdgcn_readlane(pre, 63);
-    const uint32_t excl = all - pre;  // values in bins >= 4l+4
-    const uint32_t c3 = excl + h.w, c2 = c3 + h.z, c1 = c2 + h.y, c0 = c1 + h.x;
-    const uint32_t r = (uint32_t)keep;
-    const bool mine = (c0 >= r) && (excl < r);
-    const int u = (c3 >= r) ? 3 : (c2 >= r) ? 2 : (c1 >= r) ? 1 : 0;
-    int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
-    src = src < 0 ? 0 : src;
-    const uint32_t digit = __builtin_amdgcn_readlane((uint32_t)(4 * lane + u), src);
-    wave_sync();
-    const uint32_t pfx = hb >= 31 ? 0u : (hmax >> (hb + 1)) << (hb + 1);
-    return pfx | (digit << lb);
+        for (int e = 0; e < E; ++e) c += v[e] >= cand ? 1u : 0u;
+        c = __builtin_amdgcn_readlane(wave_incl_scan_u32(c), 63);
+        if (c >= (uint32_t)keep) p = cand;
+    }
+    return p;
 }
 
 // One wavefront thins its distinct non-zero keys kr[0..E) (0 = empty) to those whose high word
