@@ -41,6 +41,10 @@ struct Plan {
     // finish kernel's scratch keys
     // [nqv][rstride] (written only when a query's candidates exceed what LDS holds).
     bool stream;
+    // Prefill path with bf16 inputs (mfma_select bound + cand, then finish over the segments):
+    // taus [nqv] in the first words of the workspace, the lengths and lists as above with
+    // wpu * topk >= 256 keys per query.
+    bool mfma;
     int64_t rstride;
     int nblk;
     int tile_rows;
@@ -59,6 +63,12 @@ hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k
                                     const int32_t *idx, float *out, hipStream_t s);
 size_t topk_lds_bytes(const Plan &pl);
 hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s);
+// Query blocks of 16 per wavefront of the two MFMA passes (64 * QB query vectors per workgroup).
+constexpr int kMfmaQBBound = 4;
+constexpr int kMfmaQBCand = 4;
+// pass 0: the bound of every query; pass 1: its candidate list.
+hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
+                              int pass);
 
 
 }  // namespace ca

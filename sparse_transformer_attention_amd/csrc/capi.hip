@@ -13,8 +13,8 @@
 namespace {
 
 // ---- measurement hooks: HIP events around each launch while profiling is on ----------------
-enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_COUNT = 3 };
-const char *const kKernelNames[K_COUNT] = {"score_select", "finish", "attend"};
+enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_BOUND = 3, K_CAND = 4, K_COUNT = 5 };
+const char *const kKernelNames[K_COUNT] = {"score_select", "finish", "attend", "mfma_bound", "mfma_cand"};
 
 struct Profiler {
     std::mutex mu;
@@ -83,6 +83,9 @@ constexpr int kMaxTopk = 512;            // running lists hold topk + chunk <= 1
 constexpr int64_t kTargetBlocks = 1024;  // score_topk workgroups to aim for (4 per CU)
 constexpr int kStreamBlockRows = 256;    // score_keys rows per workgroup
 constexpr double kStreamKeysMax = 1024.0 * 1024 * 1024;  // key buffer budget (bytes)
+constexpr int64_t kMfmaMinVectors = 64;  // query vectors per KV head for the MFMA passes
+constexpr int kMfmaMaxTopk = 128;        // classes of the MFMA bound
+constexpr int kMfmaListMin = 256;        // candidate list capacity per query (at least)
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -144,6 +147,20 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     // reads it) when that buffer stays within kStreamKeysMax; others use the fused score_topk
     // kernel.
     P.stream = false;
+    P.mfma = false;
+    // Many bf16 query vectors per KV head: the MFMA passes (bound, then candidate lists in the
+    // segment layout of the chunked path, wpu * topk >= 256 keys per query).
+    if (P.candidates && p->chunk == 0 && P.dtype == CA_BF16 && P.topk <= kMfmaMaxTopk &&
+        nvec >= kMfmaMinVectors && nvec < ((int64_t)1 << 31) && P.nqv < ((int64_t)1 << 31)) {
+        P.mfma = true;
+        P.wpu = (kMfmaListMin + P.topk - 1) / P.topk;
+        P.lmax = (int64_t)P.wpu * P.topk;
+        P.nwg = 0;
+        const size_t slot_bytes = ((size_t)(3 * P.nqv * P.wpu) * sizeof(uint32_t) + 255) & ~(size_t)255;
+        P.lists_offset = slot_bytes;
+        P.ws_bytes = slot_bytes + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t);
+        return CA_OK;
+    }
     if (P.candidates && p->chunk == 0) {
         // Blocks of 256 rows from row 0 cover rows 1..rmax.
         const int64_t nblk = (P.rmax + kStreamBlockRows) / kStreamBlockRows;
@@ -205,7 +222,16 @@ int check_ws(const ca::Plan &pl, void *ws, size_t ws_bytes) {
 int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, int32_t *out_idx,
              float *out, void *ws, hipStream_t s) {
     hipError_t e;
-    if (pl.candidates && pl.stream) {
+    if (pl.candidates && pl.mfma) {
+        ProfScope pb(K_BOUND, s);
+        e = ca::launch_mfma_select(pl, q, k, ws, s, 0);
+        pb.done();
+        if (e != hipSuccess) return hip_fail(e, "mfma_select (bound) launch");
+        ProfScope pc(K_CAND, s);
+        e = ca::launch_mfma_select(pl, q, k, ws, s, 1);
+        pc.done();
+        if (e != hipSuccess) return hip_fail(e, "mfma_select (candidates) launch");
+    } else if (pl.candidates && pl.stream) {
         ProfScope ps(K_SCORE, s);
         e = ca::launch_score_keys(pl, q, k, ws, s);
         ps.done();
