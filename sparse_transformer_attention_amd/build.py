@@ -27,9 +27,14 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-source flags. The MFMA kernels take their products in VGPRs (read by VALU code at once)
+# rather than in accumulation registers, which would need a copy per value.
+FILE_FLAGS = {"mfma_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # The host pass does not know the packed-fp32 target feature and says so; that is harmless.
     noise = "'-packed-fp32-ops' is not a recognized feature"

@@ -31,7 +31,8 @@ struct Plan {
     int rcap;             // running-list capacity per query: 512, 768 or 1536
     int wpu;              // workgroups per unit
     int64_t nwg;          // score_topk workgroups
-    int64_t lmax;         // candidate slots per query (wpu * topk)
+    int64_t lmax;         // candidate slots per query (wpu * seg)
+    int seg;              // keys per segment: topk (score_topk) or kMfmaSeg (MFMA passes)
     size_t lists_offset;  // byte offset of the lists in the workspace
     size_t ws_bytes;      // total workspace
     // Decode path (score_keys, then finish reading its tile summaries): rows per unit covered
@@ -43,7 +44,7 @@ struct Plan {
     bool stream;
     // Prefill path with bf16 inputs (mfma_select bound + cand, then finish over the segments):
     // taus [nqv] in the first words of the workspace, the lengths and lists as above with
-    // wpu * topk >= 256 keys per query.
+    // wpu = 4 segments of seg = kMfmaSeg keys per query.
     bool mfma;
     int64_t rstride;
     int nblk;
@@ -66,6 +67,8 @@ hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void 
 // Query blocks of 16 per wavefront of the two MFMA passes (64 * QB query vectors per workgroup).
 constexpr int kMfmaQBBound = 4;
 constexpr int kMfmaQBCand = 4;
+// The candidate pass keeps four lists of kMfmaSeg keys per query (one per lane that holds it).
+constexpr int kMfmaSeg = 64;
 // pass 0: the bound of every query; pass 1: its candidate list.
 hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
                               int pass);

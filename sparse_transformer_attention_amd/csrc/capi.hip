@@ -85,7 +85,6 @@ constexpr int kStreamBlockRows = 256;    // score_keys rows per workgroup
 constexpr double kStreamKeysMax = 1024.0 * 1024 * 1024;  // key buffer budget (bytes)
 constexpr int64_t kMfmaMinVectors = 64;  // query vectors per KV head for the MFMA passes
 constexpr int kMfmaMaxTopk = 128;        // classes of the MFMA bound
-constexpr int kMfmaListMin = 256;        // candidate list capacity per query (at least)
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -148,13 +147,15 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     // kernel.
     P.stream = false;
     P.mfma = false;
+    P.seg = 1;
     // Many bf16 query vectors per KV head: the MFMA passes (bound, then candidate lists in the
-    // segment layout of the chunked path, wpu * topk >= 256 keys per query).
+    // segment layout of the chunked path: 4 segments of kMfmaSeg keys per query).
     if (P.candidates && p->chunk == 0 && P.dtype == CA_BF16 && P.topk <= kMfmaMaxTopk &&
         nvec >= kMfmaMinVectors && nvec < ((int64_t)1 << 31) && P.nqv < ((int64_t)1 << 31)) {
         P.mfma = true;
-        P.wpu = (kMfmaListMin + P.topk - 1) / P.topk;
-        P.lmax = (int64_t)P.wpu * P.topk;
+        P.wpu = 4;
+        P.seg = ca::kMfmaSeg;
+        P.lmax = (int64_t)P.wpu * P.seg;
         P.nwg = 0;
         const size_t slot_bytes = ((size_t)(3 * P.nqv * P.wpu) * sizeof(uint32_t) + 255) & ~(size_t)255;
         P.lists_offset = slot_bytes;
@@ -197,7 +198,8 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         P.wpu = (int)(w < nchunks ? w : nchunks);
     }
     P.nwg = P.wpu > 1 ? P.units * P.wpu : P.units;
-    P.lmax = (int64_t)P.wpu * (P.topk > 0 ? P.topk : 1);
+    P.seg = P.topk > 0 ? P.topk : 1;
+    P.lmax = (int64_t)P.wpu * P.seg;
     if (P.nwg > (int64_t)UINT32_MAX / 256 || P.nqv > (int64_t)UINT32_MAX / 256)
         return fail(CA_ERR_UNSUPPORTED, "problem too large for one launch");
     const double list_bytes = (double)P.nqv * (double)P.lmax * 8.0;

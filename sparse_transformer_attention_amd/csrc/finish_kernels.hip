@@ -20,10 +20,10 @@ namespace {
 
 struct FinishArgs {
     int64_t n, nq;
-    int Hq, Hkv, g, W, topk, cap, wpu;
+    int Hq, Hkv, g, W, topk, cap, wpu, seg;
     float scale_log2e;
     const uint32_t *cnt;    // [nqv][wpu] keys in each segment
-    const uint64_t *lists;  // [nqv][wpu][topk] segments of candidate ranking keys
+    const uint64_t *lists;  // [nqv][wpu][seg] segments of candidate ranking keys
     // Tile-summary path (score_keys): units of G query vectors, blocks and tiles of key rows.
     int G, nblk, tile_shift;  // rows per tile: 1 << tile_shift
     int64_t groups, rstride;
@@ -175,8 +175,8 @@ __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at,
     __syncthreads();
 }
 
-// Candidates from the segments score_topk left (the first cnt[w] keys of each segment w of
-// lists[w][0..topk)), gathered into LDS by wavefront 0 while the other wavefronts run
+// Candidates from the segments of score_topk or of the MFMA passes (the first cnt[w] keys of
+// each segment w of lists[w][0..seg)), gathered into LDS by wavefront 0 while the other wavefronts run
 // overlap(); then the exact top-kp.
 template <int NT, typename Overlap>
 __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt,
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
                                  rescore_tiles<T, D, NT>(q, kb, a, b, kvh, gq, t, (int)rl, ntl, tile_at, emit);
                              });
         } else {
-            select_segments<NT>(a.cnt + qv * a.wpu, a.lists + qv * a.wpu * a.topk, a.wpu, a.topk,
+            select_segments<NT>(a.cnt + qv * a.wpu, a.lists + qv * a.wpu * a.seg, a.wpu, a.seg,
                                 kp, js + base, sel, gathered, ssh, overlap);
         }
     } else {
@@ -600,7 +600,7 @@ __global__ __launch_bounds__(NT) void attend_kernel(const T *__restrict__ q, con
 FinishArgs finish_args(const Plan &pl, const void *ws) {
     FinishArgs a;
     a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g;
-    a.W = pl.W; a.topk = pl.topk; a.cap = pl.cap; a.wpu = pl.wpu;
+    a.W = pl.W; a.topk = pl.topk; a.cap = pl.cap; a.wpu = pl.wpu; a.seg = pl.seg;
     a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
     a.cnt = ws ? static_cast<const uint32_t *>(ws) + 2 * pl.nqv * pl.wpu : nullptr;
     a.lists = ws ? reinterpret_cast<const uint64_t *>(static_cast<const char *>(ws) + pl.lists_offset) : nullptr;

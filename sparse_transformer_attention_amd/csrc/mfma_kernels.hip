@@ -7,8 +7,9 @@
 // here on the matrix cores: v_mfma_f32_16x16x32_bf16 multiplies 16 key rows by 16 query vectors
 // over 32 elements of d per instruction, accumulating in fp32. A workgroup takes 64*QB query
 // vectors of one KV head (4 wavefronts of 16*QB, whose slices stay in registers) and brings the
-// key rows 0..max(i - W) through LDS in tiles of 64 rows: double-buffered, the 16-byte chunks
-// of a row XOR-swizzled so that the operand reads of 16 rows hit distinct banks. The scores are
+// key rows 0..max(i - W) through LDS in tiles of 64 rows: a ring of four tiles filled straight
+// from memory (global_load_lds) three tiles ahead of their use, the 16-byte chunks of a row
+// XOR-swizzled so that the operand reads of 16 rows hit distinct banks. The scores are
 // the plain dot products: the positive factor 1/sqrt(d) changes no order.
 //
 // The exact top-k' of R_i (k' = min(k, |R_i|) <= 128) takes two passes over the same products
@@ -35,8 +36,16 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;      // key rows per LDS tile
+constexpr int kBuf = 4;        // LDS ring of tiles: rows arrive three tiles ahead of their use
 constexpr int kXcds = 8;       // workgroups are dealt to the XCDs in turn
-constexpr int kKeepE = 8;      // keys per lane in a list cut (lists of up to 512)
+constexpr int kMaxKeep = 128;  // largest k' of the path
+constexpr int kLanesPerQuery = 4;  // lanes that hold one query's scores
+constexpr int kCutE = kLanesPerQuery * kMfmaSeg / 64;  // keys per lane in a list cut
+// A lane's list takes at most 16 keys per tile (4 blocks x 4 rows); it is cut before it might
+// not, and a cut leaves at most kMaxKeep / 4 keys in each of a query's lists.
+static_assert(kMaxKeep / kLanesPerQuery + 16 <= kMfmaSeg, "list room");
+
+__device__ __forceinline__ int wave_of_thread() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 struct MfmaArgs {
     int64_t n, nq;
@@ -44,10 +53,9 @@ struct MfmaArgs {
     uint32_t nvec;         // query vectors per KV head (g * nq)
     uint32_t wg_per_unit;  // workgroups per (batch, KV head)
     uint32_t nwg;          // workgroups of the launch
-    int wpu, lcap;         // segments per query, list capacity (wpu * topk)
     uint32_t *tau;         // [nqv] bound of each query (score key; 0xFFFFFFFF: no candidates)
-    uint32_t *cnt;         // [nqv][wpu] segment lengths
-    uint64_t *lists;       // [nqv][lcap] ranking keys
+    uint32_t *cnt;         // [nqv][4] list lengths
+    uint64_t *lists;       // [nqv][4][kMfmaSeg] ranking keys: list g is kept by lane group g
 };
 
 // Inverse of score_key for the admission test in float: keys below every finite score give
@@ -82,9 +90,12 @@ __device__ __forceinline__ uint32_t quad_min_u32(uint32_t x) {
 // then cover 16 distinct 16-byte bank groups (rows of 256 bytes: row & 15; of 128 bytes, two
 // rows share 256 bytes: (row >> 1) & 7).
 template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
 __device__ __forceinline__ int chunk_at(int row, int c) {
-    constexpr int CPR = D / 8;
-    return row * CPR + (c ^ (D == 128 ? (row & 15) : ((row >> 1) & 7)));
+    return row * (D / 8) + (c ^ chunk_swizzle<D>(row));
 }
 
 template <int D, int QB, bool CAND>
@@ -97,9 +108,18 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
     constexpr int QW = 16 * QB;                 // query vectors per wavefront
     constexpr int ROWS = 4 * QW;                // per workgroup
     static_assert(NCH >= 1 && NCH * 256 == kTile * CPR, "tile");
-    __shared__ uint4 kt[2][kTile * CPR];
-    __shared__ uint32_t lcnt[CAND ? ROWS : 1], ladm[CAND ? ROWS : 1];
-    __shared__ uint32_t hist[CAND ? 4 : 1][CAND ? 320 : 1];
+    // s_waitcnt with vmcnt = the loads a wavefront issues for kBuf - 2 tiles (expcnt and
+    // lgkmcnt at their maxima: no wait on them).
+    constexpr int kAhead = NCH * (kBuf - 2);
+    constexpr int kWaitAhead = (kAhead & 15) | (7 << 4) | (15 << 8) | ((kAhead >> 4) << 14);
+    // One LDS object: the tile ring, then (candidate pass) per wavefront the histogram of a list
+    // cut and the keys it keeps. (With several LDS objects the compiler waits for every tile in
+    // flight before each operand read; the waits below are the ones needed.)
+    constexpr int kCutWords = 320 + 2 * kMaxKeep;
+    constexpr int kExtra = CAND ? 4 * kCutWords / 4 : 0;
+    __shared__ uint4 smem[kBuf * kTile * CPR + kExtra];
+    uint4 (*kt)[kTile * CPR] = reinterpret_cast<uint4 (*)[kTile * CPR]>(smem);
+    uint32_t *cutw = reinterpret_cast<uint32_t *>(smem + kBuf * kTile * CPR) + wave_of_thread() * kCutWords;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -157,16 +177,18 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
     }
     const int ntiles = jmax >= 1 ? jmax / kTile + 1 : 0;
 
+    // Candidate pass: admission key of each query (a score is appended when its key reaches
+    // adm, tested first as a float against tf) and the length of this lane's list of it.
     float tf[QB];
+    uint32_t adm[QB], lc[QB];
+    uint64_t *lbase[QB];  // this lane's list of each query
     if constexpr (CAND) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const uint32_t adm = kq[qb] > 0 ? a.tau[qvi[qb]] : 0xFFFFFFFFu;
-            tf[qb] = key_floor_float(adm);
-            if (grp == 0) {
-                lcnt[wave * QW + qb * 16 + col] = 0u;
-                ladm[wave * QW + qb * 16 + col] = adm;
-            }
+            adm[qb] = kq[qb] > 0 ? a.tau[qvi[qb]] : 0xFFFFFFFFu;
+            tf[qb] = key_floor_float(adm[qb]);
+            lc[qb] = 0u;
+            lbase[qb] = a.lists + ((size_t)qvi[qb] * kLanesPerQuery + grp) * kMfmaSeg;
         }
     }
     float m[2][4][4][QB];  // [tile parity][16-row block][row of the lane][query]: class maxima
@@ -183,62 +205,75 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
 
     const __bf16 *kbase = k + (size_t)bk * (size_t)a.n * D;
     const int nlast = (int)a.n - 1;
-    uint4 pre[NCH];
-    auto gload = [&](int t) {
+    // The wavefronts' share of tile t, straight from memory into LDS buffer B: instruction u of
+    // wavefront w fills chunks (4u + w)*64 .. +63 of the tile, lane by lane (16 bytes each), so
+    // lane l fetches the row chunk that the swizzle puts there. Rows past n - 1 are clamped.
+    auto issue = [&](int t, auto bufc) {
+        constexpr int B = decltype(bufc)::value;
 #pragma unroll
         for (int u = 0; u < NCH; ++u) {
-            const int cid = tid + 256 * u, row = cid / CPR, c = cid % CPR;
+            const int p = (u * 4 + wave) * 64 + lane;
+            const int row = p / CPR, c = (p % CPR) ^ chunk_swizzle<D>(row);
             const int j = t * kTile + row;
-            pre[u] = reinterpret_cast<const uint4 *>(kbase + (size_t)(j < nlast ? j : nlast) * D)[c];
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int cid = tid + 256 * u, row = cid / CPR, c = cid % CPR;
-            kt[buf][chunk_at<D>(row, c)] = pre[u];
+            const __bf16 *src = kbase + (size_t)(j < nlast ? j : nlast) * D + c * 8;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)&kt[B][(u * 4 + wave) * 64],
+                                             16, 0, 0);
         }
     };
 
-    // Cut of list ql (wavefront-local) to its exact top-k'; returns nothing, updates LDS and tf.
-    auto cut_list = [&](int ql) {
-        uint32_t qv;
-        int lm;
-        vec_of(idx_w + (uint32_t)ql, qv, lm);
+    // Cut of the four lists of query col c of block QBC (wavefront-uniform): the exact top-k'
+    // of their keys so far (wave_keep_top_u64), dealt back to the lists in turn (key e to list
+    // e mod 4). When k' keys are kept, a later row can only enter with a larger score: its
+    // position is larger than theirs.
+    auto cut_list = [&](auto qbc, int c) {
+        constexpr int QBC = decltype(qbc)::value;
+        const uint32_t qv = __builtin_amdgcn_readlane(qvi[QBC], c);
+        const int lm = __builtin_amdgcn_readlane(lim[QBC], c);
         const int keep = a.topk < lm ? a.topk : lm;
-        const int row = wave * QW + ql;
-        __threadfence_block();  // this wavefront's appends are visible to its loads
-        const uint32_t c = lcnt[row];
-        uint64_t *lst = a.lists + (size_t)qv * a.lcap;
-        uint64_t kr[kKeepE];
+        uint32_t n4[kLanesPerQuery];
+        int total = 0;
 #pragma unroll
-        for (int e = 0; e < kKeepE; ++e) {
-            const uint32_t f = lane + 64 * e;
-            kr[e] = f < c ? lst[f] : 0ull;
+        for (int gq = 0; gq < kLanesPerQuery; ++gq) {
+            n4[gq] = __builtin_amdgcn_readlane(lc[QBC], c + 16 * gq);
+            total += (int)n4[gq];
         }
-        const uint32_t hi = wave_keep_top_u64(kr, keep, hist[wave], lst);
-        __threadfence_block();
-        const uint32_t adm = hi + 1u > ladm[row] ? hi + 1u : ladm[row];
-        if (lane == 0) { lcnt[row] = (uint32_t)keep; ladm[row] = adm; }
-        const float f = key_floor_float(adm);
+        uint64_t *lst = a.lists + (size_t)qv * (kLanesPerQuery * kMfmaSeg);
+        __threadfence_block();  // this wavefront's appends are visible to its loads
+        uint64_t kr[kCutE];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-            if (qb * 16 + col == ql) tf[qb] = f;
+        for (int e = 0; e < kCutE; ++e) {
+            const int f = lane + 64 * e, gq = f / kMfmaSeg;
+            kr[e] = (uint32_t)(f % kMfmaSeg) < n4[gq] ? lst[f] : 0ull;
+        }
+        uint64_t *kept = reinterpret_cast<uint64_t *>(cutw + 320);
+        const uint32_t hi = wave_keep_top_u64(kr, keep, cutw, kept);
+        const int nk = total < keep ? total : keep;
+        for (int e = lane; e < nk; e += 64) lst[(e % kLanesPerQuery) * kMfmaSeg + e / kLanesPerQuery] = kept[e];
+        __threadfence_block();
+        if (col == c) {
+            lc[QBC] = (uint32_t)((nk - grp + kLanesPerQuery - 1) / kLanesPerQuery);
+            if (total >= keep) {
+                adm[QBC] = hi + 1u > adm[QBC] ? hi + 1u : adm[QBC];
+                tf[QBC] = key_floor_float(adm[QBC]);
+            }
+        }
     };
 
-    // Products of tile t (LDS buffer buf) with this wavefront's queries; P = t & 1.
-    auto compute = [&](int t, int buf, auto parity) {
-        constexpr int P = decltype(parity)::value;
+    // Products of tile t (LDS buffer B, t = B mod kBuf, so t & 1 = B & 1) with this wavefront's
+    // queries: four blocks of 16 rows; the products of block kb + 1 are issued before block kb
+    // is examined.
+    auto compute = [&](int t, auto bufc) {
+        constexpr int B = decltype(bufc)::value;
+        constexpr int P = B & 1;
         const int j0 = t * kTile;
         const bool inner = j0 >= 1 && j0 + kTile - 1 <= lim_lo;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        auto products = [&](int kb, f32x4_t (&acc)[QB]) {
             bf16x8_t af[KS];
             const int row = kb * 16 + col;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                af[ks] = __builtin_bit_cast(bf16x8_t, kt[buf][chunk_at<D>(row, ks * 4 + grp)]);
-            f32x4_t acc[QB];
+                af[ks] = __builtin_bit_cast(bf16x8_t, kt[B][chunk_at<D>(row, ks * 4 + grp)]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) acc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -246,7 +281,11 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], qf[qb][ks], acc[qb], 0, 0, 0);
-            // acc[qb][r]: row jb + r of the tile for query qb*16 + col.
+        };
+        // acc[qb][r]: row jb + r of the tile for query qb*16 + col.
+        auto examine = [&](auto kbc, const f32x4_t (&acc)[QB], auto innerc) {
+            constexpr int kb = decltype(kbc)::value;
+            constexpr bool INNER = decltype(innerc)::value;
             const int jb = j0 + kb * 16 + 4 * grp;
             if constexpr (!CAND) {
 #pragma unroll
@@ -254,61 +293,91 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         float v = acc[qb][r];
-                        if (!inner) v = (jb + r >= 1 && jb + r <= lim[qb]) ? v : -INFINITY;
+                        if constexpr (!INNER) v = (jb + r >= 1 && jb + r <= lim[qb]) ? v : -INFINITY;
                         m[P][kb][r][qb] = fmaxf(m[P][kb][r][qb], v);
                     }
             } else {
-                bool hit = false;
+                // About k + k/4 of a query's rows reach its bound, so with 64 queries a block
+                // of 16 rows holds a few on average: each (query block, row) slot with a score
+                // that passes in some lane appends it, the others cost a branch.
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) hit |= acc[qb][r] >= tf[qb];
-                if (__builtin_expect(__ballot(hit) != 0ull, 0)) {
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = jb + r;
-                            const float v = acc[qb][r];
-                            if (v >= tf[qb] && j >= 1 && j <= lim[qb]) {
-                                const uint32_t key = score_key(v);
-                                const int row = wave * QW + qb * 16 + col;
-                                if (key >= ladm[row]) {
-                                    const uint32_t pos = atomicAdd(&lcnt[row], 1u);
-                                    a.lists[(size_t)qvi[qb] * a.lcap + pos] = make_rank_key(key, (uint32_t)j);
-                                }
-                            }
+                    for (int r = 0; r < 4; ++r) {
+                        const float v = acc[qb][r];
+                        bool h = v >= tf[qb];
+                        if constexpr (!INNER) h = h && jb + r >= 1 && jb + r <= lim[qb];
+                        // (v >= tf is key >= adm: score_key orders every non-NaN float as
+                        // the float compare does, -0 and +0 alike.)
+                        if (__builtin_expect(__ballot(h) != 0ull, 0) && h) {
+                            lbase[qb][lc[qb]] = make_rank_key(score_key(v), (uint32_t)(jb + r));
+                            ++lc[qb];
                         }
-                }
+                    }
+                // (These stores may still be in flight at the next tile's wait: loads complete
+                // in order among themselves, so the wait still covers the tile.)
             }
-        }
+        };
+        // Tiles inside every query's candidate rows need no row mask: a separate copy of the
+        // code, so that no test is made per score.
+        auto run = [&](auto innerc) {
+            f32x4_t acc0[QB], acc1[QB];
+            products(0, acc0);
+            products(1, acc1);
+            examine(std::integral_constant<int, 0>(), acc0, innerc);
+            products(2, acc0);
+            examine(std::integral_constant<int, 1>(), acc1, innerc);
+            products(3, acc1);
+            examine(std::integral_constant<int, 2>(), acc0, innerc);
+            examine(std::integral_constant<int, 3>(), acc1, innerc);
+        };
+        if (inner) run(std::true_type());
+        else run(std::false_type());
         if constexpr (CAND) {
-            // A list that might not take another tile (64 more rows) is cut now.
-            const bool full = lane < QW && lcnt[wave * QW + lane] + kTile > (uint32_t)a.lcap;
-            uint64_t bal = __ballot(full);
-            while (bal) {
-                const int ql = __builtin_ctzll(bal);
-                bal &= bal - 1ull;
-                cut_list(ql);
-            }
+            // Lists that might not take another tile are cut now.
+            auto cut_full = [&](auto qbc) {
+                constexpr int QBC = decltype(qbc)::value;
+                const uint64_t bal = __ballot(lc[QBC] + 16u > (uint32_t)kMfmaSeg);
+                uint32_t cols = (uint32_t)(bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xFFFFu;
+                while (cols) {
+                    const int c = __builtin_ctz(cols);
+                    cols &= cols - 1u;
+                    cut_list(qbc, c);
+                }
+            };
+            cut_full(std::integral_constant<int, 0>());
+            if constexpr (QB > 1) cut_full(std::integral_constant<int, 1>());
+            if constexpr (QB > 2) cut_full(std::integral_constant<int, 2>());
+            if constexpr (QB > 3) cut_full(std::integral_constant<int, 3>());
         }
     };
 
-    if (ntiles > 0) {
-        gload(0);
-        lstore(0);
+    // One tile: wait for this wavefront's part of tile t (the loads of the kBuf - 2 tiles after
+    // it may still fly), then for everyone's (the barrier also ends every use of the buffer that
+    // the next issue refills), issue tile t + kBuf - 1, compute tile t.
+    auto step = [&](int t, auto bufc) {
+        constexpr int B = decltype(bufc)::value;
+        // (A plain barrier: __syncthreads would also wait for the loads of the tiles ahead.)
+        __builtin_amdgcn_s_waitcnt(kWaitAhead);
+        asm volatile("s_barrier" ::: "memory");
+        issue(t + kBuf - 1, std::integral_constant<int, (B + kBuf - 1) % kBuf>());
+        if (t <= t_wave) compute(t, bufc);
+    };
+    // Tiles past the last one are fetched too (clamped rows, never read), so that every wait
+    // counts the same loads.
+    issue(0, std::integral_constant<int, 0>());
+    issue(1, std::integral_constant<int, 1>());
+    issue(2, std::integral_constant<int, 2>());
+    static_assert(kBuf == 4, "ring");
+    for (int t0 = 0; t0 < ntiles; t0 += kBuf) {
+        step(t0, std::integral_constant<int, 0>());
+        if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 1>());
+        if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>());
+        if (t0 + 3 < ntiles) step(t0 + 3, std::integral_constant<int, 3>());
     }
+    // No LDS fill may outlive the workgroup.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) gload(t + 1);
-        if (t <= t_wave) {
-            if (t & 1) compute(t, buf, std::integral_constant<int, 1>());
-            else compute(t, buf, std::integral_constant<int, 0>());
-        }
-        if (t + 1 < ntiles) lstore(buf ^ 1);
-        __syncthreads();
-    }
 
     if constexpr (!CAND) {
         // Bound of each query from its 128 class maxima (32 in each of its four lanes).
@@ -352,16 +421,9 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
             if (grp == 0 && lim[qb] == -1 && idx_w + qb * 16 + col < a.nvec) a.tau[qvi[qb]] = 0xFFFFFFFFu;
         }
     } else {
-        if (lane < QW && idx_w + lane < a.nvec) {
-            uint32_t qv;
-            int lm;
-            vec_of(idx_w + (uint32_t)lane, qv, lm);
-            const int total = (int)lcnt[wave * QW + lane];
-            for (int w = 0; w < a.wpu; ++w) {
-                const int c = total - w * a.topk;
-                a.cnt[(size_t)qv * a.wpu + w] = (uint32_t)(c < 0 ? 0 : (c > a.topk ? a.topk : c));
-            }
-        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            if (idx_w + qb * 16 + col < a.nvec) a.cnt[(size_t)qvi[qb] * kLanesPerQuery + grp] = lc[qb];
     }
 }
 
@@ -372,8 +434,6 @@ hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void
     MfmaArgs a;
     a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g; a.W = pl.W; a.topk = pl.topk;
     a.nvec = (uint32_t)(pl.g * pl.nq);
-    a.wpu = pl.wpu;
-    a.lcap = (int)pl.lmax;
     char *w = static_cast<char *>(ws);
     a.tau = reinterpret_cast<uint32_t *>(w);
     a.cnt = reinterpret_cast<uint32_t *>(w) + 2 * pl.nqv * pl.wpu;
