@@ -65,7 +65,7 @@ hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k
 size_t topk_lds_bytes(const Plan &pl);
 hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s);
 // Query blocks of 16 per wavefront of the two MFMA passes (64 * QB query vectors per workgroup).
-constexpr int kMfmaQBBound = 4;
+constexpr int kMfmaQBBound = 2;
 constexpr int kMfmaQBCand = 4;
 // The candidate pass keeps four lists of kMfmaSeg keys per query (one per lane that holds it).
 constexpr int kMfmaSeg = 64;

@@ -89,7 +89,8 @@ class Workload:
 
 
 # The five workloads: a small prefill the oracle finishes in seconds, an 8K MHA decode,
-# the 131K GQA decode, a 4K-query prefill chunk over 32K keys and a 1M-token batch-4 decode.
+# the 131K GQA decode, a 4K-query prefill chunk over 32K keys and a 1M-token batch-4 decode;
+# then a full 131K prefill and the 131K decode at other window sizes.
 WORKLOADS = {
     "prefill_1k_f32": Workload(
         "prefill_1k_f32", batch=1, heads=1, kv_heads=1, d=64, n=1024, nq=1024, dtype="f32",
@@ -106,6 +107,21 @@ WORKLOADS = {
     "decode_1m_b4_gqa_bf16": Workload(
         "decode_1m_b4_gqa_bf16", batch=4, heads=32, kv_heads=8, d=128, n=1048576, nq=1,
         dtype="bf16", W=256, topk=128, q_scale=2.0, needles_per_kv_head=512),
+    # Full causal prefill at the shape of the pages' timing table (section 5.1.2: 8 heads,
+    # d = 64, 131,072 tokens), with the defaults of their two-stage sketch (section 5.2.2:
+    # W = 64, k = 32).
+    "prefill_131k_h8_bf16": Workload(
+        "prefill_131k_h8_bf16", batch=1, heads=8, kv_heads=8, d=64, n=131072, nq=131072,
+        dtype="bf16", W=64, topk=32, q_scale=1.0, needles_per_kv_head=64, mode="prefill"),
+    # The 131K GQA decode with the other windows of the pages' per-layer schedule (sections
+    # 6.1-6.2: W = 1024 in the shallow quarter of the layers, 256 in the next quarter, 64 in
+    # the deep half).
+    "decode_131k_gqa_w64_bf16": Workload(
+        "decode_131k_gqa_w64_bf16", batch=1, heads=32, kv_heads=8, d=128, n=131072, nq=1,
+        dtype="bf16", W=64, topk=64, q_scale=2.0, needles_per_kv_head=64),
+    "decode_131k_gqa_w1024_bf16": Workload(
+        "decode_131k_gqa_w1024_bf16", batch=1, heads=32, kv_heads=8, d=128, n=131072, nq=1,
+        dtype="bf16", W=1024, topk=64, q_scale=2.0, needles_per_kv_head=64),
 }
 
 WORKLOAD_ORDER = list(WORKLOADS)

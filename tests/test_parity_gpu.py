@@ -299,3 +299,29 @@ def test_full_size_prefill_chunk_4k_32k():
     rows += [(0, int(torch.randint(w.heads, (1,), generator=g)), int(torch.randint(w.nq, (1,), generator=g)))
              for _ in range(12)]
     check_sampled(w, x, out.cpu().numpy(), idx.cpu().numpy(), rows)
+
+
+def test_full_size_prefill_131k():
+    """Full causal prefill, 8 heads, d = 64, 131,072 positions (every position a query): the
+    first W rows have no candidates, the next ones fewer than k."""
+    w = synth.WORKLOADS["prefill_131k_h8_bf16"]
+    x = synth.make_inputs(w, device="cuda")
+    announce("full-size prefill 131k")
+    out, idx = ca.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(1)
+    rows = [(0, 0, 0), (0, 1, w.W), (0, 2, w.W + 1), (0, 3, w.W + w.topk), (0, 7, w.nq - 1)]
+    rows += [(0, int(torch.randint(w.heads, (1,), generator=g)), int(torch.randint(w.nq, (1,), generator=g)))
+             for _ in range(11)]
+    check_sampled(w, x, out.cpu().numpy(), idx.cpu().numpy(), rows)
+
+
+@pytest.mark.parametrize("name", ["decode_131k_gqa_w64_bf16", "decode_131k_gqa_w1024_bf16"])
+def test_full_size_decode_131k_other_windows(name):
+    """The 131K GQA decode with W = 64 and W = 1024; every query vector checked."""
+    w = synth.WORKLOADS[name]
+    x = synth.make_inputs(w, device="cuda")
+    announce(f"full-size {name}")
+    out, idx = ca.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    torch.cuda.synchronize()
+    check_sampled(w, x, out.cpu().numpy(), idx.cpu().numpy(), [(0, h, 0) for h in range(w.heads)])
