@@ -185,13 +185,15 @@ def main():
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": pass_s * 1e6,
         }
-    launches, score_ms = prof.get("score_select", (0, 0.0))
+    # Decode path: score_keys; chunked path: score_topk (profiled as score_select).
+    score_name = "score_keys" if "score_keys" in prof else "score_select"
+    launches, score_ms = prof.get(score_name, (0, 0.0))
     score_avg_s = score_ms / max(1, launches) / 1e3
     achieved = score_bytes / score_avg_s / 1e9 if launches else None
     traffic = recorded_traffic(w.name)
     if "mfma_bound" not in prof:
         roofline = {
-            "kernel": "score_keys (score stage)" if not args.chunk else "score_topk (score stage)",
+            "kernel": "score_keys (score stage)" if score_name == "score_keys" else "score_topk (score stage)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,

@@ -200,7 +200,7 @@ __device__ __forceinline__ void merge_partials(SoftmaxPartials<D, NP> &ps, int p
         const float lsum = wave_sum_f32_dpp(l * f);
         if (p < p1) ps.f[p] = f / lsum;
     }
-    __syncthreads();
+    lds_barrier();
     for (int t = tid; t < D; t += NT) {
         float o = 0.f;
 #pragma unroll 8

@@ -13,8 +13,9 @@
 namespace {
 
 // ---- measurement hooks: HIP events around each launch while profiling is on ----------------
-enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_BOUND = 3, K_CAND = 4, K_COUNT = 5 };
-const char *const kKernelNames[K_COUNT] = {"score_select", "finish", "attend", "mfma_bound", "mfma_cand"};
+enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_BOUND = 3, K_CAND = 4, K_KEYS = 5, K_COUNT = 6 };
+const char *const kKernelNames[K_COUNT] = {"score_select", "finish", "attend", "mfma_bound", "mfma_cand",
+                                           "score_keys"};
 
 struct Profiler {
     std::mutex mu;
@@ -234,7 +235,7 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
         pc.done();
         if (e != hipSuccess) return hip_fail(e, "mfma_select (candidates) launch");
     } else if (pl.candidates && pl.stream) {
-        ProfScope ps(K_SCORE, s);
+        ProfScope ps(K_KEYS, s);
         e = ca::launch_score_keys(pl, q, k, ws, s);
         ps.done();
         if (e != hipSuccess) return hip_fail(e, "score_keys launch");

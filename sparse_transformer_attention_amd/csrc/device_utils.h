@@ -112,6 +112,18 @@ __device__ __forceinline__ uint32_t score_key(float s) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The score a key of score_key stands for (any key >= 0x00800000).
+__device__ __forceinline__ float key_score(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Workgroup barrier for LDS traffic: waits for this wavefront's LDS operations, not for its
+// vector memory loads in flight (__syncthreads waits for those as well).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not constrained
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // Count of set bits of `m` in lanes below this one.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
