@@ -46,6 +46,7 @@ struct Plan {
     // taus [nqv] in the first words of the workspace, the lengths and lists as above with
     // wpu = 4 segments of seg = kMfmaSeg keys per query.
     bool mfma;
+    size_t win_offset;    // MFMA path: anchor-and-window partials [nqv][d + 2] floats
     int64_t rstride;
     int nblk;
     int tile_rows;
@@ -72,6 +73,9 @@ constexpr int kMfmaSeg = 64;
 // pass 0: the bound of every query; pass 1: its candidate list.
 hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
                               int pass);
+// Anchor-and-window softmax partials of every query vector into the workspace (MFMA path).
+hipError_t launch_mfma_window(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
+                              hipStream_t s);
 
 
 }  // namespace ca

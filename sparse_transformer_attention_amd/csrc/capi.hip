@@ -13,9 +13,10 @@
 namespace {
 
 // ---- measurement hooks: HIP events around each launch while profiling is on ----------------
-enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_BOUND = 3, K_CAND = 4, K_KEYS = 5, K_COUNT = 6 };
+enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_BOUND = 3, K_CAND = 4, K_KEYS = 5, K_WINDOW = 6,
+       K_COUNT = 7 };
 const char *const kKernelNames[K_COUNT] = {"score_select", "finish", "attend", "mfma_bound", "mfma_cand",
-                                           "score_keys"};
+                                           "score_keys", "mfma_window"};
 
 struct Profiler {
     std::mutex mu;
@@ -149,6 +150,7 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     P.stream = false;
     P.mfma = false;
     P.seg = 1;
+    P.win_offset = 0;
     // Many bf16 query vectors per KV head: the MFMA passes (bound, then candidate lists in the
     // segment layout of the chunked path: 4 segments of kMfmaSeg keys per query).
     if (P.candidates && p->chunk == 0 && P.dtype == CA_BF16 && P.topk <= kMfmaMaxTopk &&
@@ -160,7 +162,8 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         P.nwg = 0;
         const size_t slot_bytes = ((size_t)(3 * P.nqv * P.wpu) * sizeof(uint32_t) + 255) & ~(size_t)255;
         P.lists_offset = slot_bytes;
-        P.ws_bytes = slot_bytes + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t);
+        P.win_offset = (slot_bytes + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) + 255) & ~(size_t)255;
+        P.ws_bytes = P.win_offset + (size_t)P.nqv * (size_t)(P.d + 2) * sizeof(float);
         return CA_OK;
     }
     if (P.candidates && p->chunk == 0) {
@@ -234,6 +237,12 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
         e = ca::launch_mfma_select(pl, q, k, ws, s, 1);
         pc.done();
         if (e != hipSuccess) return hip_fail(e, "mfma_select (candidates) launch");
+        if (v) {
+            ProfScope pw(K_WINDOW, s);
+            e = ca::launch_mfma_window(pl, q, k, v, ws, s);
+            pw.done();
+            if (e != hipSuccess) return hip_fail(e, "mfma_window launch");
+        }
     } else if (pl.candidates && pl.stream) {
         ProfScope ps(K_KEYS, s);
         e = ca::launch_score_keys(pl, q, k, ws, s);

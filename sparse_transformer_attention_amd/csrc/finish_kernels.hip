@@ -32,6 +32,7 @@ struct FinishArgs {
     const uint2 *rest;        // second key; offsets of the best two (bits 0-15), third key's upper half
     const uint32_t *bmax;     // [units][nblk][G]
     uint32_t *scratch;        // [nqv][rstride]
+    const float *win;         // [nqv][D + 2] anchor-and-window partials (MFMA path), or null
 };
 
 constexpr int kGather = 1024;  // candidates gathered into LDS for the one-wavefront select
@@ -186,15 +187,29 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
                                                 Overlap overlap) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (wave == 0) {
+        // Every slot of every segment, four per lane in flight with their segments' lengths,
+        // kept when inside its segment's length (compacted by ballot).
+        constexpr int GU = 4;
+        const int slots = wpu * topk;
         int base = 0;
-        for (int j0 = 0; j0 < wpu; j0 += 64) {
-            const int w = j0 + lane;
-            const int c = w < wpu ? (int)cnt[w] : 0;
-            int tot;
-            const int off = base + wave_excl_scan(c, &tot);
-            for (int e = 0; e < c; ++e)
-                if (off + e < kGather) gathered[off + e] = lists[(size_t)w * topk + e];
-            base += tot;
+        for (int f0 = 0; f0 < slots; f0 += 64 * GU) {
+            uint64_t x[GU];
+            uint32_t c[GU];
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                const int f = f0 + u * 64 + lane, fc = f < slots ? f : slots - 1;
+                x[u] = lists[fc];
+                c[u] = cnt[fc / topk];
+            }
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                const int f = f0 + u * 64 + lane;
+                const bool ok = f < slots && (uint32_t)(f % topk) < c[u];
+                const uint64_t bal = __ballot(ok);
+                const int pos = base + lanes_below(bal);
+                if (ok && pos < kGather) gathered[pos] = x[u];
+                base += __popcll(bal);
+            }
         }
         if (lane == 0) sh.sel_count = base;
     } else {
@@ -515,9 +530,10 @@ __device__ __forceinline__ void rescore_tiles(const T *__restrict__ q, const T *
 
 // Rows per lane in flight in the attend phase (rows past the set's end are loaded as clamped
 // duplicates, so these match the common sizes: 15 wavefronts x 4 rows x 5 cover the anchor and
-// a window of up to 299 rows of 256 bytes in one round, 16 x 4 x 1 a top-64 part).
+// a window of up to 299 rows of 256 bytes in one round, 16 x 4 x 1 or 4 x 4 x 4 a top-64 part).
 constexpr int kWindowU = 5;
-constexpr int kTopU = 1;
+template <int NT>
+constexpr int kTopU = NT >= 1024 ? 1 : 4;  // 256 threads: 4 x 4 x 4 rows, still one round
 
 template <typename T, int D, int NT, bool ATTEND, bool TILES>
 __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, const T *__restrict__ k,
@@ -566,8 +582,20 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     const T *kb = k + kv0, *vb = v + kv0;
     uint4 qs = make_uint4(0, 0, 0, 0);
     if constexpr (ATTEND) qs = reinterpret_cast<const uint4 *>(q + qv * D)[lane % AttendShape<D, T>::LPR];
+    // MFMA path: mfma_window computed the anchor-and-window partial already; it goes to slot
+    // NW - 1, next to the top-k rows' partials NW..2NW-1.
+    const bool pre_win = a.win != nullptr;
+    if constexpr (ATTEND) {
+        if (pre_win && tid >= 64 && tid < 64 + D + 2) {
+            const float x = a.win[(size_t)qv * (D + 2) + (tid - 64)];
+            if (tid == 64) part.m[NW - 1] = x;
+            else if (tid == 65) part.l[NW - 1] = x;
+            else part.acc[NW - 1][tid - 66] = x;
+        }
+    }
     auto window_part = [&](int wv, int nw) {
         if constexpr (ATTEND) {
+            if (pre_win) return;
             auto row_at = [&](int c) -> size_t { return c < base ? 0 : (size_t)(wlo - base + c); };
             wave_partial<D, T, kWindowU>(qs, kb, vb, row_at, base + wcount, wv, nw, a.scale_log2e,
                                          part, wave);
@@ -607,13 +635,13 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
         if (kp > 0 && !top_done) {
             const int32_t *top = js + base;
             auto row_at = [&](int c) -> size_t { return (size_t)(uint32_t)top[c]; };
-            wave_partial<D, T, kTopU>(qs, kb, vb, row_at, kp, wave, NW, a.scale_log2e, part, NW + wave);
+            wave_partial<D, T, kTopU<NT>>(qs, kb, vb, row_at, kp, wave, NW, a.scale_log2e, part, NW + wave);
         }
         // (The index row's stores need not complete before the merge: LDS only.)
         lds_barrier();
-        // Window partials: 1..NW-1 (wavefront 0 took the bound) or 0..NW-1; top-k partials
-        // NW..2NW-1.
-        const int p0 = kp > 0 ? 1 : 0;
+        // Window partials: NW-1 (from mfma_window), 1..NW-1 (wavefront 0 took the bound) or
+        // 0..NW-1; top-k partials NW..2NW-1.
+        const int p0 = pre_win ? NW - 1 : (kp > 0 ? 1 : 0);
         merge_partials<NT, D>(part, p0, kp > 0 ? 2 * NW : NW, a.scale_log2e, out + qv * D);
     }
 }
@@ -684,6 +712,7 @@ FinishArgs finish_args(const Plan &pl, const void *ws) {
     a.bmax = sm ? reinterpret_cast<const uint32_t *>(wb + pl.bmax_offset) : nullptr;
     a.scratch = sm ? reinterpret_cast<uint32_t *>(const_cast<char *>(wb) + pl.scratch_offset) : nullptr;
     a.nvec = (uint32_t)(pl.g * pl.nq);
+    a.win = ws && pl.mfma ? reinterpret_cast<const float *>(wb + pl.win_offset) : nullptr;
     return a;
 }
 

@@ -73,6 +73,13 @@ __device__ __forceinline__ uint32_t quad_sum_u32(uint32_t x) {
     const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
     return r32[0] + r32[1];
 }
+// Float sum over the same four lanes (bits in, bits out), in a fixed order.
+__device__ __forceinline__ uint32_t quad_sum_f32_bits(uint32_t x) {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    float y = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __float_as_uint(__uint_as_float(r32[0]) + __uint_as_float(r32[1]));
+}
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t x) {
     const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
     x = r16[0] > r16[1] ? r16[0] : r16[1];
@@ -427,6 +434,200 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
     }
 }
 
+// Anchor-and-window softmax partials of the query vectors (pages of "The Condensate Theorem",
+// metaphor-xennon blog: section 2.1 Definition 1, {0} u {i-W+1..i}; section 2.3, the softmax
+// over C_i and its product with V). Consecutive positions share almost all of their window
+// rows, so a workgroup takes 64 query vectors of one KV head (16 per wavefront) and brings the
+// rows of their windows (and row 0) through LDS once, in tiles of 64 rows. Per tile and
+// wavefront the scores are K . Q^T on the matrix cores (the layout of the selection passes:
+// lane l holds query l % 16 and rows 4(l/16)..+3 of each block of 16), masked to each query's
+// anchor and window, folded into a running softmax (largest score m, weight sum l), and the
+// weights times V are accumulated as O^T += V^T P^T: the weights a lane holds for two blocks of
+// 16 rows are exactly its B operand of one 32-row step (the same rows on both sides of the
+// contraction), and V^T comes from a transposed copy of the tile in LDS. The weights enter the
+// product as bf16 (relative error 2^-9 per weight), accumulation is fp32. Output per query
+// vector: m, l and the weighted sum of V rows, the partial the finish kernel merges.
+constexpr int kWinTile = 64;
+constexpr int kVtStride = kWinTile + 4;  // bf16 per transposed V row (padded against bank conflicts)
+
+struct WinArgs {
+    int64_t n, nq;
+    int Hq, Hkv, g, W;
+    uint32_t nvec, wg_per_unit, nwg;
+    float scale_log2e;
+    float *win;  // [nqv][D + 2]
+};
+
+// K and V rows base..base+63 of a tile (clamped to n - 1): 16-byte chunks, NCH per thread.
+// (Native 4 x u32 vectors: arrays of HIP's uint4 struct filled from memory stay on the stack.)
+typedef unsigned int win_u32x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+__device__ __forceinline__ void win_tile_load(win_u32x4 (&pk)[kWinTile * D / 8 / 256],
+                                              win_u32x4 (&pv)[kWinTile * D / 8 / 256],
+                                              const __bf16 *__restrict__ kb, const __bf16 *__restrict__ vb,
+                                              int base, int nlast, int tid) {
+    constexpr int CPR = D / 8, NCH = kWinTile * CPR / 256;
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+        const int cid = tid + 256 * u, row = cid / CPR, c = cid % CPR;
+        const int j = base + row < nlast ? base + row : nlast;
+        pk[u] = reinterpret_cast<const win_u32x4 *>(kb + (size_t)j * D)[c];
+        pv[u] = reinterpret_cast<const win_u32x4 *>(vb + (size_t)j * D)[c];
+    }
+}
+// The tile into LDS: K with swizzled chunks, V transposed ([d][row], bf16 bits).
+template <int D>
+__device__ __forceinline__ void win_tile_store(const win_u32x4 (&pk)[kWinTile * D / 8 / 256],
+                                               const win_u32x4 (&pv)[kWinTile * D / 8 / 256], uint4 *kt,
+                                               uint16_t *vt, int tid) {
+    constexpr int CPR = D / 8, NCH = kWinTile * CPR / 256;
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+        const int cid = tid + 256 * u, row = cid / CPR, c = cid % CPR;
+        reinterpret_cast<win_u32x4 *>(kt)[chunk_at<D>(row, c)] = pk[u];
+        uint16_t *vd = vt + (c * 8) * kVtStride + row;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vd[(2 * e) * kVtStride] = (uint16_t)pv[u][e];
+            vd[(2 * e + 1) * kVtStride] = (uint16_t)(pv[u][e] >> 16);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void mfma_window_kernel(const __bf16 *__restrict__ q,
+                                                          const __bf16 *__restrict__ k,
+                                                          const __bf16 *__restrict__ v, WinArgs a) {
+    constexpr int KS = D / 32, CPR = D / 8, NCH = kWinTile * CPR / 256, DB = D / 16;
+    static_assert(NCH * 256 == kWinTile * CPR, "tile");
+    __shared__ uint4 kt[kWinTile * CPR];
+    __shared__ uint16_t vt[D * kVtStride];  // bf16 bits
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+    const uint32_t bid = blockIdx.x, xcd = bid % kXcds;
+    const uint32_t per = a.nwg / kXcds, rem = a.nwg % kXcds;
+    const uint32_t L = xcd * per + (xcd < rem ? xcd : rem) + bid / kXcds;
+    const uint32_t bk = L / a.wg_per_unit, part = L - bk * a.wg_per_unit;
+    const uint32_t b = bk / (uint32_t)a.Hkv, kvh = bk - b * (uint32_t)a.Hkv, g = (uint32_t)a.g;
+    auto pos_of = [&](uint32_t idx) -> int { return (int)(a.n - a.nq + idx / g); };
+    // This lane's query vector.
+    const uint32_t idx = part * 64 + wave * 16 + col;
+    const bool valid = idx < a.nvec;
+    const uint32_t idxc = valid ? idx : a.nvec - 1;
+    const uint32_t qv = (b * (uint32_t)a.Hq + kvh * g + idxc % g) * (uint32_t)a.nq + idxc / g;
+    const int i = pos_of(idxc);
+    const int wlo = i - a.W + 1 > 0 ? i - a.W + 1 : 0;
+    uint4 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = reinterpret_cast<const uint4 *>(q + (size_t)qv * D)[ks * 4 + grp];
+    // Rows of the workgroup: the windows of its first to last vector, and row 0 in a tile of
+    // its own when no window reaches it.
+    const int i_first = pos_of(part * 64);
+    const uint32_t last = part * 64 + 63 < a.nvec ? part * 64 + 63 : a.nvec - 1;
+    const int s_lo = i_first - a.W + 1 > 0 ? i_first - a.W + 1 : 0, s_hi = pos_of(last);
+    const int anchor_tile = s_lo > 0 ? 1 : 0;
+    const int ntiles = anchor_tile + (s_hi - s_lo + kWinTile) / kWinTile;
+    const __bf16 *kb = k + (size_t)bk * (size_t)a.n * D, *vb = v + (size_t)bk * (size_t)a.n * D;
+    const int nlast = (int)a.n - 1;
+
+    float m = -INFINITY, lsum = 0.f;
+    f32x4_t o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    win_u32x4 pk[NCH], pv[NCH];
+    // Tile t: rows base(t) + 0..63 (row 0 alone for the anchor tile).
+    auto tile_base = [&](int t) { return t < anchor_tile ? 0 : s_lo + (t - anchor_tile) * kWinTile; };
+    if (ntiles > 0) {
+        win_tile_load<D>(pk, pv, kb, vb, tile_base(0), nlast, tid);
+        win_tile_store<D>(pk, pv, kt, vt, tid);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) win_tile_load<D>(pk, pv, kb, vb, tile_base(t + 1), nlast, tid);
+        const int base = tile_base(t);
+        const bool is_anchor = t < anchor_tile;
+        // Scores of the tile's 64 rows for this wavefront's 16 queries.
+        f32x4_t sc[4];
+#pragma unroll
+        for (int kbk = 0; kbk < 4; ++kbk) {
+            bf16x8_t af[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                af[ks] = __builtin_bit_cast(bf16x8_t, kt[chunk_at<D>(kbk * 16 + col, ks * 4 + grp)]);
+            sc[kbk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                sc[kbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], __builtin_bit_cast(bf16x8_t, qf[ks]), sc[kbk], 0, 0, 0);
+        }
+        // Rows of C_i: row 0 (the anchor), and rows wlo..i (the window).
+        float mt = -INFINITY;
+        uint32_t inm = 0u;  // bit 4*kbk + r: row base + 16 kbk + 4 grp + r is in C_i
+#pragma unroll
+        for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = base + kbk * 16 + 4 * grp + r;
+                const bool in = valid && (is_anchor ? j == 0 : (j == 0 || (j >= wlo && j <= i)));
+                inm |= in ? 1u << (4 * kbk + r) : 0u;
+                mt = in ? fmaxf(mt, sc[kbk][r]) : mt;
+            }
+        {
+            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+            mt = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+            mt = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+        }
+        const float mn = fmaxf(m, mt);
+        if (mn != -INFINITY) {  // same for the four lanes of a query
+            const float alpha = m == -INFINITY ? 0.f : exp2f((m - mn) * a.scale_log2e);
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] *= alpha;
+            m = mn;
+        }
+        f32x4_t pw[4];
+#pragma unroll
+        for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pw[kbk][r] = (inm >> (4 * kbk + r)) & 1u ? exp2f((sc[kbk][r] - m) * a.scale_log2e) : 0.f;
+                lsum += pw[kbk][r];
+            }
+        // O^T += V^T P^T over two steps of 32 rows (blocks 0,1 and 2,3).
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            bf16x8_t pb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pb[r] = (__bf16)pw[2 * h2][r];
+                pb[4 + r] = (__bf16)pw[2 * h2 + 1][r];
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const uint16_t *vr = vt + (db * 16 + col) * kVtStride + h2 * 32 + 4 * grp;
+                const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
+                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[db], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+        if (t + 1 < ntiles) win_tile_store<D>(pk, pv, kt, vt, tid);
+        __syncthreads();
+    }
+    lsum = __uint_as_float(quad_sum_f32_bits(__float_as_uint(lsum)));
+    if (valid) {
+        float *out = a.win + (size_t)qv * (D + 2);
+        if (grp == 0) { out[0] = m; out[1] = lsum; }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[2 + db * 16 + 4 * grp + r] = o[db][r];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
@@ -451,6 +652,22 @@ hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void
         if (cand) hipLaunchKernelGGL((mfma_select_kernel<64, kMfmaQBCand, true>), grid, block, 0, s, qt, kt, a);
         else hipLaunchKernelGGL((mfma_select_kernel<64, kMfmaQBBound, false>), grid, block, 0, s, qt, kt, a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_window(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
+                              hipStream_t s) {
+    WinArgs a;
+    a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g; a.W = pl.W;
+    a.nvec = (uint32_t)(pl.g * pl.nq);
+    a.wg_per_unit = (a.nvec + 63) / 64;
+    a.nwg = (uint32_t)(pl.B * pl.Hkv) * a.wg_per_unit;
+    a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
+    a.win = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.win_offset);
+    const __bf16 *qt = static_cast<const __bf16 *>(q), *kt = static_cast<const __bf16 *>(k),
+                 *vt = static_cast<const __bf16 *>(v);
+    if (pl.d == 128) hipLaunchKernelGGL((mfma_window_kernel<128>), dim3(a.nwg), dim3(256), 0, s, qt, kt, vt, a);
+    else hipLaunchKernelGGL((mfma_window_kernel<64>), dim3(a.nwg), dim3(256), 0, s, qt, kt, vt, a);
     return hipGetLastError();
 }
 
