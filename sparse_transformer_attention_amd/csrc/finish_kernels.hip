@@ -244,17 +244,7 @@ constexpr int kTileCap = 1024;
 constexpr int kOvfCap = 64;
 constexpr int kRankSelectMax = 256;  // candidates selected by rank counting (else radix select)
 
-//
-// With ATT, when the rank select applies, k' <= kTopRowsMax and the candidates' V rows fit the
-// registers, the softmax partial of the selected rows is computed here as well: their V rows are
-// requested as soon as the candidates are known (they arrive while the selection runs) and
-// their scores are the ones in their ranking keys (no K row is read again). The rows are then
-// staged in LDS by key rank (vrows, scs), so that the sum runs in an order that does not depend
-// on the gather's. It goes to partial NT/64 + wavefront of *part, and *top_done is set.
-constexpr int kTopRowsU = 4;     // V rows per lane held for the selected-row partial
-constexpr int kTopRowsMax = 128;  // selected rows of that partial, staged in LDS by key rank
-
-template <int NT, typename T, int D, bool ATT, int NP, typename Overlap, typename Rescore>
+template <int NT, typename Overlap, typename Rescore>
 __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
                                              const uint2 *__restrict__ rest,
                                              const uint32_t *__restrict__ bm, int G, int nblk,
@@ -262,9 +252,7 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
                                              uint64_t *sel, uint64_t *gathered, int32_t *tiles,
                                              int32_t *ovf, uint32_t *scratch,
                                              SelectShared<NT> &sh, Overlap overlap,
-                                             Rescore rescore, const T *__restrict__ vb,
-                                             float scale_log2e, SoftmaxPartials<D, NP> *part,
-                                             uint4 *vrows, float *scs, bool *top_done) {
+                                             Rescore rescore) {
     constexpr int E = 8;   // block maxima per lane: at most 512 (merged in groups beyond)
     constexpr int TU = 8;  // tile maxima in flight per thread
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -381,27 +369,10 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
     }
     __syncthreads();
     if (n <= kRankSelectMax && n >= kp) {
-        // V rows of the candidates (row slot vslot of wavefront w takes candidates
-        // w*RPW + vslot + u*RPR), requested before the selection.
-        using AS = AttendShape<D, T>;
-        constexpr int NW = NT / 64, RPR = NW * AS::RPW;
-        const bool att = ATT && n <= kTopRowsU * RPR && kp <= kTopRowsMax;
-        int *rank_of = reinterpret_cast<int *>(&sh.hist[0][0]);  // key rank of each candidate
-        const int vslot = lane / AS::LPR, vcs = lane % AS::LPR;
-        uint4 vv[kTopRowsU];
-#pragma unroll
-        for (int u = 0; u < kTopRowsU; ++u) {
-            vv[u] = make_uint4(0, 0, 0, 0);
-            if (att && u * RPR < n) {
-                int cc = wave * AS::RPW + vslot + u * RPR;
-                cc = cc < n ? cc : n - 1;
-                vv[u] = reinterpret_cast<const uint4 *>(vb + (size_t)(uint32_t)rank_key_pos(gathered[cc]) * D)[vcs];
-            }
-        }
         // Few candidates: a key is selected when fewer than kp keys beat it; the selected
         // positions are then placed by their rank among the selected ones (ascending). S lanes
         // per candidate (S*n <= NT, S <= 16): lane s compares against keys s, s+S, ..., and the S
-        // counts are summed. (Barriers for LDS only: the V rows stay in flight.)
+        // counts are summed.
         int lg = 4;
         while (lg > 0 && (n << lg) > NT) --lg;
         const int S = 1 << lg, c = tid >> lg, sl = tid & (S - 1);
@@ -415,10 +386,7 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
         for (int off = 1; off < S; off <<= 1) above += __shfl_xor(above, off);
         const bool chosen = mine && above < kp;
         // Selected keys (0 = not) in the tail of gathered[], clear of [0, n).
-        if (mine && sl == 0) {
-            gathered[kGather - 1 - c] = chosen ? x : 0ull;
-            rank_of[c] = above;
-        }
+        if (mine && sl == 0) gathered[kGather - 1 - c] = chosen ? x : 0ull;
         lds_barrier();
         const int32_t pos = rank_key_pos(x);
         int rank = 0;
@@ -431,39 +399,6 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
         }
         for (int off = 1; off < S; off <<= 1) rank += __shfl_xor(rank, off);
         if (chosen && sl == 0) js[rank] = pos;
-        if constexpr (ATT) {
-            if (att) {
-                // Selected rows to LDS at their key rank (< k'), with their scores.
-#pragma unroll
-                for (int u = 0; u < kTopRowsU; ++u) {
-                    const int cv = wave * AS::RPW + vslot + u * RPR;
-                    const uint64_t y = cv < n ? gathered[kGather - 1 - cv] : 0ull;
-                    if (y != 0ull) {
-                        const int r = rank_of[cv];
-                        vrows[r * AS::LPR + vcs] = vv[u];
-                        if (vcs == 0) scs[r] = key_score((uint32_t)(y >> 32));
-                    }
-                }
-                lds_barrier();
-                // Rank r goes to row slot r % RPR of the workgroup, in rank order per slot.
-                const int ur = (kp + RPR - 1) / RPR;
-                SlotState<D, T> st;
-                for (int u = 0; u < ur; ++u) {
-                    const int r = wave * AS::RPW + vslot + u * RPR;
-                    if (r < kp) st.m = fmaxf(st.m, scs[r]);
-                }
-                for (int u = 0; u < ur; ++u) {
-                    const int r = wave * AS::RPW + vslot + u * RPR;
-                    if (r < kp) {
-                        const float w = exp2f((scs[r] - st.m) * scale_log2e);
-                        st.l += w;
-                        accumulate16(st.acc, vrows[r * AS::LPR + vcs], w, T());
-                    }
-                }
-                store_wave_partial<D, T>(st, scale_log2e, *part, NW + wave);
-                *top_done = true;
-            }
-        }
         lds_barrier();
         return;
     }
@@ -549,10 +484,6 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     // Softmax partials: [0, NW) the anchor and window rows (wavefronts 1..NW-1 when wavefront 0
     // takes the bound), [NW, 2NW) the top-k rows.
     __shared__ SoftmaxPartials<D, ATTEND ? 2 * NW : 1> part;
-    // Selected rows of the top-k partial, by key rank (1024-thread tile-summary kernel only).
-    constexpr bool kStage = ATTEND && TILES && NT == 1024;
-    __shared__ uint4 top_rows[kStage ? kTopRowsMax * AttendShape<D, T>::LPR : 1];
-    __shared__ float top_scores[kStage ? kTopRowsMax : 1];
     int32_t *js = fsm;
     uint64_t *sel = reinterpret_cast<uint64_t *>(fsm + 2 * a.cap);
 
@@ -573,7 +504,6 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     // js layout: [0 if the anchor is separate][top-k' ascending][window ascending]
     const int base = wlo > 0 ? 1 : 0;
     const int wcount = (int)(i - wlo + 1);
-    bool top_done = false;  // partial of the top-k rows computed during the selection
 
     // Attend over the anchor and the window: the rows are known from the start, so they are
     // processed by the wavefronts that do not take the bound (all of them when there is no
@@ -610,14 +540,13 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
             const int64_t u = ((int64_t)b * a.Hkv + kvh) * a.groups + gq;
             const int t = (int)(idx - gq * (uint32_t)a.G);
             const size_t qt = ((size_t)u * a.G + t) * (size_t)(a.rstride >> a.tile_shift);
-            select_tiles<NT, T, D, kStage>(a.best1 + qt, a.rest + qt,
+            select_tiles<NT>(a.best1 + qt, a.rest + qt,
                              a.bmax + (size_t)u * a.nblk * a.G + t, a.G, a.nblk, a.tile_shift,
                              (int)rl, kp, js + base, sel, gathered, tile_idx, ovf_idx,
                              a.scratch + qv * a.rstride, ssh, overlap,
                              [&](int ntl, auto tile_at, auto emit) {
                                  rescore_tiles<T, D, NT>(q, kb, a, b, kvh, gq, t, (int)rl, ntl, tile_at, emit);
-                             },
-                             vb, a.scale_log2e, &part, top_rows, top_scores, &top_done);
+                             });
         } else {
             select_segments<NT>(a.cnt + qv * a.wpu, a.lists + qv * a.wpu * a.seg, a.wpu, a.seg,
                                 kp, js + base, sel, gathered, ssh, overlap);
@@ -632,7 +561,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     int32_t *row = out_idx + qv * a.cap;
     for (int t = tid; t < a.cap; t += NT) row[t] = t < count ? js[t] : -1;
     if constexpr (ATTEND) {
-        if (kp > 0 && !top_done) {
+        if (kp > 0) {
             const int32_t *top = js + base;
             auto row_at = [&](int c) -> size_t { return (size_t)(uint32_t)top[c]; };
             wave_partial<D, T, kTopU<NT>>(qs, kb, vb, row_at, kp, wave, NW, a.scale_log2e, part, NW + wave);
@@ -727,12 +656,9 @@ hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const 
     const bool tiles = pl.stream && ws != nullptr;
     const dim3 grid((unsigned)pl.nqv);
     const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v);
-    // Static LDS of the 1024-thread kernel (staged top-k rows included) plus the dynamic part
-    // within the 160 KiB of a CU.
     const size_t fixed1024 = kGather * sizeof(uint64_t) + sizeof(SelectShared<1024>) +
-                             (kTileCap + kOvfCap) * sizeof(int32_t) + sizeof(SoftmaxPartials<D, 32>) +
-                             kTopRowsMax * (AttendShape<D, T>::LPR * sizeof(uint4) + sizeof(float));
-    const bool wide = pl.nqv < kWideBelow && shmem + fixed1024 <= 160 * 1024;
+                             (kTileCap + kOvfCap) * sizeof(int32_t) + sizeof(SoftmaxPartials<D, 32>);
+    const bool wide = pl.nqv < kWideBelow && shmem + fixed1024 <= 64 * 1024;
 #define CA_LAUNCH_FIN(NT, TILES)                                                                  \
     hipLaunchKernelGGL((finish_kernel<T, D, NT, ATTEND, TILES>), grid, dim3(NT), shmem, s, qt, kt, vt, \
                        out_idx, out, a)
