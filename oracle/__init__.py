@@ -21,7 +21,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "condensate_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
-N_DIAG = 5
+N_DIAG = 8
 
 
 class Problem(ctypes.Structure):
@@ -51,9 +51,7 @@ def lib():
     if _lib is None:
         path = os.environ.get("CONDENSATE_ORACLE_LIB")   # mutation tests load a planted variant
         if path is None:
-            path = _LIB_PATH
-            if not os.path.exists(path):
-                build()
+            path = build()   # (re)compiled when missing or older than its source
         L = ctypes.CDLL(path)
         P = ctypes.POINTER(Problem)
         vp = ctypes.c_void_p
@@ -98,7 +96,8 @@ def _check(rc: int, what: str):
 
 def condensate(q, k, v, W: int, topk: int, threads: int = 0):
     """Full method. Returns (idx int32 [B][Hq][nq][1+W+topk], out float64 [B][Hq][nq][d],
-    diag float64 [B][Hq][nq][5] = tau, max|s|, eps, |C|, k')."""
+    diag float64 [B][Hq][nq][8] = tau, max|s|, eps, |C|, k', and the full-softmax mass of
+    position 0, of the window without 0, of the top-k positions."""
     q, k, v = _prep(q), _prep(k), _prep(v)
     p = problem(q, k, W, topk, threads)
     B, Hq, nq, d = q.shape

@@ -19,6 +19,8 @@
  *           o = sum_C p_j v_j / sum_C p_j, summed in ascending j            (sec. 2.3 Theorem 1 Attention_C; 3.2.4 Theorem 4)
  *   full    the same step 5 with C = {0..i}: plain causal attention         (sec. 1.1 eq.)
  *   eps     excluded mass: full-softmax weight of positions outside C       (sec. 3.2.2)
+ *   masses  full-softmax weight of the anchor, the window (without 0) and
+ *           the top-k positions; with eps they sum to 1                     (sec. 2.2.1-2.2.3, 3.2.2)
  *
  * Readings where the pages are silent or loose (each also listed with the design notes):
  *   - top-k ranks only R, the positions outside the anchor and the window (the section 4.2.1
@@ -159,7 +161,8 @@ static void load_query(const oracle_problem *p, const void *q, const query_loc *
     for (int64_t t = 0; t < p->d; ++t) qrow[t] = load_elem(q, p->dtype, L->q_off + t);
 }
 
-/* Steps 1-6 for one query. diag gets {tau, max_j |s_j|, eps, |C|, k'}. */
+/* Steps 1-6 for one query. diag gets {tau, max_j |s_j|, eps, |C|, k', and the full-softmax
+ * mass of position 0, of the window positions other than 0, and of the top-k positions}. */
 static void condensate_query(const oracle_problem *p, const void *q, const void *k, const void *v,
                              int64_t flat, scratch_bufs *w, int32_t *idx_row, double *o, double *diag)
 {
@@ -207,12 +210,21 @@ static void condensate_query(const oracle_problem *p, const void *q, const void 
         z_all += e;
         if (!w->member[j]) z_out += e;
     }
+    /* The parts of C: the anchor (sec. 2.2.1, its share of the mass), the window without
+     * position 0 (sec. 2.2.2), and the top-k positions (sec. 2.2.3), which lie in R. */
+    const double z_anchor = exp(w->s[0] - mall);
+    double z_window = 0.0, z_topk = 0.0;
+    for (int64_t j = wlo > 1 ? wlo : 1; j <= i; ++j) z_window += exp(w->s[j] - mall);
+    for (int64_t t = 0; t < kp; ++t) z_topk += exp(w->s[w->cand[t].j] - mall);
     if (diag) {
         diag[0] = tau;
         diag[1] = mabs;
         diag[2] = z_out / z_all;
         diag[3] = (double)count;
         diag[4] = (double)kp;
+        diag[5] = z_anchor / z_all;
+        diag[6] = z_window / z_all;
+        diag[7] = z_topk / z_all;
     }
 }
 
@@ -225,11 +237,12 @@ static void set_threads(const oracle_problem *p)
 #endif
 }
 
-#define N_DIAG 5
+#define N_DIAG 8
 
 /* The whole method for every query of the problem.
  * out_idx: [batch][heads][nq][1+W+topk] int32; out: [batch][heads][nq][d] float64;
- * diag (may be NULL): [batch][heads][nq][5] float64 = {tau, max|s|, eps, |C|, k'}. */
+ * diag (may be NULL): [batch][heads][nq][8] float64 = {tau, max|s|, eps, |C|, k', mass of
+ * position 0, of the window without 0, of the top-k}. */
 int oracle_condensate(const oracle_problem *p, const void *q, const void *k, const void *v,
                       int32_t *out_idx, double *out, double *diag)
 {

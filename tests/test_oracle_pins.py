@@ -309,3 +309,45 @@ def test_threads_do_not_change_results():
     b = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk, threads=4)
     for u, v in zip(a, b):
         assert np.array_equal(u, v, equal_nan=True)
+
+
+@pytest.mark.parametrize("case", [
+    dict(n=300, nq=5, W=32, topk=16),       # all three parts present
+    dict(n=40, nq=40, W=8, topk=4),         # prefill: early rows with window over 0, |R| < k
+    dict(n=300, nq=2, W=16, topk=0),        # k = 0: no top-k mass
+    dict(n=50, nq=3, W=64, topk=8),         # the window covers every position
+])
+def test_mass_parts_partition_one(case):
+    """The full-softmax masses of the anchor, of the window without position 0, of the top-k
+    positions and outside C (eps) are those of disjoint sets covering 0..i: they sum to 1. With
+    k = 0 or an empty R the top-k mass is 0; with C = {0..i} eps is 0 as well."""
+    w, x = make(Hq=2, Hkv=1, d=16, **case)
+    _, _, diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    eps, anchor, window, topk = diag[..., 2], diag[..., 5], diag[..., 6], diag[..., 7]
+    assert np.allclose(eps + anchor + window + topk, 1.0, rtol=0, atol=1e-12)
+    assert np.all(anchor > 0) and np.all(window >= 0) and np.all(topk >= 0)
+    kp = diag[..., 4]
+    assert np.all(topk[kp == 0] == 0.0)
+    full = diag[..., 3] == (w.n - w.nq + np.arange(w.nq) + 1)[None, None, :]
+    assert np.all(eps[full] == 0.0)
+
+
+def test_mass_parts_hand_computed():
+    """Scores built so that exp(s_j) = 1, 2, 8, 4, 1, 2 at positions 0..5 (q = e_0, k_j =
+    sqrt(d) ln(e^{s_j}) e_0). For the query at 5 with W = 2, k = 1: window {4, 5}, R = {1, 2, 3},
+    top-1 = position 2; Z = 18, so anchor 1/18, window 3/18, top-k 8/18, eps (positions 1, 3)
+    6/18."""
+    d, n = 64, 6
+    ez = [1.0, 2.0, 8.0, 4.0, 1.0, 2.0]
+    q = torch.zeros(1, 1, 1, d, dtype=torch.float64)
+    q[..., 0] = 1.0
+    k = torch.zeros(1, 1, n, d, dtype=torch.float64)
+    for j, e in enumerate(ez):
+        k[0, 0, j, 0] = math.sqrt(d) * math.log(e)
+    v = torch.zeros(1, 1, n, d, dtype=torch.float64)
+    idx, _, diag = oracle.condensate(q.float(), k.float(), v.float(), 2, 1)
+    assert sorted(j for j in idx[0, 0, 0].tolist() if j >= 0) == [0, 2, 4, 5]
+    got = diag[0, 0, 0]
+    expect = {2: 6 / 18, 5: 1 / 18, 6: 3 / 18, 7: 8 / 18}
+    for col, val in expect.items():
+        assert abs(got[col] - val) < 1e-6, (col, got[col], val)
