@@ -78,6 +78,8 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mass", action="store_true",
+                    help="time the call with the mass diagnostic (decode path only)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (counter calibration)")
     args = ap.parse_args()
@@ -118,9 +120,14 @@ def main():
     out = torch.empty((w.batch, w.heads, w.nq, w.d), dtype=torch.float32, device="cuda")
     idx = torch.empty((w.batch, w.heads, w.nq, w.set_cap), dtype=torch.int32, device="cuda")
 
+    mass = torch.empty((w.batch, w.heads, w.nq, 4), dtype=torch.float32, device="cuda") if args.mass else None
+
     def step(s):
         kk, vv = sets[s % rotate]
-        ca.condensate_attention_ex(p, q, kk, vv, out, idx, ws)
+        if args.mass:
+            ca.condensate_attention_mass_ex(p, q, kk, vv, out, idx, mass, ws)
+        else:
+            ca.condensate_attention_ex(p, q, kk, vv, out, idx, ws)
 
     for s in range(args.warmup):
         step(s)
@@ -220,7 +227,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "kv_heads": w.kv_heads,
                    "d": w.d, "n": w.n, "nq": w.nq, "W": w.W, "topk": w.topk, "accumulate": "f32",
-                   "chunk": args.chunk or "auto", "kv_sets_rotated": rotate, "seed": seed},
+                   "chunk": args.chunk or "auto", "kv_sets_rotated": rotate, "seed": seed,
+                   "mass_diagnostic": bool(args.mass)},
         "hbm_gbps": step_bytes / (ms_per_step / 1e3) / 1e9,
         "step_algorithmic_bytes": step_bytes,
         "gpu_ms_per_step": gpu_ms / args.steps,

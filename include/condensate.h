@@ -95,6 +95,19 @@ int ca_condensate_attention_ex(const ca_params *p, const void *q, const void *k,
                                float *out, int32_t *out_idx, void *ws, size_t ws_bytes,
                                void *stream);
 
+/* The full method plus the mass diagnostic of the pages (metaphor-xennon blog: section 3.2.2,
+ * the weight the full causal softmax puts outside C_i; sections 2.2.1-2.2.3, the parts of C_i):
+ * as ca_condensate_attention_ex, and mass[batch][heads][nq][4] float32 (device pointer, owned
+ * by the caller) = {eps_i, anchor, window, top-k}: the full-softmax weight of the positions
+ * outside C_i, of position 0, of the window positions other than 0, and of the top-k positions
+ * (the four sum to 1; fp32 sums, so eps is resolved to about 1e-6 of the candidates' mass). The
+ * candidates' part of the full normaliser is summed inside the score pass. Only for problems
+ * that take the streaming decode path (chunk = 0, some query with candidates, the key buffer
+ * within its budget); others return CA_ERR_UNSUPPORTED before any HIP call. Same workspace. */
+int ca_condensate_attention_mass_ex(const ca_params *p, const void *q, const void *k,
+                                    const void *v, float *out, int32_t *out_idx, float *mass,
+                                    void *ws, size_t ws_bytes, void *stream);
+
 /* Stage 1 (identify_condensate, section 5.2.2): scores every causal key and writes C_i to
  * out_idx only. Same workspace as the full method. */
 int ca_condensate_select(const ca_params *p, const void *q, const void *k, int32_t *out_idx,
@@ -116,7 +129,8 @@ int ca_attention_on_subset(const ca_params *p, const void *q, const void *k, con
  * kernel name (launches, summed milliseconds) into out[0..capacity), setting *count to the
  * number of kernels seen. Not meant to be used from several threads at once. */
 typedef struct {
-    const char *kernel;  /* static name: "score_select", "finish" or "attend" */
+    const char *kernel;  /* static name: "score_keys", "score_select", "mfma_bound", "mfma_cand",
+                            "mfma_window", "finish" or "attend" */
     int64_t launches;
     double total_ms;
 } ca_kernel_time;

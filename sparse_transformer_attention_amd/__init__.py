@@ -29,8 +29,8 @@ CA_F32, CA_BF16 = 0, 1
 CA_MAX_SET = 4096
 
 EXPORTED = ("ca_condensate_attention", "ca_workspace_size", "ca_condensate_attention_ex",
-            "ca_condensate_select", "ca_attention_on_subset", "ca_profile_start",
-            "ca_profile_stop", "ca_status_string", "ca_last_error")
+            "ca_condensate_attention_mass_ex", "ca_condensate_select", "ca_attention_on_subset",
+            "ca_profile_start", "ca_profile_stop", "ca_status_string", "ca_last_error")
 
 
 class Params(ctypes.Structure):
@@ -71,6 +71,7 @@ def load() -> ctypes.CDLL:
                                               ctypes.c_int32, vp, vp]
         L.ca_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         L.ca_condensate_attention_ex.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.ca_condensate_attention_mass_ex.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.ca_condensate_select.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.ca_attention_on_subset.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.ca_profile_start.argtypes = [ctypes.c_int32]
@@ -81,8 +82,8 @@ def load() -> ctypes.CDLL:
         L.ca_last_error.argtypes = []
         L.ca_last_error.restype = ctypes.c_char_p
         for f in (L.ca_condensate_attention, L.ca_workspace_size, L.ca_condensate_attention_ex,
-                  L.ca_condensate_select, L.ca_attention_on_subset, L.ca_profile_start,
-                  L.ca_profile_stop):
+                  L.ca_condensate_attention_mass_ex, L.ca_condensate_select,
+                  L.ca_attention_on_subset, L.ca_profile_start, L.ca_profile_stop):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -158,6 +159,18 @@ def condensate_attention_ex(p: Params, q, k, v, out, out_idx, ws, stream=None):
         _dev_ptr(ws, "ws"), ws_bytes, _stream_ptr(stream)), "ca_condensate_attention_ex")
 
 
+def condensate_attention_mass_ex(p: Params, q, k, v, out, out_idx, mass, ws, stream=None):
+    """ca_condensate_attention_mass_ex: also mass float32 [B][Hq][nq][4] = (excluded mass,
+    anchor, window without position 0, top-k) of the full causal softmax."""
+    dt = q.dtype
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(load().ca_condensate_attention_mass_ex(
+        ctypes.byref(p), _dev_ptr(q, "q", dt), _dev_ptr(k, "k", dt), _dev_ptr(v, "v", dt),
+        _dev_ptr(out, "out", torch.float32), _dev_ptr(out_idx, "out_idx", torch.int32),
+        _dev_ptr(mass, "mass", torch.float32), _dev_ptr(ws, "ws"), ws_bytes, _stream_ptr(stream)),
+        "ca_condensate_attention_mass_ex")
+
+
 def condensate_select(p: Params, q, k, out_idx, ws, stream=None):
     dt = q.dtype
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
@@ -191,6 +204,20 @@ def condensate(q, k, v, W: int, topk: int, chunk: int = 0, ws=None, stream=None)
         ws = alloc_workspace(p, q.device)
     condensate_attention_ex(p, q, k, v, out, out_idx, ws, stream)
     return out, out_idx
+
+
+def condensate_mass(q, k, v, W: int, topk: int, ws=None, stream=None):
+    """As condensate(), with the mass diagnostic: returns (out, out_idx, mass float32
+    [B][Hq][nq][4] = excluded mass, anchor, window without position 0, top-k)."""
+    p = params_for(q, k, W, topk, 0)
+    B, Hq, nq, d = q.shape
+    out = torch.empty((B, Hq, nq, d), dtype=torch.float32, device=q.device)
+    out_idx = torch.empty((B, Hq, nq, 1 + W + topk), dtype=torch.int32, device=q.device)
+    mass = torch.empty((B, Hq, nq, 4), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = alloc_workspace(p, q.device)
+    condensate_attention_mass_ex(p, q, k, v, out, out_idx, mass, ws, stream)
+    return out, out_idx, mass
 
 
 def profile_start(reserve_launches: int = 0):

@@ -51,6 +51,7 @@ struct Plan {
     int nblk;
     int tile_rows;
     size_t best1_offset, rest_offset, bmax_offset, scratch_offset;
+    size_t zsum_offset;   // mass diagnostic: [units][nblk][G] (largest score, sum) float pairs
 };
 
 // Launchers (enqueue only; return the hipError_t of the last launch).
@@ -58,13 +59,17 @@ hipError_t launch_score_select(const Plan &pl, const void *q, const void *k, voi
                                hipStream_t s);
 // Merge + set assembly (+ restricted softmax times V when out != nullptr), one workgroup per
 // query vector.
+// mass != nullptr (decode path only): also [nqv][4] = excluded mass, anchor, window, top-k.
 hipError_t launch_finish(const Plan &pl, const void *ws, const void *q, const void *k,
-                         const void *v, int32_t *out_idx, float *out, hipStream_t s);
+                         const void *v, int32_t *out_idx, float *out, hipStream_t s,
+                         float *mass = nullptr);
 // Restricted softmax times V on caller-supplied index sets.
 hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k, const void *v,
                                     const int32_t *idx, float *out, hipStream_t s);
 size_t topk_lds_bytes(const Plan &pl);
-hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s);
+// mass: also the per-block sums of the mass diagnostic (zsum_offset).
+hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
+                             bool mass = false);
 // Query blocks of 16 per wavefront of the two MFMA passes (64 * QB query vectors per workgroup).
 constexpr int kMfmaQBBound = 2;
 constexpr int kMfmaQBCand = 4;

@@ -151,6 +151,7 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     P.mfma = false;
     P.seg = 1;
     P.win_offset = 0;
+    P.zsum_offset = 0;
     // Many bf16 query vectors per KV head: the MFMA passes (bound, then candidate lists in the
     // segment layout of the chunked path: 4 segments of kMfmaSeg keys per query).
     if (P.candidates && p->chunk == 0 && P.dtype == CA_BF16 && P.topk <= kMfmaMaxTopk &&
@@ -190,7 +191,8 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
             P.rest_offset = P.best1_offset + up(ntiles * sizeof(uint32_t));
             P.bmax_offset = P.rest_offset + up(ntiles * 2 * sizeof(uint32_t));
             P.scratch_offset = P.bmax_offset + up((size_t)P.units * P.nblk * P.G * sizeof(uint32_t));
-            P.ws_bytes = P.scratch_offset + (size_t)P.nqv * (size_t)P.rstride * sizeof(uint32_t);
+            P.zsum_offset = up(P.scratch_offset + (size_t)P.nqv * (size_t)P.rstride * sizeof(uint32_t));
+            P.ws_bytes = P.zsum_offset + (size_t)P.units * P.nblk * P.G * 2 * sizeof(float);
             return CA_OK;
         }
     }
@@ -226,7 +228,7 @@ int check_ws(const ca::Plan &pl, void *ws, size_t ws_bytes) {
 // Scores and candidate lists, then the merge and set assembly into out_idx; with out != nullptr
 // the restricted softmax times V runs in the same (finish) kernel.
 int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, int32_t *out_idx,
-             float *out, void *ws, hipStream_t s) {
+             float *out, void *ws, hipStream_t s, float *mass = nullptr) {
     hipError_t e;
     if (pl.candidates && pl.mfma) {
         ProfScope pb(K_BOUND, s);
@@ -245,7 +247,7 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
         }
     } else if (pl.candidates && pl.stream) {
         ProfScope ps(K_KEYS, s);
-        e = ca::launch_score_keys(pl, q, k, ws, s);
+        e = ca::launch_score_keys(pl, q, k, ws, s, mass != nullptr);
         ps.done();
         if (e != hipSuccess) return hip_fail(e, "score_keys launch");
     } else if (pl.candidates) {
@@ -255,7 +257,7 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
         if (e != hipSuccess) return hip_fail(e, "score_topk launch");
     }
     ProfScope pf(K_FINISH, s);
-    e = ca::launch_finish(pl, pl.candidates ? ws : nullptr, q, k, v, out_idx, out, s);
+    e = ca::launch_finish(pl, pl.candidates ? ws : nullptr, q, k, v, out_idx, out, s, mass);
     pf.done();
     if (e != hipSuccess) return hip_fail(e, "finish launch");
     return CA_OK;
@@ -325,6 +327,21 @@ int ca_condensate_attention_ex(const ca_params *p, const void *q, const void *k,
         return fail(CA_ERR_INVALID_ARG, "q, k, v, out and out_idx must be non-NULL");
     if ((rc = check_ws(pl, ws, ws_bytes)) != CA_OK) return rc;
     return run_path(pl, q, k, v, out_idx, out, ws, static_cast<hipStream_t>(stream));
+}
+
+int ca_condensate_attention_mass_ex(const ca_params *p, const void *q, const void *k,
+                                    const void *v, float *out, int32_t *out_idx, float *mass,
+                                    void *ws, size_t ws_bytes, void *stream) {
+    ca::Plan pl;
+    int rc = make_plan(p, &pl);
+    if (rc != CA_OK) return rc;
+    if (!(pl.candidates && pl.stream))
+        return fail(CA_ERR_UNSUPPORTED, "the mass diagnostic needs the streaming decode path "
+                                        "(chunk 0, some query with candidates, key buffer within budget)");
+    if (!q || !k || !v || !out || !out_idx || !mass)
+        return fail(CA_ERR_INVALID_ARG, "q, k, v, out, out_idx and mass must be non-NULL");
+    if ((rc = check_ws(pl, ws, ws_bytes)) != CA_OK) return rc;
+    return run_path(pl, q, k, v, out_idx, out, ws, static_cast<hipStream_t>(stream), mass);
 }
 
 int ca_condensate_attention(const void *q, const void *k, const void *v, int64_t n, int32_t d,

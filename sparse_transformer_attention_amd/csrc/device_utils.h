@@ -112,6 +112,11 @@ __device__ __forceinline__ uint32_t score_key(float s) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The score a key of score_key stands for (any key >= 0x00800000).
+__device__ __forceinline__ float key_score(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 // Workgroup barrier for LDS traffic: waits for this wavefront's LDS operations, not for its
 // vector memory loads in flight (__syncthreads waits for those as well).
 __device__ __forceinline__ void lds_barrier() {

@@ -33,6 +33,10 @@ struct FinishArgs {
     const uint32_t *bmax;     // [units][nblk][G]
     uint32_t *scratch;        // [nqv][rstride]
     const float *win;         // [nqv][D + 2] anchor-and-window partials (MFMA path), or null
+    // Mass diagnostic (tile-summary path; null: off): per-block sums of score_keys and the
+    // output [nqv][4] = excluded mass, anchor, window without position 0, top-k.
+    const float2 *zsum;
+    float *mass;
 };
 
 constexpr int kGather = 1024;  // candidates gathered into LDS for the one-wavefront select
@@ -504,6 +508,12 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     // js layout: [0 if the anchor is separate][top-k' ascending][window ascending]
     const int base = wlo > 0 ? 1 : 0;
     const int wcount = (int)(i - wlo + 1);
+    // Tile-summary path: unit and slot of this query vector (vector index r*g + (h - kvh*g) of
+    // its KV head).
+    const uint32_t idx = (uint32_t)r * g32 + (h - kvh * g32);
+    const uint32_t gq = TILES ? idx / (uint32_t)a.G : 0u;
+    const int64_t u = ((int64_t)b * a.Hkv + kvh) * a.groups + gq;
+    const int t = (int)(idx - gq * (uint32_t)(TILES ? a.G : 0));
 
     // Attend over the anchor and the window: the rows are known from the start, so they are
     // processed by the wavefronts that do not take the bound (all of them when there is no
@@ -534,11 +544,6 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     if (kp > 0) {
         auto overlap = [&]() { window_part(wave - 1, NW - 1); };
         if constexpr (TILES) {
-            // Unit and slot of this query vector: vector index r*g + (h - kvh*g) of its KV head.
-            const uint32_t idx = (uint32_t)r * g32 + (h - kvh * g32);
-            const uint32_t gq = idx / (uint32_t)a.G;
-            const int64_t u = ((int64_t)b * a.Hkv + kvh) * a.groups + gq;
-            const int t = (int)(idx - gq * (uint32_t)a.G);
             const size_t qt = ((size_t)u * a.G + t) * (size_t)(a.rstride >> a.tile_shift);
             select_tiles<NT>(a.best1 + qt, a.rest + qt,
                              a.bmax + (size_t)u * a.nblk * a.G + t, a.G, a.nblk, a.tile_shift,
@@ -571,6 +576,55 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
         // Window partials: NW-1 (from mfma_window), 1..NW-1 (wavefront 0 took the bound) or
         // 0..NW-1; top-k partials NW..2NW-1.
         const int p0 = pre_win ? NW - 1 : (kp > 0 ? 1 : 0);
+        if constexpr (TILES) {
+            if (a.mass && tid < 64) {
+                // Mass diagnostic (pages of "The Condensate Theorem", metaphor-xennon blog:
+                // section 3.2.2, the full-softmax mass outside C_i; sections 2.2.1-2.2.3, the
+                // parts of C_i). Sum over the candidate rows R_i from score_keys' per-block
+                // sums; the window part (with row 0) and the top-k part from the partials above;
+                // row 0's own weight from its score. All relative to one maximum M.
+                const float2 *zs = a.zsum + (size_t)u * a.nblk * a.G + t;
+                float ml = -INFINITY, ll = 0.f;  // this lane's blocks lane, lane + 64, ...
+                for (int blk = lane; blk < a.nblk; blk += 64) {
+                    const float2 z = zs[(size_t)blk * a.G];
+                    if (z.x != -INFINITY) {
+                        const float mn = fmaxf(ml, z.x);
+                        ll = (ml == -INFINITY ? 0.f : ll * exp2f((ml - mn) * a.scale_log2e)) +
+                             z.y * exp2f((z.x - mn) * a.scale_log2e);
+                        ml = mn;
+                    }
+                }
+                const float mr = wave_max_f32_dpp(ml);
+                const float lr = wave_sum_f32_dpp(ml == -INFINITY ? 0.f : ll * exp2f((ml - mr) * a.scale_log2e));
+                auto range = [&](int q0, int q1, float &mx, float &sm) {
+                    const int pc = lane < 2 * NW ? lane : 2 * NW - 1;
+                    const float pm = lane >= q0 && lane < q1 ? part.m[pc] : -INFINITY;
+                    const float pl = lane >= q0 && lane < q1 ? part.l[pc] : 0.f;
+                    mx = wave_max_f32_dpp(pm);
+                    sm = wave_sum_f32_dpp(pm == -INFINITY ? 0.f : pl * exp2f((pm - mx) * a.scale_log2e));
+                };
+                float mw, lw, mt = -INFINITY, lt = 0.f;
+                range(p0, NW, mw, lw);
+                if (kp > 0) range(NW, 2 * NW, mt, lt);
+                using S = AttendShape<D, T>;
+                const uint4 k0 = reinterpret_cast<const uint4 *>(kb)[lane % S::LPR];
+                const float s0 = row_sum<S::LPR>(dot16(k0, qs, 0.f, T()));
+                const float mg = fmaxf(mr, mw);
+                auto rel = [&](float mx, float sm) {
+                    return mx == -INFINITY ? 0.f : sm * exp2f((mx - mg) * a.scale_log2e);
+                };
+                const float zr = rel(mr, lr), zw = rel(mw, lw), zt = rel(mt, lt);
+                const float z0 = exp2f((s0 - mg) * a.scale_log2e);
+                const float zf = zr + zw;
+                if (lane == 0) {
+                    float *mo = a.mass + qv * 4;
+                    mo[0] = fmaxf(zr - zt, 0.f) / zf;
+                    mo[1] = z0 / zf;
+                    mo[2] = fmaxf(zw - z0, 0.f) / zf;
+                    mo[3] = zt / zf;
+                }
+            }
+        }
         merge_partials<NT, D>(part, p0, kp > 0 ? 2 * NW : NW, a.scale_log2e, out + qv * D);
     }
 }
@@ -642,6 +696,8 @@ FinishArgs finish_args(const Plan &pl, const void *ws) {
     a.scratch = sm ? reinterpret_cast<uint32_t *>(const_cast<char *>(wb) + pl.scratch_offset) : nullptr;
     a.nvec = (uint32_t)(pl.g * pl.nq);
     a.win = ws && pl.mfma ? reinterpret_cast<const float *>(wb + pl.win_offset) : nullptr;
+    a.zsum = sm ? reinterpret_cast<const float2 *>(wb + pl.zsum_offset) : nullptr;
+    a.mass = nullptr;
     return a;
 }
 
@@ -650,8 +706,9 @@ constexpr int64_t kWideBelow = 4096;
 
 template <typename T, int D, bool ATTEND>
 hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const void *k,
-                           const void *v, int32_t *out_idx, float *out, hipStream_t s) {
-    const FinishArgs a = finish_args(pl, ws);
+                           const void *v, int32_t *out_idx, float *out, hipStream_t s, float *mass) {
+    FinishArgs a = finish_args(pl, ws);
+    a.mass = mass;
     const size_t shmem = (size_t)pl.cap * (2 * sizeof(int32_t)) + (size_t)pl.topk * sizeof(uint64_t);
     const bool tiles = pl.stream && ws != nullptr;
     const dim3 grid((unsigned)pl.nqv);
@@ -689,10 +746,10 @@ hipError_t launch_attend_t(const Plan &pl, const void *q, const void *k, const v
 }  // namespace
 
 hipError_t launch_finish(const Plan &pl, const void *ws, const void *q, const void *k,
-                         const void *v, int32_t *out_idx, float *out, hipStream_t s) {
+                         const void *v, int32_t *out_idx, float *out, hipStream_t s, float *mass) {
     const bool attend = out != nullptr;
-#define CA_FIN(T, D) (attend ? launch_finish_t<T, D, true>(pl, ws, q, k, v, out_idx, out, s) \
-                             : launch_finish_t<T, D, false>(pl, ws, q, k, v, out_idx, out, s))
+#define CA_FIN(T, D) (attend ? launch_finish_t<T, D, true>(pl, ws, q, k, v, out_idx, out, s, mass) \
+                             : launch_finish_t<T, D, false>(pl, ws, q, k, v, out_idx, out, s, nullptr))
     if (pl.dtype == 1) return pl.d == 128 ? CA_FIN(__bf16, 128) : CA_FIN(__bf16, 64);
     return pl.d == 128 ? CA_FIN(float, 128) : CA_FIN(float, 64);
 #undef CA_FIN

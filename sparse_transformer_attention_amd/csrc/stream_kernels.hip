@@ -40,6 +40,10 @@ struct KeysArgs {
     uint2 *rest;      // [units][G][rstride / TR]: second key; offsets of the best (bits 0-7) and
                       // the second (bits 8-15), upper 16 bits of the third key (bits 16-31)
     uint32_t *bmax;   // [units][nblk][G]
+    // Mass diagnostic (null: off): per block and query the largest candidate score m and
+    // sum of exp2((s - m) * scale_log2e) over the block's candidate rows, [units][nblk][G][2].
+    float2 *zsum;
+    float scale_log2e;
 };
 
 // 16-byte load of a key-row slice; NTL: non-temporal (streamed once, kept out of the caches).
@@ -50,7 +54,7 @@ __device__ __forceinline__ uint4 load_row16(const uint4 *p) {
 }
 
 // BW blocks of 256 rows per workgroup (4 wavefronts each).
-template <typename T, int D, int G, int BW, bool NTL>
+template <typename T, int D, int G, int BW, bool NTL, bool MASS>
 __global__ __launch_bounds__(256 * BW) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 5 : 4))) void score_keys_kernel(
     const T *__restrict__ q, const T *__restrict__ k, KeysArgs a) {
     constexpr int EB = sizeof(T);
@@ -166,9 +170,21 @@ __global__ __launch_bounds__(256 * BW) __attribute__((amdgpu_waves_per_eu(sizeof
     }
     // Tile summaries, one thread per (query, tile) of the workgroup's blocks: the two best
     // (key, offset) in the ranking order (larger key, then smaller offset) and the third key.
+    // With the mass diagnostic also the tile's sum of exp2((s - m) * scale) relative to its
+    // block's best score m.
     const int nt = nbw * kBlockRows / TR;
+    __shared__ float tsum[MASS ? G : 1][MASS ? BW * kBlockRows / TR : 1];
+    constexpr bool mass = MASS;
     for (int x = tid; x < G * nt; x += 256 * BW) {
         const int t = x / nt, j = x - t * nt;
+        float mb = 0.f, zs = 0.f;
+        if constexpr (mass) {
+            const int b2 = j * TR / kBlockRows;
+            uint32_t mk = 0u;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) mk = red[4 * b2 + w][t] > mk ? red[4 * b2 + w][t] : mk;
+            mb = mk ? key_score(mk) : 0.f;
+        }
         uint32_t k1 = 0u, o1 = 0u, k2 = 0u, o2 = 0u, k3 = 0u;
 #pragma unroll
         for (int w4 = 0; w4 < TR / 4; ++w4) {
@@ -177,6 +193,9 @@ __global__ __launch_bounds__(256 * BW) __attribute__((amdgpu_waves_per_eu(sizeof
 #pragma unroll
             for (int c = 0; c < 4; ++c) {  // staged position 4*w4 + c holds row offset RPG*c + w4
                 const uint32_t key = kv[c], off = (uint32_t)(RPG * c + w4);
+                if constexpr (mass) {
+                    if (key) zs += exp2f((key_score(key) - mb) * a.scale_log2e);
+                }
                 const bool b1 = key > k1 || (key == k1 && off < o1);
                 const bool b2 = key > k2 || (key == k2 && off < o2);
                 k3 = b2 ? k2 : (key > k3 ? key : k3);
@@ -189,12 +208,32 @@ __global__ __launch_bounds__(256 * BW) __attribute__((amdgpu_waves_per_eu(sizeof
         const size_t o = ((size_t)u * G + t) * (size_t)(a.rstride / TR) + wg_row0 / TR + j;
         a.best1[o] = k1;
         a.rest[o] = make_uint2(k2, o1 | (o2 << 8) | (k3 & 0xFFFF0000u));
+        if constexpr (mass) tsum[t][j] = zs;
+    }
+    if constexpr (mass) {
+        // Per block and query: its tiles' sums in tile order.
+        __syncthreads();
+        constexpr int TPB = kBlockRows / TR;  // tiles per block
+        if (tid < BW * G) {
+            const int b2 = tid / G, t = tid % G;
+            if (b2 < nbw) {
+                uint32_t mk = 0u;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) mk = red[4 * b2 + w][t] > mk ? red[4 * b2 + w][t] : mk;
+                float l = 0.f;
+#pragma unroll
+                for (int jj = 0; jj < TPB; ++jj) l += tsum[t][b2 * TPB + jj];
+                a.zsum[((size_t)u * a.nblk + wg_row0 / kBlockRows + b2) * G + t] =
+                    make_float2(mk ? key_score(mk) : -INFINITY, mk ? l : 0.f);
+            }
+        }
     }
 }
 
 }  // namespace
 
-hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s) {
+hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
+                             bool mass) {
     KeysArgs a;
     a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g; a.W = pl.W;
     a.groups = pl.groups; a.units = pl.units; a.rstride = pl.rstride; a.nblk = pl.nblk;
@@ -204,10 +243,18 @@ hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void 
     a.best1 = reinterpret_cast<uint32_t *>(w + pl.best1_offset);
     a.rest = reinterpret_cast<uint2 *>(w + pl.rest_offset);
     a.bmax = reinterpret_cast<uint32_t *>(w + pl.bmax_offset);
+    a.zsum = mass ? reinterpret_cast<float2 *>(w + pl.zsum_offset) : nullptr;
+    a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
     dim3 grid((unsigned)(pl.units * ((pl.nblk + kKeysBW - 1) / kKeysBW))), block(256 * kKeysBW);
-#define CA_LAUNCH_SK(T, D, G) \
-    hipLaunchKernelGGL((score_keys_kernel<T, D, G, kKeysBW, kKeysNT>), grid, block, 0, s,       \
-                       static_cast<const T *>(q), static_cast<const T *>(k), a)
+#define CA_LAUNCH_SK(T, D, G)                                                                      \
+    do {                                                                                           \
+        if (mass)                                                                                  \
+            hipLaunchKernelGGL((score_keys_kernel<T, D, G, kKeysBW, kKeysNT, true>), grid, block, 0, s, \
+                               static_cast<const T *>(q), static_cast<const T *>(k), a);            \
+        else                                                                                       \
+            hipLaunchKernelGGL((score_keys_kernel<T, D, G, kKeysBW, kKeysNT, false>), grid, block, 0, s, \
+                               static_cast<const T *>(q), static_cast<const T *>(k), a);            \
+    } while (0)
 #define CA_LAUNCH_SK_G(T, D)                          \
     do {                                              \
         if (pl.G == 4) CA_LAUNCH_SK(T, D, 4);         \

@@ -120,3 +120,27 @@ def test_workspace_size_rules(lib):
     for c in (0, 256, 512, 1024):
         assert ws_size(good(chunk=c))[0] == ca.CA_OK
     assert ws_size(good(topk=512, W=16))[0] == ca.CA_OK
+
+
+def test_mass_entry_point_rules(lib):
+    """The mass diagnostic runs on the streaming decode path only; other plans, missing
+    pointers and short workspaces are rejected on the host."""
+    vp = ctypes.c_void_p(16)
+    # A decode (streaming path): a NULL mass pointer is an argument error, a short workspace a
+    # workspace error.
+    p = ca.Params(batch=1, heads=4, kv_heads=1, d=128, n=4000, nq=1, W=64, topk=32,
+                  dtype=ca.CA_BF16, chunk=0)
+    rc, need = ws_size(p)
+    assert rc == ca.CA_OK and need > 0
+    assert lib.ca_condensate_attention_mass_ex(ctypes.byref(p), vp, vp, vp, vp, vp, None, vp, need,
+                                               None) == ca.CA_ERR_INVALID_ARG
+    assert lib.ca_condensate_attention_mass_ex(ctypes.byref(p), vp, vp, vp, vp, vp, vp, vp, need - 1,
+                                               None) == ca.CA_ERR_WORKSPACE
+    # The chunked path (chunk = 256) and a prefill that takes the MFMA path: unsupported.
+    for q in (ca.Params(batch=1, heads=4, kv_heads=1, d=128, n=4000, nq=1, W=64, topk=32,
+                        dtype=ca.CA_BF16, chunk=256),
+              ca.Params(batch=1, heads=2, kv_heads=2, d=128, n=2000, nq=600, W=64, topk=64,
+                        dtype=ca.CA_BF16, chunk=0)):
+        assert lib.ca_condensate_attention_mass_ex(ctypes.byref(q), vp, vp, vp, vp, vp, vp, vp,
+                                                   1 << 40, None) == ca.CA_ERR_UNSUPPORTED
+        assert "streaming decode" in ca.last_error()
