@@ -80,6 +80,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mass", action="store_true",
                     help="time the call with the mass diagnostic (decode path only)")
+    ap.add_argument("--dense", action="store_true",
+                    help="time dense causal attention (bf16) on the workload instead of the method")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (counter calibration)")
     args = ap.parse_args()
@@ -124,7 +126,9 @@ def main():
 
     def step(s):
         kk, vv = sets[s % rotate]
-        if args.mass:
+        if args.dense:
+            ca.dense_attention_ex(p, q, kk, vv, out)
+        elif args.mass:
             ca.condensate_attention_mass_ex(p, q, kk, vv, out, idx, mass, ws)
         else:
             ca.condensate_attention_ex(p, q, kk, vv, out, idx, ws)
@@ -161,7 +165,7 @@ def main():
     rmax = max(0, w.n - 1 - w.W)
     q_bytes = w.batch * w.heads * w.nq * w.d * eb
     score_bytes = w.batch * w.kv_heads * rmax * w.d * eb + q_bytes
-    idx_np = idx.cpu().numpy()
+    idx_np = idx.cpu().numpy() if not args.dense else np.full(idx.shape, -1, dtype=np.int32)
     v_rows = 0
     for b in range(w.batch):
         for kvh in range(w.kv_heads):
@@ -171,7 +175,26 @@ def main():
                   + idx_np.size * 4)
     nqv = w.batch * w.heads * w.nq
 
-    if "mfma_bound" in prof:
+    if args.dense:
+        # Dense causal attention: q.k and the weights times V for every causal pair.
+        nd, td = prof.get("dense", (0, 0.0))
+        dense_s = td / max(1, nd) / 1e3
+        pos0 = w.n - w.nq
+        pairs = w.batch * w.heads * (w.nq * (pos0 + 1) + w.nq * (w.nq - 1) // 2)
+        flops = 4 * w.d * pairs
+        ach = flops / dense_s / 1e12 if nd else None
+        roofline = {
+            "kernel": "dense (mfma_window over every causal row)",
+            "bound": "mfma",
+            "achieved": ach,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": ach / MFMA_BF16_PEAK_TFLOPS if ach else None,
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": dense_s * 1e6,
+        }
+    elif "mfma_bound" in prof:
         # Prefill path: the scores of every causal pair j <= i are a dense bf16 product run on
         # the matrix cores, twice (bound pass, candidate pass); the algorithmic work is one.
         nb, tb = prof["mfma_bound"]
@@ -198,7 +221,7 @@ def main():
     score_avg_s = score_ms / max(1, launches) / 1e3
     achieved = score_bytes / score_avg_s / 1e9 if launches else None
     traffic = recorded_traffic(w.name)
-    if "mfma_bound" not in prof:
+    if "mfma_bound" not in prof and not args.dense:
         roofline = {
             "kernel": "score_keys (score stage)" if score_name == "score_keys" else "score_topk (score stage)",
             "bound": "hbm",
@@ -228,7 +251,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "kv_heads": w.kv_heads,
                    "d": w.d, "n": w.n, "nq": w.nq, "W": w.W, "topk": w.topk, "accumulate": "f32",
                    "chunk": args.chunk or "auto", "kv_sets_rotated": rotate, "seed": seed,
-                   "mass_diagnostic": bool(args.mass)},
+                   "mass_diagnostic": bool(args.mass), "dense_baseline": bool(args.dense)},
         "hbm_gbps": step_bytes / (ms_per_step / 1e3) / 1e9,
         "step_algorithmic_bytes": step_bytes,
         "gpu_ms_per_step": gpu_ms / args.steps,

@@ -108,6 +108,14 @@ int ca_condensate_attention_mass_ex(const ca_params *p, const void *q, const voi
                                     const void *v, float *out, int32_t *out_idx, float *mass,
                                     void *ws, size_t ws_bytes, void *stream);
 
+/* Dense causal attention, the baseline of the pages' speed comparison (section 5.1.2, against
+ * full attention): for each query, softmax of q . k_j / sqrt(d) over every j <= i, times V, on
+ * the matrix cores (bf16 products, fp32 accumulation; the weights enter the V product as bf16).
+ * W and topk of p are validated but not used. bfloat16 only (else CA_ERR_UNSUPPORTED); no
+ * workspace; asynchronous on `stream`. */
+int ca_dense_attention_ex(const ca_params *p, const void *q, const void *k, const void *v,
+                          float *out, void *stream);
+
 /* Stage 1 (identify_condensate, section 5.2.2): scores every causal key and writes C_i to
  * out_idx only. Same workspace as the full method. */
 int ca_condensate_select(const ca_params *p, const void *q, const void *k, int32_t *out_idx,
@@ -130,7 +138,7 @@ int ca_attention_on_subset(const ca_params *p, const void *q, const void *k, con
  * number of kernels seen. Not meant to be used from several threads at once. */
 typedef struct {
     const char *kernel;  /* static name: "score_keys", "score_select", "mfma_bound", "mfma_cand",
-                            "mfma_window", "finish" or "attend" */
+                            "mfma_window", "finish", "attend" or "dense" */
     int64_t launches;
     double total_ms;
 } ca_kernel_time;

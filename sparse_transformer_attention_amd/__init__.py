@@ -29,7 +29,8 @@ CA_F32, CA_BF16 = 0, 1
 CA_MAX_SET = 4096
 
 EXPORTED = ("ca_condensate_attention", "ca_workspace_size", "ca_condensate_attention_ex",
-            "ca_condensate_attention_mass_ex", "ca_condensate_select", "ca_attention_on_subset",
+            "ca_condensate_attention_mass_ex", "ca_dense_attention_ex", "ca_condensate_select",
+            "ca_attention_on_subset",
             "ca_profile_start", "ca_profile_stop", "ca_status_string", "ca_last_error")
 
 
@@ -72,6 +73,7 @@ def load() -> ctypes.CDLL:
         L.ca_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         L.ca_condensate_attention_ex.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.ca_condensate_attention_mass_ex.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.ca_dense_attention_ex.argtypes = [P, vp, vp, vp, vp, vp]
         L.ca_condensate_select.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.ca_attention_on_subset.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.ca_profile_start.argtypes = [ctypes.c_int32]
@@ -82,7 +84,7 @@ def load() -> ctypes.CDLL:
         L.ca_last_error.argtypes = []
         L.ca_last_error.restype = ctypes.c_char_p
         for f in (L.ca_condensate_attention, L.ca_workspace_size, L.ca_condensate_attention_ex,
-                  L.ca_condensate_attention_mass_ex, L.ca_condensate_select,
+                  L.ca_condensate_attention_mass_ex, L.ca_dense_attention_ex, L.ca_condensate_select,
                   L.ca_attention_on_subset, L.ca_profile_start, L.ca_profile_stop):
             f.restype = ctypes.c_int
         _lib = L
@@ -169,6 +171,23 @@ def condensate_attention_mass_ex(p: Params, q, k, v, out, out_idx, mass, ws, str
         _dev_ptr(out, "out", torch.float32), _dev_ptr(out_idx, "out_idx", torch.int32),
         _dev_ptr(mass, "mass", torch.float32), _dev_ptr(ws, "ws"), ws_bytes, _stream_ptr(stream)),
         "ca_condensate_attention_mass_ex")
+
+
+def dense_attention_ex(p: Params, q, k, v, out, stream=None):
+    """ca_dense_attention_ex: dense causal attention (bf16), out float32 [B][Hq][nq][d]."""
+    dt = q.dtype
+    _check(load().ca_dense_attention_ex(
+        ctypes.byref(p), _dev_ptr(q, "q", dt), _dev_ptr(k, "k", dt), _dev_ptr(v, "v", dt),
+        _dev_ptr(out, "out", torch.float32), _stream_ptr(stream)), "ca_dense_attention_ex")
+
+
+def dense_attention(q, k, v, stream=None):
+    """Dense causal attention of the last nq positions over all n keys (bf16 inputs)."""
+    p = params_for(q, k, 1, 0, 0)
+    B, Hq, nq, d = q.shape
+    out = torch.empty((B, Hq, nq, d), dtype=torch.float32, device=q.device)
+    dense_attention_ex(p, q, k, v, out, stream)
+    return out
 
 
 def condensate_select(p: Params, q, k, out_idx, ws, stream=None):

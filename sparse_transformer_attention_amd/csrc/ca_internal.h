@@ -78,6 +78,9 @@ constexpr int kMfmaSeg = 64;
 // pass 0: the bound of every query; pass 1: its candidate list.
 hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
                               int pass);
+// Dense causal attention (bf16, matrix cores): the baseline the method is measured against.
+hipError_t launch_dense_attention(const Plan &pl, const void *q, const void *k, const void *v,
+                                  float *out, hipStream_t s);
 // Anchor-and-window softmax partials of every query vector into the workspace (MFMA path).
 hipError_t launch_mfma_window(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
                               hipStream_t s);

@@ -14,9 +14,9 @@ namespace {
 
 // ---- measurement hooks: HIP events around each launch while profiling is on ----------------
 enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_BOUND = 3, K_CAND = 4, K_KEYS = 5, K_WINDOW = 6,
-       K_COUNT = 7 };
+       K_DENSE = 7, K_COUNT = 8 };
 const char *const kKernelNames[K_COUNT] = {"score_select", "finish", "attend", "mfma_bound", "mfma_cand",
-                                           "score_keys", "mfma_window"};
+                                           "score_keys", "mfma_window", "dense"};
 
 struct Profiler {
     std::mutex mu;
@@ -342,6 +342,22 @@ int ca_condensate_attention_mass_ex(const ca_params *p, const void *q, const voi
         return fail(CA_ERR_INVALID_ARG, "q, k, v, out, out_idx and mass must be non-NULL");
     if ((rc = check_ws(pl, ws, ws_bytes)) != CA_OK) return rc;
     return run_path(pl, q, k, v, out_idx, out, ws, static_cast<hipStream_t>(stream), mass);
+}
+
+int ca_dense_attention_ex(const ca_params *p, const void *q, const void *k, const void *v,
+                          float *out, void *stream) {
+    ca::Plan pl;
+    int rc = make_plan(p, &pl);
+    if (rc != CA_OK) return rc;
+    if (pl.dtype != CA_BF16)
+        return fail(CA_ERR_UNSUPPORTED, "dense attention runs on the matrix cores: bfloat16 inputs only");
+    if (!q || !k || !v || !out) return fail(CA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ProfScope pd(K_DENSE, s);
+    hipError_t e = ca::launch_dense_attention(pl, q, k, v, out, s);
+    pd.done();
+    if (e != hipSuccess) return hip_fail(e, "dense attention launch");
+    return CA_OK;
 }
 
 int ca_condensate_attention(const void *q, const void *k, const void *v, int64_t n, int32_t d,

@@ -455,7 +455,8 @@ struct WinArgs {
     int Hq, Hkv, g, W;
     uint32_t nvec, wg_per_unit, nwg;
     float scale_log2e;
-    float *win;  // [nqv][D + 2]
+    float *win;  // [nqv][D + 2] partials, or null
+    float *out;  // [nqv][D] normalised outputs (with W >= n: dense causal attention), or null
 };
 
 // K and V rows base..base+63 of a tile (clamped to n - 1): 16-byte chunks, NCH per thread.
@@ -618,7 +619,16 @@ __global__ __launch_bounds__(256) void mfma_window_kernel(const __bf16 *__restri
         __syncthreads();
     }
     lsum = __uint_as_float(quad_sum_f32_bits(__float_as_uint(lsum)));
-    if (valid) {
+    if (valid && a.out) {
+        // The softmax over the rows seen, times V: with a window of n or more rows, dense causal
+        // attention (the denominator of the method's speedup).
+        float *out = a.out + (size_t)qv * D;
+        const float inv = 1.f / lsum;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[db * 16 + 4 * grp + r] = o[db][r] * inv;
+    } else if (valid) {
         float *out = a.win + (size_t)qv * (D + 2);
         if (grp == 0) { out[0] = m; out[1] = lsum; }
 #pragma unroll
@@ -664,6 +674,25 @@ hipError_t launch_mfma_window(const Plan &pl, const void *q, const void *k, cons
     a.nwg = (uint32_t)(pl.B * pl.Hkv) * a.wg_per_unit;
     a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
     a.win = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.win_offset);
+    a.out = nullptr;
+    const __bf16 *qt = static_cast<const __bf16 *>(q), *kt = static_cast<const __bf16 *>(k),
+                 *vt = static_cast<const __bf16 *>(v);
+    if (pl.d == 128) hipLaunchKernelGGL((mfma_window_kernel<128>), dim3(a.nwg), dim3(256), 0, s, qt, kt, vt, a);
+    else hipLaunchKernelGGL((mfma_window_kernel<64>), dim3(a.nwg), dim3(256), 0, s, qt, kt, vt, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_attention(const Plan &pl, const void *q, const void *k, const void *v,
+                                  float *out, hipStream_t s) {
+    WinArgs a;
+    a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g;
+    a.W = (int)pl.n;  // the window covers every causal position: C_i = {0..i}
+    a.nvec = (uint32_t)(pl.g * pl.nq);
+    a.wg_per_unit = (a.nvec + 63) / 64;
+    a.nwg = (uint32_t)(pl.B * pl.Hkv) * a.wg_per_unit;
+    a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
+    a.win = nullptr;
+    a.out = out;
     const __bf16 *qt = static_cast<const __bf16 *>(q), *kt = static_cast<const __bf16 *>(k),
                  *vt = static_cast<const __bf16 *>(v);
     if (pl.d == 128) hipLaunchKernelGGL((mfma_window_kernel<128>), dim3(a.nwg), dim3(256), 0, s, qt, kt, vt, a);

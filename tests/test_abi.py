@@ -144,3 +144,13 @@ def test_mass_entry_point_rules(lib):
         assert lib.ca_condensate_attention_mass_ex(ctypes.byref(q), vp, vp, vp, vp, vp, vp, vp,
                                                    1 << 40, None) == ca.CA_ERR_UNSUPPORTED
         assert "streaming decode" in ca.last_error()
+
+
+def test_dense_entry_point_rules(lib):
+    vp = ctypes.c_void_p(16)
+    p = ca.Params(batch=1, heads=2, kv_heads=2, d=128, n=1000, nq=1000, W=4, topk=2,
+                  dtype=ca.CA_F32, chunk=0)
+    assert lib.ca_dense_attention_ex(ctypes.byref(p), vp, vp, vp, vp, None) == ca.CA_ERR_UNSUPPORTED
+    assert "bfloat16" in ca.last_error()
+    p.dtype = ca.CA_BF16
+    assert lib.ca_dense_attention_ex(ctypes.byref(p), vp, None, vp, vp, None) == ca.CA_ERR_INVALID_ARG
