@@ -153,9 +153,11 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     P.win_offset = 0;
     P.zsum_offset = 0;
     // Many bf16 query vectors per KV head: the MFMA passes (bound, then candidate lists in the
-    // segment layout of the chunked path: 4 segments of kMfmaSeg keys per query).
+    // segment layout of the chunked path: 4 segments of kMfmaSeg keys per query). They address
+    // a KV head's key rows with 32-bit byte offsets.
     if (P.candidates && p->chunk == 0 && P.dtype == CA_BF16 && P.topk <= kMfmaMaxTopk &&
-        nvec >= kMfmaMinVectors && nvec < ((int64_t)1 << 31) && P.nqv < ((int64_t)1 << 31)) {
+        nvec >= kMfmaMinVectors && nvec < ((int64_t)1 << 31) && P.nqv < ((int64_t)1 << 31) &&
+        P.n * (int64_t)P.d * 2 <= ((int64_t)1 << 32)) {
         P.mfma = true;
         P.wpu = 4;
         P.seg = ca::kMfmaSeg;

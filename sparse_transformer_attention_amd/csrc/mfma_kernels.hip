@@ -14,10 +14,11 @@
 //
 // The exact top-k' of R_i (k' = min(k, |R_i|) <= 128) takes two passes over the same products
 // (the same instruction sequence, hence bit-identical scores):
-//   bound  For each query, the maxima of its candidate rows in the 128 classes j mod 128. The
-//          classes are disjoint, so k' distinct rows reach the k'-th largest of those maxima: a
-//          lower bound of the query's k'-th score. The lower edge of the 16-bit radix bin that
-//          holds it goes out as a score key.
+//   bound  For each query, one score of its candidate rows in each of the 128 classes j mod 128
+//          (the class maximum whenever the class holds a non-negative score). The classes are
+//          disjoint, so k' distinct rows reach the k'-th largest of those scores: a lower bound
+//          of the query's k'-th score. The lower edge of the 16-bit radix bin that holds it goes
+//          out as a score key.
 //   cand   Every candidate row whose score key reaches the bound is appended to the query's
 //          list as a ranking key (about k + k/4 of them on Gaussian data). A list that might
 //          not take another tile is cut to its exact top-k' (wave_keep_top_u64); from then on
@@ -198,7 +199,14 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
             lbase[qb] = a.lists + ((size_t)qvi[qb] * kLanesPerQuery + grp) * kMfmaSeg;
         }
     }
-    float m[2][4][4][QB];  // [tile parity][16-row block][row of the lane][query]: class maxima
+    // [tile parity][16-row block][row of the lane][query]: per class, the largest score as a
+    // signed integer over the float's bits. That order agrees with the float order for every
+    // pair that holds a non-negative score, so a class with one gets its maximum; a class with
+    // only negative scores gets one of them (the most negative) and one with none gets INT_MIN
+    // (the bits of -0.0, read as "no row"). Every value kept is the score of a row of its class,
+    // which is all the bound needs, and the maximum costs one integer instruction per score (a
+    // float maximum would first quiet each product as a possible NaN).
+    int32_t m[2][4][4][QB];
     if constexpr (!CAND) {
 #pragma unroll
         for (int p = 0; p < 2; ++p)
@@ -207,23 +215,34 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) m[p][kb][r][qb] = -INFINITY;
+                    for (int qb = 0; qb < QB; ++qb) m[p][kb][r][qb] = INT32_MIN;
     }
 
     const __bf16 *kbase = k + (size_t)bk * (size_t)a.n * D;
     const int nlast = (int)a.n - 1;
     // The wavefronts' share of tile t, straight from memory into LDS buffer B: instruction u of
     // wavefront w fills chunks (4u + w)*64 .. +63 of the tile, lane by lane (16 bytes each), so
-    // lane l fetches the row chunk that the swizzle puts there. Rows past n - 1 are clamped.
+    // lane l fetches the row chunk that the swizzle puts there: row lrow[u] of the tile, chunk
+    // byte offset coff[u]. Rows past n - 1 are clamped. Addresses are the KV head's base plus a
+    // 32-bit byte offset (the plan keeps a KV head's rows below 4 GiB).
+    int lrow[NCH];
+    uint32_t coff[NCH];
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+        const int p = (u * 4 + wave) * 64 + lane;
+        const int row = p / CPR, c = (p % CPR) ^ chunk_swizzle<D>(row);
+        lrow[u] = row;
+        coff[u] = (uint32_t)c * 16u;
+    }
+    const char *kbytes = reinterpret_cast<const char *>(kbase);
     auto issue = [&](int t, auto bufc) {
         constexpr int B = decltype(bufc)::value;
+        const int j0 = t * kTile;
 #pragma unroll
         for (int u = 0; u < NCH; ++u) {
-            const int p = (u * 4 + wave) * 64 + lane;
-            const int row = p / CPR, c = (p % CPR) ^ chunk_swizzle<D>(row);
-            const int j = t * kTile + row;
-            const __bf16 *src = kbase + (size_t)(j < nlast ? j : nlast) * D + c * 8;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+            const int j = j0 + lrow[u];
+            const uint32_t off = (uint32_t)(j < nlast ? j : nlast) * (uint32_t)(D * sizeof(__bf16)) + coff[u];
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(kbytes + off),
                                              (__attribute__((address_space(3))) void *)&kt[B][(u * 4 + wave) * 64],
                                              16, 0, 0);
         }
@@ -299,9 +318,9 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
                 for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float v = acc[qb][r];
-                        if constexpr (!INNER) v = (jb + r >= 1 && jb + r <= lim[qb]) ? v : -INFINITY;
-                        m[P][kb][r][qb] = fmaxf(m[P][kb][r][qb], v);
+                        int32_t v = __float_as_int(acc[qb][r]);
+                        if constexpr (!INNER) v = (jb + r >= 1 && jb + r <= lim[qb]) ? v : INT32_MIN;
+                        m[P][kb][r][qb] = v > m[P][kb][r][qb] ? v : m[P][kb][r][qb];
                     }
             } else {
                 // About k + k/4 of a query's rows reach its bound, so with 64 queries a block
@@ -394,8 +413,8 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
             uint32_t nz = 0u, hmax = 0u, hmin = 0xFFFFFFFFu;
 #pragma unroll
             for (int s = 0; s < 32; ++s) {
-                const float v = m[s / 16][(s / 4) % 4][s % 4][qb];
-                x[s] = v > -INFINITY ? score_key(v) : 0u;
+                const int32_t v = m[s / 16][(s / 4) % 4][s % 4][qb];
+                x[s] = v != INT32_MIN ? score_key(__int_as_float(v)) : 0u;
                 nz += x[s] != 0u;
                 hmax = x[s] > hmax ? x[s] : hmax;
                 hmin = x[s] != 0u && x[s] < hmin ? x[s] : hmin;
