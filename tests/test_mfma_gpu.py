@@ -76,6 +76,9 @@ def integer_inputs(w, seed, levels=2):
 @pytest.mark.parametrize("shape", [
     dict(d=64, heads=2, kv_heads=2, n=3000, nq=128, W=30, topk=20),
     dict(d=128, heads=4, kv_heads=1, n=2500, nq=70, W=10, topk=128),
+    # Over 1024 rows per kept key: the candidate pass with its block pre-test (and here the
+    # pre-test lets every block of a tied bound through to the exact compare).
+    dict(d=128, heads=2, kv_heads=2, n=3000, nq=64, W=30, topk=2),
 ])
 def test_mfma_exact_ties_follow_the_tie_break(shape):
     """Many keys tie at the bound, so candidate lists fill and are cut to their exact top-k'
