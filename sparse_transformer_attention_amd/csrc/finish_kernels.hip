@@ -180,6 +180,46 @@ __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at,
     __syncthreads();
 }
 
+// Exact top-kp of n distinct non-zero ranking keys in gathered[0..n) (kp <= n <= kRankSelectMax,
+// so the tail of gathered[] holds a copy clear of them) by rank counting: a key is selected when
+// fewer than kp keys beat it; the selected positions are then placed by their rank among the
+// selected ones (ascending) in js[0..kp). S lanes per candidate (S*n <= NT, S <= 16): lane s
+// compares against keys s, s+S, ..., and the S counts are summed. All threads; ends with an
+// LDS barrier.
+constexpr int kRankSelectMax = 256;
+static_assert(2 * kRankSelectMax <= kGather, "rank select room");
+template <int NT>
+__device__ __forceinline__ void select_by_rank(int n, int kp, uint64_t *gathered, int32_t *js) {
+    const int tid = threadIdx.x;
+    int lg = 4;
+    while (lg > 0 && (n << lg) > NT) --lg;
+    const int S = 1 << lg, c = tid >> lg, sl = tid & (S - 1);
+    const bool mine = c < n;
+    const uint64_t x = gathered[mine ? c : 0];
+    int above = 0;
+    if (mine) {
+#pragma unroll 4
+        for (int f = sl; f < n; f += S) above += gathered[f] > x;
+    }
+    for (int off = 1; off < S; off <<= 1) above += __shfl_xor(above, off);
+    const bool chosen = mine && above < kp;
+    // Selected keys (0 = not) in the tail of gathered[], clear of [0, n).
+    if (mine && sl == 0) gathered[kGather - 1 - c] = chosen ? x : 0ull;
+    lds_barrier();
+    const int32_t pos = rank_key_pos(x);
+    int rank = 0;
+    if (chosen) {
+#pragma unroll 4
+        for (int f = sl; f < n; f += S) {
+            const uint64_t y = gathered[kGather - 1 - f];
+            rank += y != 0ull && rank_key_pos(y) < pos;
+        }
+    }
+    for (int off = 1; off < S; off <<= 1) rank += __shfl_xor(rank, off);
+    if (chosen && sl == 0) js[rank] = pos;
+    lds_barrier();
+}
+
 // Candidates from the segments of score_topk or of the MFMA passes (the first cnt[w] keys of
 // each segment w of lists[w][0..seg)), gathered into LDS by wavefront 0 while the other wavefronts run
 // overlap(); then the exact top-kp.
@@ -222,6 +262,10 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
     __syncthreads();
     const int n = sh.sel_count;
     __syncthreads();
+    if (n >= kp && n <= kRankSelectMax) {
+        select_by_rank<NT>(n, kp, gathered, js);
+        return;
+    }
     auto key_at = [&](int64_t f) -> uint64_t {
         const int w = (int)(f / topk);
         const int e = (int)(f - (int64_t)w * topk);
@@ -246,7 +290,6 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
 // this query, calling emit(key, row) for each of its candidate rows. All threads.
 constexpr int kTileCap = 1024;
 constexpr int kOvfCap = 64;
-constexpr int kRankSelectMax = 256;  // candidates selected by rank counting (else radix select)
 
 template <int NT, typename Overlap, typename Rescore>
 __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
@@ -373,37 +416,7 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
     }
     __syncthreads();
     if (n <= kRankSelectMax && n >= kp) {
-        // Few candidates: a key is selected when fewer than kp keys beat it; the selected
-        // positions are then placed by their rank among the selected ones (ascending). S lanes
-        // per candidate (S*n <= NT, S <= 16): lane s compares against keys s, s+S, ..., and the S
-        // counts are summed.
-        int lg = 4;
-        while (lg > 0 && (n << lg) > NT) --lg;
-        const int S = 1 << lg, c = tid >> lg, sl = tid & (S - 1);
-        const bool mine = c < n;
-        const uint64_t x = gathered[mine ? c : 0];
-        int above = 0;
-        if (mine) {
-#pragma unroll 4
-            for (int f = sl; f < n; f += S) above += gathered[f] > x;
-        }
-        for (int off = 1; off < S; off <<= 1) above += __shfl_xor(above, off);
-        const bool chosen = mine && above < kp;
-        // Selected keys (0 = not) in the tail of gathered[], clear of [0, n).
-        if (mine && sl == 0) gathered[kGather - 1 - c] = chosen ? x : 0ull;
-        lds_barrier();
-        const int32_t pos = rank_key_pos(x);
-        int rank = 0;
-        if (chosen) {
-#pragma unroll 4
-            for (int f = sl; f < n; f += S) {
-                const uint64_t y = gathered[kGather - 1 - f];
-                rank += y != 0ull && rank_key_pos(y) < pos;
-            }
-        }
-        for (int off = 1; off < S; off <<= 1) rank += __shfl_xor(rank, off);
-        if (chosen && sl == 0) js[rank] = pos;
-        lds_barrier();
+        select_by_rank<NT>(n, kp, gathered, js);
         return;
     }
     // Keys from scratch for rows of passing tiles (others hold none that reach the bound).
