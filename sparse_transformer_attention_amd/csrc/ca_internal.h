@@ -70,9 +70,16 @@ size_t topk_lds_bytes(const Plan &pl);
 // mass: also the per-block sums of the mass diagnostic (zsum_offset).
 hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
                              bool mass = false);
-// Query blocks of 16 per wavefront of the two MFMA passes (64 * QB query vectors per workgroup).
-constexpr int kMfmaQBBound = 2;
+// Query blocks of 16 per wavefront of the two MFMA passes (16 * QB * kMfmaWaves query vectors per
+// workgroup).
+// Bound pass, per d. Measured: 3 at d = 64 (more products per operand read, 2 wavefronts per
+// SIMD instead of 3) gives 9.0 ms against 8.8 on the 131K prefill; at d = 128, 3 spills.
+constexpr int kMfmaQBBound128 = 2;
+constexpr int kMfmaQBBound64 = 2;
 constexpr int kMfmaQBCand = 4;
+// Wavefronts per workgroup of the MFMA passes (they share its LDS tiles). Measured: 8 (half the
+// key-row traffic from L2) is slower, 131K prefill candidate pass 9.8 -> 13.0 ms.
+constexpr int kMfmaWaves = 4;
 // The candidate pass keeps four lists of kMfmaSeg keys per query (one per lane that holds it).
 constexpr int kMfmaSeg = 64;
 // pass 0: the bound of every query; pass 1: its candidate list.

@@ -5,8 +5,8 @@
 //
 // When many query vectors read the same KV head, their scores are a dense product, computed
 // here on the matrix cores: v_mfma_f32_16x16x32_bf16 multiplies 16 key rows by 16 query vectors
-// over 32 elements of d per instruction, accumulating in fp32. A workgroup takes 64*QB query
-// vectors of one KV head (4 wavefronts of 16*QB, whose slices stay in registers) and brings the
+// over 32 elements of d per instruction, accumulating in fp32. A workgroup takes 16*QB*NWV query
+// vectors of one KV head (NWV wavefronts of 16*QB, whose slices stay in registers) and brings the
 // key rows 0..max(i - W) through LDS in tiles of 64 rows: a ring of four tiles filled straight
 // from memory (global_load_lds) three tiles ahead of their use, the 16-byte chunks of a row
 // XOR-swizzled so that the operand reads of 16 rows hit distinct banks. The scores are
@@ -106,16 +106,17 @@ __device__ __forceinline__ int chunk_at(int row, int c) {
     return row * (D / 8) + (c ^ chunk_swizzle<D>(row));
 }
 
-template <int D, int QB, bool CAND, bool PRE>
-__global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restrict__ q,
+template <int D, int QB, bool CAND, bool PRE, int NWV>
+__global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__restrict__ q,
                                                           const __bf16 *__restrict__ k,
                                                           MfmaArgs a) {
     constexpr int KS = D / 32;                  // MFMA steps over d
     constexpr int CPR = D / 8;                  // 16-byte chunks per key row
-    constexpr int NCH = kTile * CPR / 256;      // chunks per thread per tile
+    constexpr int NT = 64 * NWV;                // threads per workgroup
+    constexpr int NCH = kTile * CPR / NT;       // chunks per thread per tile
     constexpr int QW = 16 * QB;                 // query vectors per wavefront
-    constexpr int ROWS = 4 * QW;                // per workgroup
-    static_assert(NCH >= 1 && NCH * 256 == kTile * CPR, "tile");
+    constexpr int ROWS = NWV * QW;              // per workgroup
+    static_assert(NCH >= 1 && NCH * NT == kTile * CPR, "tile");
     // s_waitcnt with vmcnt = the loads a wavefront issues for kBuf - 2 tiles (expcnt and
     // lgkmcnt at their maxima: no wait on them).
     constexpr int kAhead = NCH * (kBuf - 2);
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
     // cut and the keys it keeps. (With several LDS objects the compiler waits for every tile in
     // flight before each operand read; the waits below are the ones needed.)
     constexpr int kCutWords = 320 + 2 * kMaxKeep;
-    constexpr int kExtra = CAND ? 4 * kCutWords / 4 : 0;
+    constexpr int kExtra = CAND ? NWV * kCutWords / 4 : 0;
     __shared__ uint4 smem[kBuf * kTile * CPR + kExtra];
     uint4 (*kt)[kTile * CPR] = reinterpret_cast<uint4 (*)[kTile * CPR]>(smem);
     uint32_t *cutw = reinterpret_cast<uint32_t *>(smem + kBuf * kTile * CPR) + wave_of_thread() * kCutWords;
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
     const __bf16 *kbase = k + (size_t)bk * (size_t)a.n * D;
     const int nlast = (int)a.n - 1;
     // The wavefronts' share of tile t, straight from memory into LDS buffer B: instruction u of
-    // wavefront w fills chunks (4u + w)*64 .. +63 of the tile, lane by lane (16 bytes each), so
+    // wavefront w fills chunks (NWV*u + w)*64 .. +63 of the tile, lane by lane (16 bytes each), so
     // lane l fetches the row chunk that the swizzle puts there: row lrow[u] of the tile, chunk
     // byte offset coff[u]. Rows past n - 1 are clamped. Addresses are the KV head's base plus a
     // 32-bit byte offset (the plan keeps a KV head's rows below 4 GiB).
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
     uint32_t coff[NCH];
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-        const int p = (u * 4 + wave) * 64 + lane;
+        const int p = (u * NWV + wave) * 64 + lane;
         const int row = p / CPR, c = (p % CPR) ^ chunk_swizzle<D>(row);
         lrow[u] = row;
         coff[u] = (uint32_t)c * 16u;
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(256) void mfma_select_kernel(const __bf16 *__restri
             const int j = j0 + lrow[u];
             const uint32_t off = (uint32_t)(j < nlast ? j : nlast) * (uint32_t)(D * sizeof(__bf16)) + coff[u];
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(kbytes + off),
-                                             (__attribute__((address_space(3))) void *)&kt[B][(u * 4 + wave) * 64],
+                                             (__attribute__((address_space(3))) void *)&kt[B][(u * NWV + wave) * 64],
                                              16, 0, 0);
         }
     };
@@ -705,10 +706,11 @@ hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void
     a.cnt = reinterpret_cast<uint32_t *>(w) + 2 * pl.nqv * pl.wpu;
     a.lists = reinterpret_cast<uint64_t *>(w + pl.lists_offset);
     const bool cand = pass != 0;
-    const int rows = 64 * (cand ? kMfmaQBCand : kMfmaQBBound);
+    const int qb_bound = pl.d == 128 ? kMfmaQBBound128 : kMfmaQBBound64;
+    const int rows = 16 * kMfmaWaves * (cand ? kMfmaQBCand : qb_bound);
     a.wg_per_unit = (uint32_t)((a.nvec + rows - 1) / rows);
     a.nwg = (uint32_t)(pl.B * pl.Hkv) * a.wg_per_unit;
-    const dim3 grid(a.nwg), block(256);
+    const dim3 grid(a.nwg), block(64 * kMfmaWaves);
     const __bf16 *qt = static_cast<const __bf16 *>(q), *kt = static_cast<const __bf16 *>(k);
     // Candidate pass: the block pre-test pays when few blocks hold a candidate, i.e. when the
     // queries have many rows per kept key: about 1.25k of a query's rows pass, so a block of 16
@@ -718,9 +720,9 @@ hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void
     const bool pre = mean_rows > 1024 * (int64_t)pl.topk;
 #define CA_MFMA_SELECT(D)                                                                          \
     do {                                                                                           \
-        if (!cand) hipLaunchKernelGGL((mfma_select_kernel<D, kMfmaQBBound, false, false>), grid, block, 0, s, qt, kt, a); \
-        else if (pre) hipLaunchKernelGGL((mfma_select_kernel<D, kMfmaQBCand, true, true>), grid, block, 0, s, qt, kt, a); \
-        else hipLaunchKernelGGL((mfma_select_kernel<D, kMfmaQBCand, true, false>), grid, block, 0, s, qt, kt, a); \
+        if (!cand) hipLaunchKernelGGL((mfma_select_kernel<D, D == 128 ? kMfmaQBBound128 : kMfmaQBBound64, false, false, kMfmaWaves>), grid, block, 0, s, qt, kt, a); \
+        else if (pre) hipLaunchKernelGGL((mfma_select_kernel<D, kMfmaQBCand, true, true, kMfmaWaves>), grid, block, 0, s, qt, kt, a); \
+        else hipLaunchKernelGGL((mfma_select_kernel<D, kMfmaQBCand, true, false, kMfmaWaves>), grid, block, 0, s, qt, kt, a); \
     } while (0)
     if (pl.d == 128) CA_MFMA_SELECT(128);
     else CA_MFMA_SELECT(64);
