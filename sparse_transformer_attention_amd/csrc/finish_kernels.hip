@@ -88,7 +88,8 @@ __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at,
         }
         __syncthreads();
         for (int t = tid; t < kp; t += NT) js[t] = rank_key_pos(sel[t]);
-    } else {
+    } else if constexpr (NT >= 256) {
+        // (128-thread workgroups select from at most 256 keys: never here.)
         uint64_t kmax = 0ull, kmin = ~0ull;
         for (int64_t f = tid; f < slots; f += NT) {
             const uint64_t x = key_at(f);
@@ -180,7 +181,7 @@ __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at,
     __syncthreads();
 }
 
-// Exact top-kp of n distinct non-zero ranking keys in gathered[0..n) (kp <= n <= kRankSelectMax,
+// Exact top-kp of n distinct non-zero ranking keys in gathered[0..n) (kp <= n <= kRankSelectMax, n <= NT,
 // so the tail of gathered[] holds a copy clear of them) by rank counting: a key is selected when
 // fewer than kp keys beat it; the selected positions are then placed by their rank among the
 // selected ones (ascending) in js[0..kp). S lanes per candidate (S*n <= NT, S <= 16): lane s
@@ -262,7 +263,7 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
     __syncthreads();
     const int n = sh.sel_count;
     __syncthreads();
-    if (n >= kp && n <= kRankSelectMax) {
+    if (n >= kp && n <= kRankSelectMax && n <= NT) {
         select_by_rank<NT>(n, kp, gathered, js);
         return;
     }
@@ -415,7 +416,7 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
         n = kGather + 1;
     }
     __syncthreads();
-    if (n <= kRankSelectMax && n >= kp) {
+    if (n <= kRankSelectMax && n <= NT && n >= kp) {
         select_by_rank<NT>(n, kp, gathered, js);
         return;
     }
@@ -485,7 +486,7 @@ __device__ __forceinline__ void rescore_tiles(const T *__restrict__ q, const T *
 // a window of up to 299 rows of 256 bytes in one round, 16 x 4 x 1 or 4 x 4 x 4 a top-64 part).
 constexpr int kWindowU = 5;
 template <int NT>
-constexpr int kTopU = NT >= 1024 ? 1 : 4;  // 256 threads: 4 x 4 x 4 rows, still one round
+constexpr int kTopU = NT >= 1024 ? 1 : 4;  // 256 threads: 4 x 4 x 4 rows, still one round (128: two)
 
 template <typename T, int D, int NT, bool ATTEND, bool TILES>
 __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, const T *__restrict__ k,
@@ -539,11 +540,12 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     // NW - 1, next to the top-k rows' partials NW..2NW-1.
     const bool pre_win = a.win != nullptr;
     if constexpr (ATTEND) {
-        if (pre_win && tid >= 64 && tid < 64 + D + 2) {
-            const float x = a.win[(size_t)qv * (D + 2) + (tid - 64)];
-            if (tid == 64) part.m[NW - 1] = x;
-            else if (tid == 65) part.l[NW - 1] = x;
-            else part.acc[NW - 1][tid - 66] = x;
+        // (Threads of the wavefronts after the first, which gathers the candidates.)
+        for (int e = tid - 64; pre_win && e >= 0 && e < D + 2; e += NT - 64) {
+            const float x = a.win[(size_t)qv * (D + 2) + e];
+            if (e == 0) part.m[NW - 1] = x;
+            else if (e == 1) part.l[NW - 1] = x;
+            else part.acc[NW - 1][e - 2] = x;
         }
     }
     auto window_part = [&](int wv, int nw) {
@@ -714,7 +716,9 @@ FinishArgs finish_args(const Plan &pl, const void *ws) {
     return a;
 }
 
-// Few query vectors: 1024 threads each (latency); many: 256.
+// Few query vectors: 1024 threads each (latency); many: 256, or 128 on the MFMA path, whose
+// candidate lists hold at most 256 keys and whose window partials are computed already (more
+// query vectors in flight per CU).
 constexpr int64_t kWideBelow = 4096;
 
 template <typename T, int D, bool ATTEND>
@@ -734,8 +738,12 @@ hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const 
                        out_idx, out, a)
     if (wide) {
         if (tiles) CA_LAUNCH_FIN(1024, true); else CA_LAUNCH_FIN(1024, false);
+    } else if (tiles) {
+        CA_LAUNCH_FIN(256, true);
+    } else if (pl.mfma && pl.wpu * pl.seg <= kRankSelectMax) {
+        CA_LAUNCH_FIN(128, false);
     } else {
-        if (tiles) CA_LAUNCH_FIN(256, true); else CA_LAUNCH_FIN(256, false);
+        CA_LAUNCH_FIN(256, false);
     }
 #undef CA_LAUNCH_FIN
     return hipGetLastError();
