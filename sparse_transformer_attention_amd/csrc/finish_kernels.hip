@@ -40,6 +40,10 @@ struct FinishArgs {
 };
 
 constexpr int kGather = 1024;  // candidates gathered into LDS for the one-wavefront select
+// Room for gathered candidates by workgroup size: 64- and 128-thread workgroups (the MFMA path)
+// gather lists of at most 256 keys.
+template <int NT>
+constexpr int kGatherFor = NT <= 128 ? 256 : kGather;
 constexpr int kMaxKeysPerThread = 16;  // candidate keys held in registers per thread
 
 template <int NT>
@@ -66,9 +70,9 @@ __device__ __forceinline__ uint64_t wave_min_u64_dpp(uint64_t x) {
 }
 
 // Exact top-kp of one query's candidates, given as n keys gathered in LDS (gathered[0..n) when
-// n <= kGather) and as key_at(f) over f in [0, slots) (0 = no candidate): the distinct,
+// n <= kGatherFor<NT>) and as key_at(f) over f in [0, slots) (0 = no candidate): the distinct,
 // non-zero ranking keys. The kp positions go to js[0..kp), ascending (js needs room for 2*kp).
-// Up to kGather candidates are selected by wavefront 0 alone with the keys in registers; more
+// Up to kGatherFor<NT> candidates are selected by wavefront 0 alone with the keys in registers; more
 // by the whole workgroup, calling key_at on every radix pass.
 template <int NT, typename KeyAt>
 __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at, int kp, int32_t *js,
@@ -76,13 +80,13 @@ __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at,
                                              SelectShared<NT> &sh) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (n <= kGather) {
+    if (n <= kGatherFor<NT>) {
         if (wave == 0) {
             uint64_t kk[kMaxKeysPerThread];
 #pragma unroll
             for (int e = 0; e < kMaxKeysPerThread; ++e) {
                 const int f = lane + 64 * e;
-                kk[e] = f < n ? gathered[f] : 0ull;
+                kk[e] = f < n && f < kGatherFor<NT> ? gathered[f] : 0ull;
             }
             (void)wave_keep_top_u64(kk, kp, &sh.hist[0][0], sel);
         }
@@ -188,7 +192,7 @@ __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at,
 // compares against keys s, s+S, ..., and the S counts are summed. All threads; ends with an
 // LDS barrier.
 constexpr int kRankSelectMax = 256;
-static_assert(2 * kRankSelectMax <= kGather, "rank select room");
+static_assert(2 * kRankSelectMax <= kGather && 2 * 128 <= kGatherFor<128>, "rank select room");
 template <int NT>
 __device__ __forceinline__ void select_by_rank(int n, int kp, uint64_t *gathered, int32_t *js) {
     const int tid = threadIdx.x;
@@ -205,14 +209,14 @@ __device__ __forceinline__ void select_by_rank(int n, int kp, uint64_t *gathered
     for (int off = 1; off < S; off <<= 1) above += __shfl_xor(above, off);
     const bool chosen = mine && above < kp;
     // Selected keys (0 = not) in the tail of gathered[], clear of [0, n).
-    if (mine && sl == 0) gathered[kGather - 1 - c] = chosen ? x : 0ull;
+    if (mine && sl == 0) gathered[kGatherFor<NT> - 1 - c] = chosen ? x : 0ull;
     lds_barrier();
     const int32_t pos = rank_key_pos(x);
     int rank = 0;
     if (chosen) {
 #pragma unroll 4
         for (int f = sl; f < n; f += S) {
-            const uint64_t y = gathered[kGather - 1 - f];
+            const uint64_t y = gathered[kGatherFor<NT> - 1 - f];
             rank += y != 0ull && rank_key_pos(y) < pos;
         }
     }
@@ -252,7 +256,7 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
                 const bool ok = f < slots && (uint32_t)(f % topk) < c[u];
                 const uint64_t bal = __ballot(ok);
                 const int pos = base + lanes_below(bal);
-                if (ok && pos < kGather) gathered[pos] = x[u];
+                if (ok && pos < kGatherFor<NT>) gathered[pos] = x[u];
                 base += __popcll(bal);
             }
         }
@@ -301,6 +305,7 @@ __device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
                                              int32_t *ovf, uint32_t *scratch,
                                              SelectShared<NT> &sh, Overlap overlap,
                                              Rescore rescore) {
+    static_assert(NT >= 256, "tile path: 256- or 1024-thread workgroups");
     constexpr int E = 8;   // block maxima per lane: at most 512 (merged in groups beyond)
     constexpr int TU = 8;  // tile maxima in flight per thread
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -496,7 +501,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     constexpr int NW = NT / 64;
     extern __shared__ int32_t fsm[];  // js[2*cap] positions, then sel[topk] keys
     __shared__ SelectShared<NT> ssh;
-    __shared__ uint64_t gathered[kGather];
+    __shared__ uint64_t gathered[kGatherFor<NT>];
     __shared__ int32_t tile_idx[TILES ? kTileCap : 1];
     __shared__ int32_t ovf_idx[TILES ? kOvfCap : 1];
     // Softmax partials: [0, NW) the anchor and window rows (wavefronts 1..NW-1 when wavefront 0
@@ -540,8 +545,10 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     // NW - 1, next to the top-k rows' partials NW..2NW-1.
     const bool pre_win = a.win != nullptr;
     if constexpr (ATTEND) {
-        // (Threads of the wavefronts after the first, which gathers the candidates.)
-        for (int e = tid - 64; pre_win && e >= 0 && e < D + 2; e += NT - 64) {
+        // (Threads of the wavefronts after the first, which gathers the candidates; all of a
+        // one-wavefront workgroup.)
+        constexpr int E0 = NT > 64 ? 64 : 0;
+        for (int e = tid - E0; pre_win && e >= 0 && e < D + 2; e += NT - E0) {
             const float x = a.win[(size_t)qv * (D + 2) + e];
             if (e == 0) part.m[NW - 1] = x;
             else if (e == 1) part.l[NW - 1] = x;
@@ -740,6 +747,8 @@ hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const 
         if (tiles) CA_LAUNCH_FIN(1024, true); else CA_LAUNCH_FIN(1024, false);
     } else if (tiles) {
         CA_LAUNCH_FIN(256, true);
+    } else if (pl.mfma && pl.wpu * pl.seg <= kRankSelectMax && pl.topk <= 32) {
+        CA_LAUNCH_FIN(64, false);
     } else if (pl.mfma && pl.wpu * pl.seg <= kRankSelectMax) {
         CA_LAUNCH_FIN(128, false);
     } else {

@@ -40,6 +40,10 @@ SHAPES = {
     "full_causal_d64": W_(d=64, heads=2, kv_heads=1, n=700, nq=700, W=16, topk=8),
     "batch2_topk1": W_(batch=2, heads=4, kv_heads=2, n=1200, nq=100, W=100, topk=1),
     "topk_exceeds_R": W_(heads=1, kv_heads=1, n=400, nq=400, W=64, topk=100),
+    # 4096 query vectors or more: the merge and attend stage runs one workgroup of 64 threads
+    # (topk <= 32) or 128 threads per vector instead of 1024.
+    "many_vectors_wave64": W_(d=64, heads=8, kv_heads=2, n=1024, nq=560, W=64, topk=16),
+    "many_vectors_wave128": W_(heads=8, kv_heads=8, n=1024, nq=520, W=64, topk=64),
 }
 
 
