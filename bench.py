@@ -220,7 +220,9 @@ def main():
     launches, score_ms = prof.get(score_name, (0, 0.0))
     score_avg_s = score_ms / max(1, launches) / 1e3
     achieved = score_bytes / score_avg_s / 1e9 if launches else None
-    traffic = recorded_traffic(w.name)
+    # The recorded counters are those of score_keys without the mass epilogue: other kernels
+    # (the mass variant, score_topk on the chunked path) report no traffic.
+    traffic = recorded_traffic(w.name) if score_name == "score_keys" and not args.mass else None
     if "mfma_bound" not in prof and not args.dense:
         roofline = {
             "kernel": "score_keys (score stage)" if score_name == "score_keys" else "score_topk (score stage)",
