@@ -111,8 +111,8 @@ int ca_condensate_attention_mass_ex(const ca_params *p, const void *q, const voi
 /* Dense causal attention, the baseline of the pages' speed comparison (section 5.1.2, against
  * full attention): for each query, softmax of q . k_j / sqrt(d) over every j <= i, times V, on
  * the matrix cores (bf16 products, fp32 accumulation; the weights enter the V product as bf16).
- * W and topk of p are validated but not used. bfloat16 only (else CA_ERR_UNSUPPORTED); no
- * workspace; asynchronous on `stream`. */
+ * W and topk of p are validated but not used. bfloat16 only, with n * d * 2 bytes per KV head at
+ * most 4 GiB (else CA_ERR_UNSUPPORTED); no workspace; asynchronous on `stream`. */
 int ca_dense_attention_ex(const ca_params *p, const void *q, const void *k, const void *v,
                           float *out, void *stream);
 

@@ -353,6 +353,8 @@ int ca_dense_attention_ex(const ca_params *p, const void *q, const void *k, cons
     if (rc != CA_OK) return rc;
     if (pl.dtype != CA_BF16)
         return fail(CA_ERR_UNSUPPORTED, "dense attention runs on the matrix cores: bfloat16 inputs only");
+    if (pl.n * (int64_t)pl.d * 2 > ((int64_t)1 << 32))
+        return fail(CA_ERR_UNSUPPORTED, "dense attention addresses a KV head's rows in 32 bits: n * d * 2 bytes must be at most 4 GiB");
     if (!q || !k || !v || !out) return fail(CA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
     hipStream_t s = static_cast<hipStream_t>(stream);
     ProfScope pd(K_DENSE, s);

@@ -504,6 +504,9 @@ __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__r
 // product as bf16 (relative error 2^-9 per weight), accumulation is fp32. Output per query
 // vector: m, l and the weighted sum of V rows, the partial the finish kernel merges.
 constexpr int kWinTile = 64;
+// Query blocks of 16 per wavefront in the dense kernel, per d.
+constexpr int kDenseQB128 = 2;
+constexpr int kDenseQB64 = 4;
 constexpr int kVtStride = kWinTile + 4;  // bf16 per transposed V row (padded against bank conflicts)
 
 struct WinArgs {
@@ -511,8 +514,8 @@ struct WinArgs {
     int Hq, Hkv, g, W;
     uint32_t nvec, wg_per_unit, nwg;
     float scale_log2e;
-    float *win;  // [nqv][D + 2] partials, or null
-    float *out;  // [nqv][D] normalised outputs (with W >= n: dense causal attention), or null
+    float *win;  // [nqv][D + 2] partials (window kernel)
+    float *out;  // [nqv][D] normalised outputs (dense kernel)
 };
 
 // K and V rows base..base+63 of a tile (clamped to n - 1): 16-byte chunks, NCH per thread.
@@ -525,12 +528,15 @@ __device__ __forceinline__ void win_tile_load(win_u32x4 (&pk)[kWinTile * D / 8 /
                                               const __bf16 *__restrict__ kb, const __bf16 *__restrict__ vb,
                                               int base, int nlast, int tid) {
     constexpr int CPR = D / 8, NCH = kWinTile * CPR / 256;
+    // (Byte offsets from the KV head's first row in 32 bits: the plan keeps a head below 4 GiB.)
+    const char *kc = reinterpret_cast<const char *>(kb), *vc = reinterpret_cast<const char *>(vb);
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
         const int cid = tid + 256 * u, row = cid / CPR, c = cid % CPR;
         const int j = base + row < nlast ? base + row : nlast;
-        pk[u] = reinterpret_cast<const win_u32x4 *>(kb + (size_t)j * D)[c];
-        pv[u] = reinterpret_cast<const win_u32x4 *>(vb + (size_t)j * D)[c];
+        const uint32_t off = (uint32_t)j * (uint32_t)(D * sizeof(__bf16)) + (uint32_t)c * 16u;
+        pk[u] = *reinterpret_cast<const win_u32x4 *>(kc + off);
+        pv[u] = *reinterpret_cast<const win_u32x4 *>(vc + off);
     }
 }
 // The tile into LDS: K with swizzled chunks, V transposed ([d][row], bf16 bits).
@@ -675,22 +681,183 @@ __global__ __launch_bounds__(256) void mfma_window_kernel(const __bf16 *__restri
         __syncthreads();
     }
     lsum = __uint_as_float(quad_sum_f32_bits(__float_as_uint(lsum)));
-    if (valid && a.out) {
-        // The softmax over the rows seen, times V: with a window of n or more rows, dense causal
-        // attention (the denominator of the method's speedup).
-        float *out = a.out + (size_t)qv * D;
-        const float inv = 1.f / lsum;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) out[db * 16 + 4 * grp + r] = o[db][r] * inv;
-    } else if (valid) {
+    if (valid) {
         float *out = a.win + (size_t)qv * (D + 2);
         if (grp == 0) { out[0] = m; out[1] = lsum; }
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) out[2 + db * 16 + 4 * grp + r] = o[db][r];
+    }
+}
+
+// Dense causal attention (every j <= i), the denominator of the method's speedup (pages of "The
+// Condensate Theorem", metaphor-xennon blog: section 2.1, softmax(S) V over all causal
+// positions; section 5.1.2 compares against it). The layout of the window kernel, for long rows:
+// each wavefront holds QB blocks of 16 query vectors, so every K and V^T fragment read from LDS
+// feeds QB products; tiles wholly below the wavefront's first query position take no mask; the
+// running output is rescaled only when some lane's maximum moved; the workgroups with the most
+// rows (the last query positions) are dispatched first.
+template <int D, int QB>
+__global__ __launch_bounds__(256) void mfma_dense_kernel(const __bf16 *__restrict__ q,
+                                                         const __bf16 *__restrict__ k,
+                                                         const __bf16 *__restrict__ v, WinArgs a) {
+    constexpr int KS = D / 32, CPR = D / 8, NCH = kWinTile * CPR / 256, DB = D / 16;
+    constexpr int QW = 16 * QB, ROWS = 4 * QW;
+    static_assert(NCH * 256 == kWinTile * CPR, "tile");
+    __shared__ uint4 kt[kWinTile * CPR];
+    __shared__ uint16_t vt[D * kVtStride];  // bf16 bits
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+    const uint32_t bid = blockIdx.x, xcd = bid % kXcds;
+    const uint32_t per = a.nwg / kXcds, rem = a.nwg % kXcds;
+    const uint32_t L = xcd * per + (xcd < rem ? xcd : rem) + bid / kXcds;
+    const uint32_t bk = L / a.wg_per_unit;
+    const uint32_t part = a.wg_per_unit - 1 - (L - bk * a.wg_per_unit);  // most rows first
+    const uint32_t b = bk / (uint32_t)a.Hkv, kvh = bk - b * (uint32_t)a.Hkv, g = (uint32_t)a.g;
+    auto pos_of = [&](uint32_t idx) -> int { return (int)(a.n - a.nq + idx / g); };
+    // This lane's query vectors (one per query block).
+    bool valid[QB];
+    uint32_t qv[QB];
+    int qi[QB];
+    bf16x8_t qf[QB][KS];
+    int i_lo = INT32_MAX, i_hi = 0;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const uint32_t idx = part * ROWS + wave * QW + qb * 16 + col;
+        valid[qb] = idx < a.nvec;
+        const uint32_t idxc = valid[qb] ? idx : a.nvec - 1;
+        qv[qb] = (b * (uint32_t)a.Hq + kvh * g + idxc % g) * (uint32_t)a.nq + idxc / g;
+        qi[qb] = pos_of(idxc);
+        i_lo = qi[qb] < i_lo ? qi[qb] : i_lo;
+        i_hi = qi[qb] > i_hi ? qi[qb] : i_hi;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[qb][ks] = __builtin_bit_cast(bf16x8_t, reinterpret_cast<const uint4 *>(q + (size_t)qv[qb] * D)[ks * 4 + grp]);
+    }
+    i_lo = (int)wave_min_u32_dpp((uint32_t)i_lo);
+    i_hi = (int)wave_max_u32_dpp((uint32_t)i_hi);
+    // Rows of the workgroup: 0 .. the position of its last vector.
+    const uint32_t last = part * ROWS + ROWS - 1 < a.nvec ? part * ROWS + ROWS - 1 : a.nvec - 1;
+    const int ntiles = pos_of(last) / kWinTile + 1;
+    const __bf16 *kb = k + (size_t)bk * (size_t)a.n * D, *vb = v + (size_t)bk * (size_t)a.n * D;
+    const int nlast = (int)a.n - 1;
+    const float sc_l2 = a.scale_log2e;
+
+    float m[QB], lsum[QB];  // running maximum of the raw scores, weight sum (this lane's rows)
+    f32x4_t o[QB][DB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m[qb] = -INFINITY;
+        lsum[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[qb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    win_u32x4 pk[NCH], pv[NCH];
+    win_tile_load<D>(pk, pv, kb, vb, 0, nlast, tid);
+    win_tile_store<D>(pk, pv, kt, vt, tid);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) win_tile_load<D>(pk, pv, kb, vb, (t + 1) * kWinTile, nlast, tid);
+        const int base = t * kWinTile;
+        if (base <= i_hi) {  // wavefront-uniform: some query of the wavefront sees these rows
+            const bool full = base + kWinTile - 1 <= i_lo;
+            f32x4_t sc[4][QB];
+#pragma unroll
+            for (int kbk = 0; kbk < 4; ++kbk) {
+                bf16x8_t af[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    af[ks] = __builtin_bit_cast(bf16x8_t, kt[chunk_at<D>(kbk * 16 + col, ks * 4 + grp)]);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    sc[kbk][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        sc[kbk][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], qf[qb][ks], sc[kbk][qb], 0, 0, 0);
+                }
+            }
+            if (!full) {  // rows past the query's position leave the softmax
+#pragma unroll
+                for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            sc[kbk][qb][r] = base + kbk * 16 + 4 * grp + r <= qi[qb] ? sc[kbk][qb][r] : -INFINITY;
+            }
+            bool moved = false;
+            float alpha[QB];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                float mt = fmaxf(fmaxf(fmaxf(sc[0][qb][0], sc[0][qb][1]), fmaxf(sc[0][qb][2], sc[0][qb][3])),
+                                 fmaxf(fmaxf(sc[1][qb][0], sc[1][qb][1]), fmaxf(sc[1][qb][2], sc[1][qb][3])));
+                mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(sc[2][qb][0], sc[2][qb][1]), fmaxf(sc[2][qb][2], sc[2][qb][3])),
+                                     fmaxf(fmaxf(sc[3][qb][0], sc[3][qb][1]), fmaxf(sc[3][qb][2], sc[3][qb][3]))));
+                const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+                mt = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+                const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+                mt = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+                const float mn = fmaxf(m[qb], mt);  // finite: row 0 is in every tile 0
+                alpha[qb] = mn > m[qb] ? __builtin_amdgcn_exp2f((m[qb] - mn) * sc_l2) : 1.f;
+                moved = moved || mn > m[qb];
+                m[qb] = mn;
+            }
+            if (__ballot(moved) != 0ull) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    lsum[qb] *= alpha[qb];
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) o[qb][db] *= alpha[qb];
+                }
+            }
+            // Weights exp2((s - m) * scale) as bf16, blocks (0, 1) and (2, 3) forming the B
+            // operand of the two 32-row steps of O^T += V^T P^T. (v_exp_f32 itself: weights
+            // below 2^-126 of the largest are dropped, the rest keep its relative error.)
+            bf16x8_t pb[2][QB];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float mb = m[qb] * sc_l2;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * h2][qb][r], sc_l2, -mb));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * h2 + 1][qb][r], sc_l2, -mb));
+                        lsum[qb] += p0 + p1;
+                        pb[h2][qb][r] = (__bf16)p0;
+                        pb[h2][qb][4 + r] = (__bf16)p1;
+                    }
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const uint16_t *vr = vt + (db * 16 + col) * kVtStride + h2 * 32 + 4 * grp;
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
+                    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[h2][qb], o[qb][db], 0, 0, 0);
+                }
+        }
+        __syncthreads();
+        if (t + 1 < ntiles) win_tile_store<D>(pk, pv, kt, vt, tid);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l = __uint_as_float(quad_sum_f32_bits(__float_as_uint(lsum[qb])));
+        if (valid[qb]) {
+            float *out = a.out + (size_t)qv[qb] * D;
+            const float inv = 1.f / l;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[db * 16 + 4 * grp + r] = o[qb][db][r] * inv;
+        }
     }
 }
 
@@ -753,15 +920,16 @@ hipError_t launch_dense_attention(const Plan &pl, const void *q, const void *k, 
     a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g;
     a.W = (int)pl.n;  // the window covers every causal position: C_i = {0..i}
     a.nvec = (uint32_t)(pl.g * pl.nq);
-    a.wg_per_unit = (a.nvec + 63) / 64;
+    const uint32_t rows = 64 * (pl.d == 128 ? kDenseQB128 : kDenseQB64);
+    a.wg_per_unit = (a.nvec + rows - 1) / rows;
     a.nwg = (uint32_t)(pl.B * pl.Hkv) * a.wg_per_unit;
     a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
     a.win = nullptr;
     a.out = out;
     const __bf16 *qt = static_cast<const __bf16 *>(q), *kt = static_cast<const __bf16 *>(k),
                  *vt = static_cast<const __bf16 *>(v);
-    if (pl.d == 128) hipLaunchKernelGGL((mfma_window_kernel<128>), dim3(a.nwg), dim3(256), 0, s, qt, kt, vt, a);
-    else hipLaunchKernelGGL((mfma_window_kernel<64>), dim3(a.nwg), dim3(256), 0, s, qt, kt, vt, a);
+    if (pl.d == 128) hipLaunchKernelGGL((mfma_dense_kernel<128, kDenseQB128>), dim3(a.nwg), dim3(256), 0, s, qt, kt, vt, a);
+    else hipLaunchKernelGGL((mfma_dense_kernel<64, kDenseQB64>), dim3(a.nwg), dim3(256), 0, s, qt, kt, vt, a);
     return hipGetLastError();
 }
 
