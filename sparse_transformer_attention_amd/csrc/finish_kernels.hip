@@ -491,7 +491,7 @@ __device__ __forceinline__ void rescore_tiles(const T *__restrict__ q, const T *
 // a window of up to 299 rows of 256 bytes in one round, 16 x 4 x 1 or 4 x 4 x 4 a top-64 part).
 constexpr int kWindowU = 5;
 template <int NT>
-constexpr int kTopU = NT >= 1024 ? 1 : 4;  // 256 threads: 4 x 4 x 4 rows, still one round (128: two)
+constexpr int kTopU = NT >= 1024 ? 1 : 4;  // 256 threads: 4 x 4 x 4 rows, still one round (fewer: more)
 
 template <typename T, int D, int NT, bool ATTEND, bool TILES>
 __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, const T *__restrict__ k,
@@ -723,9 +723,9 @@ FinishArgs finish_args(const Plan &pl, const void *ws) {
     return a;
 }
 
-// Few query vectors: 1024 threads each (latency); many: 256, or 128 on the MFMA path, whose
-// candidate lists hold at most 256 keys and whose window partials are computed already (more
-// query vectors in flight per CU).
+// Few query vectors: 1024 threads each (latency); many: 256, or on the MFMA path, whose
+// candidate lists hold at most 256 keys and whose window partials are computed already, 128
+// (64 when topk <= 32): more query vectors in flight per CU.
 constexpr int64_t kWideBelow = 4096;
 
 template <typename T, int D, bool ATTEND>
