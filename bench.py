@@ -158,6 +158,21 @@ def main():
     torch.cuda.synchronize()
     ms_per_step_profiled = (time.perf_counter() - t1) * 1e3 / args.steps
     prof = ca.profile_stop()
+    # Per-step spread: a third pass with an event pair around every step on the stream the
+    # library launches on (torch's current stream), for the median and the 10th / 90th
+    # percentiles of the step's GPU time.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s, (e0, e1) in enumerate(evs):
+        e0.record()
+        step(s)
+        e1.record()
+    torch.cuda.synchronize()
+    per_step_us = np.sort(np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]))
+    step_spread = {"median": float(np.median(per_step_us)),
+                   "p10": float(np.percentile(per_step_us, 10)),
+                   "p90": float(np.percentile(per_step_us, 90))}
 
     # Algorithmic bytes. score_select reads the key rows of the candidate range once per KV
     # head plus the queries; the whole step reads all of K, the distinct V rows of the sets,
@@ -258,6 +273,7 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "gpu_ms_per_step": gpu_ms / args.steps,
         "ms_per_step_profiled": ms_per_step_profiled,
+        "step_us_events": step_spread,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None,
