@@ -282,44 +282,57 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         qc, kc, vc = q.cpu(), x["k"].cpu(), x["v"].cpu()
-        reps, t_cpu = 0, 0.0
-        if nqv * w.n <= (1 << 28):
-            # Whole steps.
-            while t_cpu < args.cpu_seconds:
-                t1 = time.perf_counter()
-                oracle.condensate(qc, kc, vc, w.W, w.topk)
-                t_cpu += time.perf_counter() - t1
-                reps += 1
-            vectors = reps * nqv
-            sample = (f"{reps} whole steps of the same workload ({nqv} query vectors each over "
-                      f"{w.n} keys), float64, {t_cpu:.1f} s")
-        else:
-            # A whole step is far beyond the time budget: blocks of m consecutive query positions
-            # at random places, all heads, each block solved as the last m positions of the keys
-            # up to its last one (the same computation as inside a whole step).
-            m = min(16, w.nq)
-            rng = np.random.default_rng(seed)
-            vectors = 0
-            while t_cpu < args.cpu_seconds:
-                r0 = int(rng.integers(0, w.nq - m + 1))
-                last = w.n - w.nq + r0 + m - 1
-                qb = qc[:, :, r0:r0 + m].contiguous()
-                kb, vb = kc[:, :, :last + 1].contiguous(), vc[:, :, :last + 1].contiguous()
-                t1 = time.perf_counter()
-                oracle.condensate(qb, kb, vb, w.W, w.topk)
-                t_cpu += time.perf_counter() - t1
-                vectors += w.batch * w.heads * m
-                reps += 1
-            sample = (f"{reps} blocks of {m} consecutive query positions x {w.batch * w.heads} "
-                      f"query heads at random positions of the workload ({vectors} query vectors, "
-                      f"each over its causal keys), float64, {t_cpu:.1f} s")
+
+        def oracle_rate(threads, seconds):
+            """Query vectors per second of the oracle on `threads` threads (0: all), over about
+            `seconds` of CPU work on the same workload, and what the sample was."""
+            reps, t_cpu, vectors = 0, 0.0, 0
+            if nqv * w.n <= (1 << 28):
+                # Whole steps.
+                while t_cpu < seconds:
+                    t1 = time.perf_counter()
+                    oracle.condensate(qc, kc, vc, w.W, w.topk, threads)
+                    t_cpu += time.perf_counter() - t1
+                    reps += 1
+                vectors = reps * nqv
+                sample = (f"{reps} whole steps of the same workload ({nqv} query vectors each "
+                          f"over {w.n} keys), float64, {t_cpu:.1f} s")
+            else:
+                # A whole step is far beyond the time budget: blocks of m consecutive query
+                # positions at random places, all heads, each block solved as the last m
+                # positions of the keys up to its last one (the same computation as inside a
+                # whole step).
+                m = min(16, w.nq)
+                rng = np.random.default_rng(seed)
+                while t_cpu < seconds:
+                    r0 = int(rng.integers(0, w.nq - m + 1))
+                    last = w.n - w.nq + r0 + m - 1
+                    qb = qc[:, :, r0:r0 + m].contiguous()
+                    kb, vb = kc[:, :, :last + 1].contiguous(), vc[:, :, :last + 1].contiguous()
+                    t1 = time.perf_counter()
+                    oracle.condensate(qb, kb, vb, w.W, w.topk, threads)
+                    t_cpu += time.perf_counter() - t1
+                    vectors += w.batch * w.heads * m
+                    reps += 1
+                sample = (f"{reps} blocks of {m} consecutive query positions x "
+                          f"{w.batch * w.heads} query heads at random positions of the workload "
+                          f"({vectors} query vectors, each over its causal keys), float64, "
+                          f"{t_cpu:.1f} s")
+            return vectors / t_cpu, sample
+
+        value_all, sample = oracle_rate(0, args.cpu_seconds)
+        cores = oracle.threads_used()
+        # (Last: a thread count set for one call stays set for the process.)
+        value_one, sample_one = oracle_rate(1, max(2.0, args.cpu_seconds / 4))
         record["cpu_baseline"] = {
-            "value": vectors / t_cpu,
+            "value": value_all,
             "unit": "query vectors/s",
-            "cores": oracle.threads_used(),
+            "cores": cores,
             "kind": "oracle",
             "sample": sample,
             "cpu": cpu_info(),
+            "single_thread_value": value_one,
+            "single_thread_sample": sample_one,
         }
     print(json.dumps(record), flush=True)
 
