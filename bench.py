@@ -99,10 +99,18 @@ def main():
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
         dst = torch.empty_like(src)
-        for _ in range(10):
-            torch.mul(src, 1.0, out=dst)   # one elementwise kernel: reads 1 GiB, writes 1 GiB
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.mul(src, 1.0, out=dst)   # one elementwise kernel: reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": 1 << 30, "launches": 10}))
+        e0.record()
+        for _ in range(9):
+            torch.mul(src, 1.0, out=dst)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_s = e0.elapsed_time(e1) / 1e3 / 9
+        # (Context for the achievable HBM bandwidth: GB/s moved by this plain copy.)
+        print(json.dumps({"calibrate_copy_bytes": 1 << 30, "launches": 10,
+                          "copy_gbps": 2 * (1 << 30) / copy_s / 1e9}))
         return
 
     import numpy as np
