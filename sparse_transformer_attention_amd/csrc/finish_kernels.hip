@@ -488,10 +488,9 @@ __device__ __forceinline__ void rescore_tiles(const T *__restrict__ q, const T *
 
 // Rows per lane in flight in the attend phase (rows past the set's end are loaded as clamped
 // duplicates, so these match the common sizes: 15 wavefronts x 4 rows x 5 cover the anchor and
-// a window of up to 299 rows of 256 bytes in one round, 16 x 4 x 1 or 4 x 4 x 4 a top-64 part).
+// a window of up to 299 rows of 256 bytes in one round, 4 x 4 x 4 a top-64 part).
 constexpr int kWindowU = 5;
-template <int NT>
-constexpr int kTopU = NT >= 1024 ? 1 : 4;  // 256 threads: 4 x 4 x 4 rows, still one round (fewer: more)
+constexpr int kTopU = 4;  // rows per lane in flight in the top-k part
 
 template <typename T, int D, int NT, bool ATTEND, bool TILES>
 __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, const T *__restrict__ k,
@@ -524,6 +523,12 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     const int64_t rl = i - a.W;
     const int64_t n_r = rl >= 1 ? rl : 0;
     const int kp = (int)(a.topk < n_r ? a.topk : n_r);
+    // Wavefronts of the top-k part: as many as one round of kTopU rows per lane needs (the
+    // top-k' positions spread over fewer partials), all of them in narrow workgroups.
+    constexpr int kTopRowsPerWave = AttendShape<D, T>::RPW * kTopU;
+    const int top_waves = NT >= 1024 ? ((kp + kTopRowsPerWave - 1) / kTopRowsPerWave < NW
+                                            ? (kp + kTopRowsPerWave - 1) / kTopRowsPerWave : NW)
+                                     : NW;
     // js layout: [0 if the anchor is separate][top-k' ascending][window ascending]
     const int base = wlo > 0 ? 1 : 0;
     const int wcount = (int)(i - wlo + 1);
@@ -591,7 +596,8 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
         if (kp > 0) {
             const int32_t *top = js + base;
             auto row_at = [&](int c) -> size_t { return (size_t)(uint32_t)top[c]; };
-            wave_partial<D, T, kTopU<NT>>(qs, kb, vb, row_at, kp, wave, NW, a.scale_log2e, part, NW + wave);
+            if (wave < top_waves)
+                wave_partial<D, T, kTopU>(qs, kb, vb, row_at, kp, wave, top_waves, a.scale_log2e, part, NW + wave);
         }
         // (The index row's stores need not complete before the merge: LDS only.)
         lds_barrier();
@@ -627,7 +633,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
                 };
                 float mw, lw, mt = -INFINITY, lt = 0.f;
                 range(p0, NW, mw, lw);
-                if (kp > 0) range(NW, 2 * NW, mt, lt);
+                if (kp > 0) range(NW, NW + top_waves, mt, lt);
                 using S = AttendShape<D, T>;
                 const uint4 k0 = reinterpret_cast<const uint4 *>(kb)[lane % S::LPR];
                 const float s0 = row_sum<S::LPR>(dot16(k0, qs, 0.f, T()));
@@ -647,7 +653,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
                 }
             }
         }
-        merge_partials<NT, D>(part, p0, kp > 0 ? 2 * NW : NW, a.scale_log2e, out + qv * D);
+        merge_partials<NT, D>(part, p0, kp > 0 ? NW + top_waves : NW, a.scale_log2e, out + qv * D);
     }
 }
 
