@@ -523,8 +523,8 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     const int64_t rl = i - a.W;
     const int64_t n_r = rl >= 1 ? rl : 0;
     const int kp = (int)(a.topk < n_r ? a.topk : n_r);
-    // Wavefronts of the top-k part: as many as one round of kTopU rows per lane needs (the
-    // top-k' positions spread over fewer partials), all of them in narrow workgroups.
+    // Wavefronts of the top-k part: in 1024-thread workgroups as many as one round of kTopU
+    // rows per lane needs (fewer partials to merge); in narrower ones every wavefront.
     constexpr int kTopRowsPerWave = AttendShape<D, T>::RPW * kTopU;
     const int top_waves = NT >= 1024 ? ((kp + kTopRowsPerWave - 1) / kTopRowsPerWave < NW
                                             ? (kp + kTopRowsPerWave - 1) / kTopRowsPerWave : NW)
