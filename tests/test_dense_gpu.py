@@ -32,6 +32,9 @@ CASES = {
     "prefill_mha_d128_ragged": W_(),
     "prefill_gqa4_d64": W_(d=64, heads=8, kv_heads=2, n=900, nq=900),
     "decode_gqa_b2": W_(batch=2, heads=8, kv_heads=2, n=3000, nq=1),
+    # 8 query heads per KV head at d = 128, batch 2: several workgroups per KV head, the last
+    # one ragged (dispatched first: it has the most rows).
+    "prefill_gqa8_d128_b2": W_(batch=2, heads=16, kv_heads=2, n=1300, nq=170),
 }
 
 

@@ -44,6 +44,8 @@ SHAPES = {
     # (topk <= 32) or 128 threads per vector instead of 1024.
     "many_vectors_wave64": W_(d=64, heads=8, kv_heads=2, n=1024, nq=560, W=64, topk=16),
     "many_vectors_wave128": W_(heads=8, kv_heads=8, n=1024, nq=520, W=64, topk=64),
+    # 8 query heads per KV head, batch 2: the vectors of a KV head interleave heads and rows.
+    "gqa8_b2_d128": W_(batch=2, heads=16, kv_heads=2, n=1800, nq=90, W=40, topk=24),
 }
 
 
