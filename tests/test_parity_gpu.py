@@ -188,10 +188,15 @@ def test_clustered_best_rows(dtype, length, topk):
     assert_outputs(out, oracle.restricted(x["q"], x["k"], x["v"], idx), w.torch_dtype)
 
 
-def test_select_stage_alone_matches_full_call():
-    w = SMALL["prefill_bf16_ragged"]
+@pytest.mark.parametrize("name", ["prefill_bf16_ragged", "mfma_wave64", "mfma_wave128"])
+def test_select_stage_alone_matches_full_call(name):
+    # (The last two: over 4096 bf16 query vectors, the MFMA path with its 64- and 128-thread
+    # merge workgroups, here without the attend part.)
+    w = {"prefill_bf16_ragged": SMALL["prefill_bf16_ragged"],
+         "mfma_wave64": W_(d=64, heads=8, kv_heads=2, n=1024, nq=560, W=64, topk=16),
+         "mfma_wave128": W_(heads=8, kv_heads=8, n=1024, nq=520, W=64, topk=64)}[name]
     x = synth.make_inputs(w, seed=4)
-    announce("select alone")
+    announce(f"select alone {name}")
     q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
     p = ca.params_for(q, k, w.W, w.topk)
     ws = ca.alloc_workspace(p)
