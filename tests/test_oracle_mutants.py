@@ -26,6 +26,10 @@ MUTANTS = {
     "no_normalisation": ("for (int64_t t = 0; t < p->d; ++t) o[t] /= l;", "(void)l;"),
     "bf16_widen_wrong": ("<< 16;", "<< 15;"),
     "anchor_dropped": ("w->member[0] = 1;", "w->member[0] = 0;"),
+    "band_signed_halved": ("if (fabs(w->s[j]) > mabs) mabs = fabs(w->s[j]);",
+                           "if (w->s[j] > mabs) mabs = w->s[j] * 0.5;"),
+    "band_signed": ("if (fabs(w->s[j]) > mabs) mabs = fabs(w->s[j]);",
+                    "if (w->s[j] > mabs) mabs = w->s[j];"),
     "k_minus_one": ("const int64_t kp = p->topk < n_r ? p->topk : n_r;",
                     "const int64_t kp = p->topk < n_r ? (p->topk > 0 ? p->topk - 1 : 0) : n_r;"),
 }

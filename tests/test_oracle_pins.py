@@ -137,6 +137,26 @@ def test_scores_match_library_matmul():
         np.testing.assert_allclose(s, ref[b, h, r, : i + 1].numpy(), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("case", CASES)
+def test_tie_band_width_is_largest_absolute_score(case):
+    """The half-width of the tie band around the k-th selected score (the Top-k of section
+    2.2.3; tau_min of the section 3.2.1 lemma) is 1e-5 * max_{j <= i} |s_ij|. The oracle's
+    diag[1] must be that maximum, taken over the causal positions only, against torch's
+    float64 matmul: a signed or halved maximum would widen or narrow what parity accepts."""
+    w, x = make(**case)
+    _, _, diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    S = scores64(w, x)
+    from_negative = 0
+    for b, h, r in itertools.product(range(w.batch), range(w.heads), range(w.nq)):
+        i = w.n - w.nq + r
+        s = S[b, h, r, : i + 1]
+        want = s.abs().max().item()
+        assert abs(diag[b, h, r, 1] - want) <= 1e-12, (b, h, r, diag[b, h, r, 1], want)
+        from_negative += int(-s.min().item() > s.max().item())
+    # The inputs exercise the absolute value: in some row the largest |s| is a negative score.
+    assert from_negative > 0
+
+
 def _beats(sa, a, sb, b):
     return sa > sb or (sa == sb and a < b)
 
