@@ -55,12 +55,17 @@ def lib():
         L = ctypes.CDLL(path)
         P = ctypes.POINTER(Problem)
         vp = ctypes.c_void_p
+        i64 = ctypes.c_int64
         L.oracle_condensate.argtypes = [P, vp, vp, vp, vp, vp, vp]
-        L.oracle_restricted.argtypes = [P, vp, vp, vp, vp, ctypes.c_int64, vp]
+        L.oracle_condensate_rows.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp]
+        L.oracle_restricted.argtypes = [P, vp, vp, vp, vp, i64, vp]
+        L.oracle_restricted_rows.argtypes = [P, vp, vp, vp, vp, i64, vp, i64, vp]
         L.oracle_full.argtypes = [P, vp, vp, vp, vp]
+        L.oracle_full_rows.argtypes = [P, vp, vp, vp, vp, i64, vp]
         L.oracle_scores.argtypes = [P, vp, vp, ctypes.c_int64, vp]
         L.oracle_threads.argtypes = [ctypes.c_int32]
-        for f in (L.oracle_condensate, L.oracle_restricted, L.oracle_full, L.oracle_scores,
+        for f in (L.oracle_condensate, L.oracle_condensate_rows, L.oracle_restricted,
+                  L.oracle_restricted_rows, L.oracle_full, L.oracle_full_rows, L.oracle_scores,
                   L.oracle_threads):
             f.restype = ctypes.c_int
         _lib = L
@@ -94,42 +99,76 @@ def _check(rc: int, what: str):
         raise RuntimeError(f"{what} failed with code {rc}")
 
 
-def condensate(q, k, v, W: int, topk: int, threads: int = 0):
+def flat_rows(q, rows) -> np.ndarray:
+    """Flat query indices b*Hq*nq + h*nq + r of (b, h, r) triples (int64, in the given order)."""
+    B, Hq, nq, _ = q.shape
+    a = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    bad = (a < 0).any() or (a[:, 0] >= B).any() or (a[:, 1] >= Hq).any() or (a[:, 2] >= nq).any()
+    if bad:
+        raise ValueError("row outside the problem")
+    return np.ascontiguousarray((a[:, 0] * Hq + a[:, 1]) * nq + a[:, 2])
+
+
+def condensate(q, k, v, W: int, topk: int, threads: int = 0, rows=None):
     """Full method. Returns (idx int32 [B][Hq][nq][1+W+topk], out float64 [B][Hq][nq][d],
     diag float64 [B][Hq][nq][8] = tau, max|s|, eps, |C|, k', and the full-softmax mass of
-    position 0, of the window without 0, of the top-k positions."""
+    position 0, of the window without 0, of the top-k positions).
+    With rows (a list of (b, h, r)), only those queries: results [len(rows)][...]."""
     q, k, v = _prep(q), _prep(k), _prep(v)
     p = problem(q, k, W, topk, threads)
     B, Hq, nq, d = q.shape
-    idx = np.empty((B, Hq, nq, 1 + W + topk), dtype=np.int32)
-    out = np.empty((B, Hq, nq, d), dtype=np.float64)
-    diag = np.empty((B, Hq, nq, N_DIAG), dtype=np.float64)
-    _check(lib().oracle_condensate(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
-                                   _ptr(out), _ptr(diag)), "oracle_condensate")
+    lead = (B, Hq, nq) if rows is None else (len(rows),)
+    idx = np.empty(lead + (1 + W + topk,), dtype=np.int32)
+    out = np.empty(lead + (d,), dtype=np.float64)
+    diag = np.empty(lead + (N_DIAG,), dtype=np.float64)
+    if rows is None:
+        _check(lib().oracle_condensate(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                       _ptr(out), _ptr(diag)), "oracle_condensate")
+    else:
+        fr = flat_rows(q, rows)
+        _check(lib().oracle_condensate_rows(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fr),
+                                            len(fr), _ptr(idx), _ptr(out), _ptr(diag)),
+               "oracle_condensate_rows")
     return idx, out, diag
 
 
-def restricted(q, k, v, idx, threads: int = 0):
-    """Softmax over each supplied set (rows of idx, -1 padded), times V. float64 [B][Hq][nq][d]."""
+def restricted(q, k, v, idx, threads: int = 0, rows=None):
+    """Softmax over each supplied set (rows of idx, -1 padded), times V. float64 [B][Hq][nq][d].
+    With rows (a list of (b, h, r)), idx is [len(rows)][cap] and so is the result."""
     q, k, v = _prep(q), _prep(k), _prep(v)
     idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
     B, Hq, nq, d = q.shape
-    if idx.shape[:3] != (B, Hq, nq):
-        raise ValueError("idx shape disagrees with q")
     p = problem(q, k, 1, 0, threads)
-    out = np.empty((B, Hq, nq, d), dtype=np.float64)
-    _check(lib().oracle_restricted(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
-                                   idx.shape[3], _ptr(out)), "oracle_restricted")
+    if rows is None:
+        if idx.shape[:3] != (B, Hq, nq):
+            raise ValueError("idx shape disagrees with q")
+        out = np.empty((B, Hq, nq, d), dtype=np.float64)
+        _check(lib().oracle_restricted(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                       idx.shape[3], _ptr(out)), "oracle_restricted")
+        return out
+    fr = flat_rows(q, rows)
+    if idx.ndim != 2 or idx.shape[0] != len(fr):
+        raise ValueError("idx must be [len(rows)][cap]")
+    out = np.empty((len(fr), d), dtype=np.float64)
+    _check(lib().oracle_restricted_rows(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fr),
+                                        len(fr), _ptr(idx), idx.shape[1], _ptr(out)),
+           "oracle_restricted_rows")
     return out
 
 
-def full(q, k, v, threads: int = 0):
-    """Plain causal attention in float64: [B][Hq][nq][d]."""
+def full(q, k, v, threads: int = 0, rows=None):
+    """Plain causal attention in float64: [B][Hq][nq][d] (with rows: [len(rows)][d])."""
     q, k, v = _prep(q), _prep(k), _prep(v)
     p = problem(q, k, 1, 0, threads)
     B, Hq, nq, d = q.shape
-    out = np.empty((B, Hq, nq, d), dtype=np.float64)
-    _check(lib().oracle_full(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out)), "oracle_full")
+    if rows is None:
+        out = np.empty((B, Hq, nq, d), dtype=np.float64)
+        _check(lib().oracle_full(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out)), "oracle_full")
+        return out
+    fr = flat_rows(q, rows)
+    out = np.empty((len(fr), d), dtype=np.float64)
+    _check(lib().oracle_full_rows(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fr), len(fr),
+                                  _ptr(out)), "oracle_full_rows")
     return out
 
 

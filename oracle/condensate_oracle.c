@@ -239,6 +239,15 @@ static void set_threads(const oracle_problem *p)
 
 #define N_DIAG 8
 
+int oracle_condensate_rows(const oracle_problem *p, const void *q, const void *k, const void *v,
+                           const int64_t *rows, int64_t nrows, int32_t *out_idx, double *out,
+                           double *diag);
+int oracle_restricted_rows(const oracle_problem *p, const void *q, const void *k, const void *v,
+                           const int64_t *rows, int64_t nrows, const int32_t *idx,
+                           int64_t idx_stride, double *out);
+int oracle_full_rows(const oracle_problem *p, const void *q, const void *k, const void *v,
+                     const int64_t *rows, int64_t nrows, double *out);
+
 /* The whole method for every query of the problem.
  * out_idx: [batch][heads][nq][1+W+topk] int32; out: [batch][heads][nq][d] float64;
  * diag (may be NULL): [batch][heads][nq][8] float64 = {tau, max|s|, eps, |C|, k', mass of
@@ -246,10 +255,33 @@ static void set_threads(const oracle_problem *p)
 int oracle_condensate(const oracle_problem *p, const void *q, const void *k, const void *v,
                       int32_t *out_idx, double *out, double *diag)
 {
+    return oracle_condensate_rows(p, q, k, v, NULL, 0, out_idx, out, diag);
+}
+
+/* Checks a row list (NULL = every query, in flat order) and returns how many rows it names,
+ * or -1 if an entry is outside [0, nflat). */
+static int64_t row_count(const oracle_problem *p, const int64_t *rows, int64_t nrows)
+{
+    const int64_t nflat = p->batch * p->heads * p->nq;
+    if (!rows) return nflat;
+    if (nrows < 0) return -1;
+    for (int64_t t = 0; t < nrows; ++t)
+        if (rows[t] < 0 || rows[t] >= nflat) return -1;
+    return nrows;
+}
+
+/* The whole method for the listed queries only: rows[t] is a flat query index
+ * b*heads*nq + h*nq + r, and result t goes to out_idx[t][1+W+topk], out[t][d], diag[t][8].
+ * rows == NULL means every query in flat order (then nrows is ignored). */
+int oracle_condensate_rows(const oracle_problem *p, const void *q, const void *k, const void *v,
+                           const int64_t *rows, int64_t nrows, int32_t *out_idx, double *out,
+                           double *diag)
+{
     int rc = check_problem(p);
     if (rc) return rc;
     if (!q || !k || !v || !out_idx || !out) return OR_BAD_ARG;
-    const int64_t nflat = p->batch * p->heads * p->nq;
+    const int64_t count = row_count(p, rows, nrows);
+    if (count < 0) return OR_BAD_ARG;
     const int64_t cap = 1 + p->W + p->topk;
     int failed = 0;
     set_threads(p);
@@ -260,9 +292,11 @@ int oracle_condensate(const oracle_problem *p, const void *q, const void *k, con
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 1)
-            for (int64_t f = 0; f < nflat; ++f)
-                condensate_query(p, q, k, v, f, &w, out_idx + f * cap, out + f * p->d,
-                                 diag ? diag + f * N_DIAG : NULL);
+            for (int64_t t = 0; t < count; ++t) {
+                const int64_t f = rows ? rows[t] : t;
+                condensate_query(p, q, k, v, f, &w, out_idx + t * cap, out + t * p->d,
+                                 diag ? diag + t * N_DIAG : NULL);
+            }
         }
         scratch_free(&w);
     }
@@ -276,10 +310,20 @@ int oracle_condensate(const oracle_problem *p, const void *q, const void *k, con
 int oracle_restricted(const oracle_problem *p, const void *q, const void *k, const void *v,
                       const int32_t *idx, int64_t idx_stride, double *out)
 {
+    return oracle_restricted_rows(p, q, k, v, NULL, 0, idx, idx_stride, out);
+}
+
+/* Step 5 alone for the listed queries (rows as in oracle_condensate_rows): idx[t] is the set
+ * of query rows[t], out[t] its result. */
+int oracle_restricted_rows(const oracle_problem *p, const void *q, const void *k, const void *v,
+                           const int64_t *rows, int64_t nrows, const int32_t *idx,
+                           int64_t idx_stride, double *out)
+{
     int rc = check_problem(p);
     if (rc) return rc;
     if (!q || !k || !v || !idx || !out || idx_stride < 1) return OR_BAD_ARG;
-    const int64_t nflat = p->batch * p->heads * p->nq;
+    const int64_t count = row_count(p, rows, nrows);
+    if (count < 0) return OR_BAD_ARG;
     int bad = 0, failed = 0;
     set_threads(p);
 #pragma omp parallel reduction(| : bad, failed)
@@ -289,28 +333,29 @@ int oracle_restricted(const oracle_problem *p, const void *q, const void *k, con
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 1)
-            for (int64_t f = 0; f < nflat; ++f) {
+            for (int64_t t = 0; t < count; ++t) {
+                const int64_t f = rows ? rows[t] : t;
                 const query_loc L = locate(p, f);
                 memset(w.member, 0, (size_t)(L.i + 1));
                 int row_bad = 0;
                 for (int64_t c = 0; c < idx_stride; ++c) {
-                    int32_t j = idx[f * idx_stride + c];
+                    int32_t j = idx[t * idx_stride + c];
                     if (j < 0) continue;
                     if (j > L.i || w.member[j]) { row_bad = 1; break; }
                     w.member[j] = 1;
                 }
-                int64_t count = 0;
+                int64_t members = 0;
                 if (!row_bad) {
                     load_query(p, q, &L, w.qrow);
                     for (int64_t j = 0; j <= L.i; ++j)
                         if (w.member[j]) {
-                            w.list[count] = j;
-                            w.s_list[count] = score(p, w.qrow, k, L.kv_off, j);
-                            ++count;
+                            w.list[members] = j;
+                            w.s_list[members] = score(p, w.qrow, k, L.kv_off, j);
+                            ++members;
                         }
                 }
-                if (row_bad || count == 0) { bad = 1; continue; }
-                attend(p, w.list, count, w.s_list, v, L.kv_off, out + f * p->d);
+                if (row_bad || members == 0) { bad = 1; continue; }
+                attend(p, w.list, members, w.s_list, v, L.kv_off, out + t * p->d);
             }
         }
         scratch_free(&w);
@@ -322,10 +367,18 @@ int oracle_restricted(const oracle_problem *p, const void *q, const void *k, con
 /* Plain causal attention (step 5 with C = {0..i}) for every query. out: [..][d] float64. */
 int oracle_full(const oracle_problem *p, const void *q, const void *k, const void *v, double *out)
 {
+    return oracle_full_rows(p, q, k, v, NULL, 0, out);
+}
+
+/* Plain causal attention for the listed queries (rows as in oracle_condensate_rows). */
+int oracle_full_rows(const oracle_problem *p, const void *q, const void *k, const void *v,
+                     const int64_t *rows, int64_t nrows, double *out)
+{
     int rc = check_problem(p);
     if (rc) return rc;
     if (!q || !k || !v || !out) return OR_BAD_ARG;
-    const int64_t nflat = p->batch * p->heads * p->nq;
+    const int64_t count = row_count(p, rows, nrows);
+    if (count < 0) return OR_BAD_ARG;
     int failed = 0;
     set_threads(p);
 #pragma omp parallel reduction(| : failed)
@@ -335,14 +388,15 @@ int oracle_full(const oracle_problem *p, const void *q, const void *k, const voi
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 1)
-            for (int64_t f = 0; f < nflat; ++f) {
+            for (int64_t t = 0; t < count; ++t) {
+                const int64_t f = rows ? rows[t] : t;
                 const query_loc L = locate(p, f);
                 load_query(p, q, &L, w.qrow);
                 for (int64_t j = 0; j <= L.i; ++j) {
                     w.list[j] = j;
                     w.s_list[j] = score(p, w.qrow, k, L.kv_off, j);
                 }
-                attend(p, w.list, L.i + 1, w.s_list, v, L.kv_off, out + f * p->d);
+                attend(p, w.list, L.i + 1, w.s_list, v, L.kv_off, out + t * p->d);
             }
         }
         scratch_free(&w);

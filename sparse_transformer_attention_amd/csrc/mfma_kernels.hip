@@ -500,8 +500,9 @@ __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__r
 // anchor and window, folded into a running softmax (largest score m, weight sum l), and the
 // weights times V are accumulated as O^T += V^T P^T: the weights a lane holds for two blocks of
 // 16 rows are exactly its B operand of one 32-row step (the same rows on both sides of the
-// contraction), and V^T comes from a transposed copy of the tile in LDS. The weights enter the
-// product as bf16 (relative error 2^-9 per weight), accumulation is fp32. Output per query
+// contraction), and V^T comes from a transposed copy of the tile in LDS. Each fp32 weight enters
+// the product as the sum of two bf16 parts (two products per step), so the weights times V agree
+// with the fp32 weight sum to about 2^-17 per weight; accumulation is fp32. Output per query
 // vector: m, l and the weighted sum of V rows, the partial the finish kernel merges.
 constexpr int kWinTile = 64;
 // Query blocks of 16 per wavefront in the dense kernel, per d.
@@ -658,14 +659,23 @@ __global__ __launch_bounds__(256) void mfma_window_kernel(const __bf16 *__restri
                 pw[kbk][r] = (inm >> (4 * kbk + r)) & 1u ? exp2f((sc[kbk][r] - m) * a.scale_log2e) : 0.f;
                 lsum += pw[kbk][r];
             }
-        // O^T += V^T P^T over two steps of 32 rows (blocks 0,1 and 2,3).
+        // O^T += V^T P^T over two steps of 32 rows (blocks 0,1 and 2,3). Each fp32 weight enters
+        // as two bf16 parts, w = hi + lo (hi = w rounded to bf16, lo = the rest rounded again),
+        // in two products with the same V^T operand: the weights V is multiplied by agree with
+        // the fp32 weights summed into lsum to about 2^-17 of each weight, as in the other
+        // attend paths, instead of the 2^-9 of one bf16 rounding.
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-            bf16x8_t pb;
+            bf16x8_t pb_hi, pb_lo;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pb[r] = (__bf16)pw[2 * h2][r];
-                pb[4 + r] = (__bf16)pw[2 * h2 + 1][r];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const float w = pw[2 * h2 + half][r];
+                    const __bf16 hi = (__bf16)w;
+                    pb_hi[4 * half + r] = hi;
+                    pb_lo[4 * half + r] = (__bf16)(w - (float)hi);
+                }
             }
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
@@ -673,7 +683,8 @@ __global__ __launch_bounds__(256) void mfma_window_kernel(const __bf16 *__restri
                 const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
                 const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
                 const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[db], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb_hi, o[db], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb_lo, o[db], 0, 0, 0);
             }
         }
         __syncthreads();

@@ -1,7 +1,9 @@
 """The dense causal-attention baseline (ca_dense_attention_ex) against the oracle's full
 attention (softmax over every j <= i, times V; section 1.1 of the metaphor-xennon page on "The
 Condensate Theorem"), which the oracle pins match to library attention (test_oracle_pins.py).
-bf16 inputs, fp32 accumulation; tolerance that of bf16 outputs."""
+bf16 inputs, fp32 accumulation; tolerance that of bf16 outputs. The dense kernel multiplies V by
+the softmax weights rounded to bf16 (a relative error of up to 2^-9 per weight), so its
+achieved-error ceiling is that of bf16 weights, not of the method's fp32 ones."""
 import sys
 
 import numpy as np
@@ -13,6 +15,9 @@ import sparse_transformer_attention_amd as ca
 from sparse_transformer_attention_amd import synth
 
 from parity import assert_outputs
+
+# bf16 weights: errors of a few 2^-9 in a convex combination of V rows.
+DENSE_CEILING = 1e-2
 
 pytestmark = pytest.mark.gpu
 
@@ -47,22 +52,29 @@ def test_dense_matches_oracle_full_attention(name):
     out = ca.dense_attention(q, k, v)
     torch.cuda.synchronize()
     ref = oracle.full(x["q"], x["k"], x["v"])
-    assert_outputs(out.cpu().numpy(), ref, torch.bfloat16)
+    err = assert_outputs(out.cpu().numpy(), ref, torch.bfloat16, ceiling=DENSE_CEILING)
+    announce(f"dense {name}: max relative error {err:.3g}")
 
 
-def test_dense_full_size_prefill_131k_sampled():
+def test_dense_full_size_prefill_131k_stratified():
+    """The full 131K prefill (8 heads, d = 64): the first and last rows, the row at every
+    256-vector boundary for every head, and 512 random rows, against the oracle's full
+    attention on those rows."""
     w = synth.WORKLOADS["prefill_131k_h8_bf16"]
     x = synth.make_inputs(w, device="cuda")
     announce("dense full-size prefill 131k")
-    out = ca.dense_attention(x["q"], x["k"], x["v"]).cpu().numpy()
-    g = torch.Generator().manual_seed(3)
-    rows = [(0, 0, 0), (0, 7, w.nq - 1)] + [
-        (0, int(torch.randint(w.heads, (1,), generator=g)), int(torch.randint(w.nq, (1,), generator=g)))
-        for _ in range(6)]
-    for (b, h, r) in rows:
-        i = w.n - w.nq + r
-        q1 = x["q"][b, h, r].reshape(1, 1, 1, w.d).cpu()
-        k1 = x["k"][b, h, : i + 1].reshape(1, 1, i + 1, w.d).cpu()
-        v1 = x["v"][b, h, : i + 1].reshape(1, 1, i + 1, w.d).cpu()
-        ref = oracle.full(q1, k1, v1)
-        assert_outputs(out[b, h, r].reshape(1, 1, 1, -1), ref, torch.bfloat16)
+    out = ca.dense_attention(x["q"], x["k"], x["v"])
+    rows = set()
+    for h in range(w.heads):
+        rows.update({(0, h, 0), (0, h, w.nq - 1)})
+        rows.update((0, h, m) for m in range(256, w.nq, 256))
+    g = np.random.default_rng(3)
+    rows.update((0, int(h), int(r)) for h, r in zip(g.integers(0, w.heads, 512), g.integers(0, w.nq, 512)))
+    rows = sorted(rows)
+    a = torch.tensor(rows, dtype=torch.int64, device="cuda")
+    g_out = out[a[:, 0], a[:, 1], a[:, 2]].cpu().numpy()
+    xh = {t: x[t].cpu() for t in ("q", "k", "v")}
+    del x, out
+    ref = oracle.full(xh["q"], xh["k"], xh["v"], rows=rows)
+    err = assert_outputs(g_out, ref, torch.bfloat16, ceiling=DENSE_CEILING)
+    announce(f"dense 131k: {len(rows)} rows, max relative error {err:.3g}")

@@ -371,3 +371,22 @@ def test_mass_parts_hand_computed():
     expect = {2: 6 / 18, 5: 1 / 18, 6: 3 / 18, 7: 8 / 18}
     for col, val in expect.items():
         assert abs(got[col] - val) < 1e-6, (col, got[col], val)
+
+
+def test_row_subsets_equal_the_whole_call():
+    """The row-subset entry points (used for sampled parity at full sizes) return, for each
+    listed (b, h, r) and in the listed order, exactly the whole call's results for that query."""
+    w, x = make(B=2, Hq=4, Hkv=2, n=260, nq=30, d=32, W=20, topk=12, dtype="bf16", seed=4)
+    idx, out, diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    full = oracle.full(x["q"], x["k"], x["v"])
+    rows = [(1, 3, 29), (0, 0, 0), (0, 2, 17), (1, 0, 5), (0, 2, 17)]
+    i2, o2, d2 = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk, rows=rows)
+    f2 = oracle.full(x["q"], x["k"], x["v"], rows=rows)
+    r2 = oracle.restricted(x["q"], x["k"], x["v"], np.stack([idx[t] for t in rows]), rows=rows)
+    for t, key in enumerate(rows):
+        assert np.array_equal(i2[t], idx[key])
+        assert np.array_equal(o2[t], out[key]) and np.array_equal(r2[t], out[key])
+        assert np.array_equal(d2[t], diag[key], equal_nan=True)
+        assert np.array_equal(f2[t], full[key])
+    with pytest.raises(ValueError):
+        oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk, rows=[(0, 4, 0)])

@@ -13,7 +13,7 @@ import oracle
 import sparse_transformer_attention_amd as ca
 from sparse_transformer_attention_amd import synth
 
-from parity import TOL, assert_outputs, compare_sets
+from parity import TOL, assert_outputs, check_sets_rows, compare_sets
 
 pytestmark = pytest.mark.gpu
 
@@ -238,95 +238,117 @@ def test_workspace_too_small_is_rejected():
 
 # ---- full-size workloads --------------------------------------------------------------------
 
-def sampled_oracle(w, x_gpu, rows):
-    """Oracle on sampled query vectors: each (b, h, r) is solved as a decode over keys 0..i,
-    with only that KV slice copied to the host."""
-    out_idx, out_ref, diag, qs, ks = {}, {}, {}, {}, {}
-    for (b, h, r) in rows:
-        i = w.n - w.nq + r
-        kvh = h // w.group
-        q1 = x_gpu["q"][b, h, r].reshape(1, 1, 1, w.d).cpu()
-        k1 = x_gpu["k"][b, kvh, : i + 1].reshape(1, 1, i + 1, w.d).cpu()
-        v1 = x_gpu["v"][b, kvh, : i + 1].reshape(1, 1, i + 1, w.d).cpu()
-        idx, out, dg = oracle.condensate(q1, k1, v1, w.W, w.topk)
-        out_idx[(b, h, r)], out_ref[(b, h, r)], diag[(b, h, r)] = idx, (q1, k1, v1), dg
-    return out_idx, out_ref, diag
+def to_host(x):
+    return {t: x[t].cpu() for t in ("q", "k", "v")}
 
 
-def check_sampled(w, x_gpu, gpu_out, gpu_idx, rows):
-    ref_idx, ref_in, ref_diag = sampled_oracle(w, x_gpu, rows)
-    worst = 0.0
-    for key in rows:
-        b, h, r = key
-        q1, k1, v1 = ref_in[key]
-        g_idx = gpu_idx[b, h, r].reshape(1, 1, 1, -1)
-        compare_sets(g_idx, ref_idx[key], ref_diag[key], q1, k1, w.W, w.topk)
-        ref = oracle.restricted(q1, k1, v1, g_idx)
-        worst = max(worst, assert_outputs(gpu_out[b, h, r].reshape(1, 1, 1, -1), ref, w.torch_dtype))
-    return worst
+def check_rows(w, xh, gpu_out, gpu_idx, rows):
+    """Oracle on the listed (b, h, r) queries (one call over the full tensors, no copies per
+    row), sets compared row by row within the band, outputs against the oracle's restricted
+    softmax on the GPU's own sets. gpu_out/gpu_idx: [B][Hq][nq][..] numpy. Returns the largest
+    relative output error."""
+    a = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    ref_idx, _, ref_diag = oracle.condensate(xh["q"], xh["k"], xh["v"], w.W, w.topk, rows=rows)
+    g_idx = np.ascontiguousarray(gpu_idx[a[:, 0], a[:, 1], a[:, 2]])
+    g_out = gpu_out[a[:, 0], a[:, 1], a[:, 2]]
+    pos = w.n - w.nq + a[:, 2]
+    check_sets_rows(g_idx, ref_idx, ref_diag, pos, w.W, w.topk,
+                    lambda t: oracle.scores(xh["q"], xh["k"], *map(int, a[t])))
+    ref = oracle.restricted(xh["q"], xh["k"], xh["v"], g_idx, rows=rows)
+    return assert_outputs(g_out, ref, w.torch_dtype)
 
 
-def test_full_size_decode_131k():
+def run_full_size(w):
+    x = synth.make_inputs(w, device="cuda")
+    out, idx = ca.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    torch.cuda.synchronize()
+    return x, out, idx
+
+
+def test_full_size_decode_131k_all_32_vectors():
     """The 131K-token GQA decode, in the launch configuration the benchmark times; every query
     vector checked."""
     w = synth.WORKLOADS["decode_131k_gqa_bf16"]
-    x = synth.make_inputs(w, device="cuda")
     announce("full-size decode 131k")
-    out, idx = ca.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
-    torch.cuda.synchronize()
-    rows = [(0, h, 0) for h in range(w.heads)]
-    check_sampled(w, x, out.cpu().numpy(), idx.cpu().numpy(), rows)
-    # The planted needles of each KV head rank high for their query; most are selected.
+    x, out, idx = run_full_size(w)
     idx_np = idx.cpu().numpy()
+    check_rows(w, to_host(x), out.cpu().numpy(), idx_np, [(0, h, 0) for h in range(w.heads)])
+    # The planted needles of each KV head rank high for their query; most are selected.
     found = sum(j in set(idx_np[0, h, r].tolist()) for kv in range(w.kv_heads)
                 for (j, h, r) in x["needles"][(0, kv)])
     assert found >= 0.5 * w.kv_heads * w.needles_per_kv_head
 
 
-def test_full_size_decode_1m_batch4():
+def test_full_size_decode_1m_batch4_all_128_vectors():
     w = synth.WORKLOADS["decode_1m_b4_gqa_bf16"]
-    x = synth.make_inputs(w, device="cuda")
-    announce("full-size decode 1m b4")
-    out, idx = ca.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
-    torch.cuda.synchronize()
-    rows = [(0, 0, 0), (0, 7, 0), (1, 13, 0), (2, 22, 0), (3, 31, 0), (3, 4, 0)]
-    check_sampled(w, x, out.cpu().numpy(), idx.cpu().numpy(), rows)
+    announce("full-size decode 1m b4 (all 128 query vectors)")
+    x, out, idx = run_full_size(w)
+    out_np, idx_np = out.cpu().numpy(), idx.cpu().numpy()
+    xh = to_host(x)
+    del x, out, idx
+    torch.cuda.empty_cache()
+    rows = [(b, h, 0) for b in range(w.batch) for h in range(w.heads)]
+    check_rows(w, xh, out_np, idx_np, rows)
 
 
-def test_full_size_prefill_chunk_4k_32k():
+def test_full_size_prefill_chunk_4k_32k_all_131072_rows():
+    """The 4K x 32K prefill chunk on the MFMA path: every one of the 32 x 4096 query rows."""
     w = synth.WORKLOADS["prefill_chunk_4k_32k_bf16"]
-    x = synth.make_inputs(w, device="cuda")
-    announce("full-size prefill chunk 4k x 32k")
-    out, idx = ca.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
-    torch.cuda.synchronize()
-    g = torch.Generator().manual_seed(0)
-    rows = [(0, 0, 0), (0, 31, w.nq - 1), (0, 5, 255), (0, 17, 256)]
-    rows += [(0, int(torch.randint(w.heads, (1,), generator=g)), int(torch.randint(w.nq, (1,), generator=g)))
-             for _ in range(12)]
-    check_sampled(w, x, out.cpu().numpy(), idx.cpu().numpy(), rows)
+    announce("full-size prefill chunk 4k x 32k (all rows)")
+    x, out, idx = run_full_size(w)
+    out_np, idx_np = out.cpu().numpy(), idx.cpu().numpy()
+    xh = to_host(x)
+    ref_idx, _, ref_diag = oracle.condensate(xh["q"], xh["k"], xh["v"], w.W, w.topk)
+    compare_sets(idx_np, ref_idx, ref_diag, xh["q"], xh["k"], w.W, w.topk)
+    del ref_idx, ref_diag
+    ref = oracle.restricted(xh["q"], xh["k"], xh["v"], idx_np)
+    assert_outputs(out_np, ref, w.torch_dtype)
 
 
-def test_full_size_prefill_131k():
-    """Full causal prefill, 8 heads, d = 64, 131,072 positions (every position a query): the
-    first W rows have no candidates, the next ones fewer than k."""
+def prefill_strata(w, seed, extra_random):
+    """Stratified query rows of a full prefill (nq = n): for every head, the rows where R_i
+    grows from empty to k (W-2 .. W+k+13), the last and the first row at every 256-vector
+    boundary of the MFMA candidate-pass workgroups (vector = row for one query head per KV
+    head), the last 16 rows; plus extra_random uniform (head, row) draws."""
+    assert w.group == 1
+    rows = set()
+    for h in range(w.heads):
+        rows.update((0, h, r) for r in range(max(0, w.W - 2), min(w.nq, w.W + w.topk + 14)))
+        for m in range(256, w.nq, 256):
+            rows.update({(0, h, m - 1), (0, h, m)})
+        rows.update((0, h, r) for r in range(w.nq - 16, w.nq))
+    g = np.random.default_rng(seed)
+    rows.update((0, int(h), int(r)) for h, r in zip(g.integers(0, w.heads, extra_random),
+                                                     g.integers(0, w.nq, extra_random)))
+    return sorted(rows)
+
+
+def test_full_size_prefill_131k_stratified_9k_rows():
+    """Full causal prefill, 8 heads, d = 64, 131,072 positions (every position a query) on the
+    MFMA path: about 9,000 stratified rows over all 8 heads (see prefill_strata)."""
     w = synth.WORKLOADS["prefill_131k_h8_bf16"]
-    x = synth.make_inputs(w, device="cuda")
-    announce("full-size prefill 131k")
-    out, idx = ca.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
-    torch.cuda.synchronize()
-    g = torch.Generator().manual_seed(1)
-    rows = [(0, 0, 0), (0, 1, w.W), (0, 2, w.W + 1), (0, 3, w.W + w.topk), (0, 7, w.nq - 1)]
-    rows += [(0, int(torch.randint(w.heads, (1,), generator=g)), int(torch.randint(w.nq, (1,), generator=g)))
-             for _ in range(11)]
-    check_sampled(w, x, out.cpu().numpy(), idx.cpu().numpy(), rows)
+    rows = prefill_strata(w, seed=1, extra_random=512)
+    announce(f"full-size prefill 131k ({len(rows)} stratified rows)")
+    assert len(rows) > 8500
+    x, out, idx = run_full_size(w)
+    a = np.asarray(rows, dtype=np.int64)
+    sel = torch.from_numpy(a).cuda()
+    g_out = out[sel[:, 0], sel[:, 1], sel[:, 2]].cpu().numpy()
+    g_idx = idx[sel[:, 0], sel[:, 1], sel[:, 2]].cpu().numpy()
+    xh = to_host(x)
+    del x, out, idx
+    ref_idx, _, ref_diag = oracle.condensate(xh["q"], xh["k"], xh["v"], w.W, w.topk, rows=rows)
+    pos = w.n - w.nq + a[:, 2]
+    check_sets_rows(g_idx, ref_idx, ref_diag, pos, w.W, w.topk,
+                    lambda t: oracle.scores(xh["q"], xh["k"], *map(int, a[t])))
+    ref = oracle.restricted(xh["q"], xh["k"], xh["v"], g_idx, rows=rows)
+    assert_outputs(g_out, ref, w.torch_dtype)
 
 
 @pytest.mark.parametrize("name", ["decode_131k_gqa_w64_bf16", "decode_131k_gqa_w1024_bf16"])
 def test_full_size_decode_131k_other_windows(name):
     """The 131K GQA decode with W = 64 and W = 1024; every query vector checked."""
     w = synth.WORKLOADS[name]
-    x = synth.make_inputs(w, device="cuda")
     announce(f"full-size {name}")
-    out, idx = ca.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
-    torch.cuda.synchronize()
-    check_sampled(w, x, out.cpu().numpy(), idx.cpu().numpy(), [(0, h, 0) for h in range(w.heads)])
+    x, out, idx = run_full_size(w)
+    check_rows(w, to_host(x), out.cpu().numpy(), idx.cpu().numpy(), [(0, h, 0) for h in range(w.heads)])
