@@ -9,9 +9,10 @@ step (32 query heads, 8 KV heads, d=128, bf16, W=256, k=64). Distinct KV buffer 
 between steps so that the key stream comes from HBM and not from the 256 MB last-level cache.
 
 Prints one JSON line: query vectors/s from a clean timed loop, the step's algorithmic HBM GB/s,
-the roofline of the dominant kernel (the score stage; durations from HIP events the library
-records around its own launches on the stream it uses, in a second pass over the same steps),
-and the CPU oracle timed on the host.
+the roofline of the dominant kernel (on the decode path the one kernel that is the whole step;
+on the prefill paths the score stage; durations from HIP events the library records around its
+own launches on the stream it uses, in a second pass over the same steps), and the CPU oracle
+timed on the host.
 """
 from __future__ import annotations
 
@@ -29,11 +30,12 @@ sys.path.insert(0, ROOT)
 METRIC = "condensate-attn decode queries/sec + achieved HBM GB/s at 131K ctx (1 GPU)"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of the chip
-# HBM bytes per launch of the score stage's kernel (score_keys on this workload) from rocprofv3
+# HBM bytes per launch of the decode kernel (the whole step on this workload) from rocprofv3
 # FETCH_SIZE / WRITE_SIZE counters, valid while the kernel's sources hash to the recorded value.
-COUNTERS = os.path.join(ROOT, "profiles", "score_keys_decode_131k_gqa_bf16_counters.md")
+COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_decode_131k_gqa_bf16_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_transformer_attention_amd", "csrc", f)
-                  for f in ("stream_kernels.hip", "score_core.h", "device_utils.h", "ca_internal.h")]
+                  for f in ("decode_kernels.hip", "attend_core.h", "merge_core.h", "score_core.h",
+                            "select_core.h", "device_utils.h", "ca_internal.h")]
 
 
 def kernel_sources_sha() -> str:
@@ -182,7 +184,7 @@ def main():
                    "p10": float(np.percentile(per_step_us, 10)),
                    "p90": float(np.percentile(per_step_us, 90))}
 
-    # Algorithmic bytes. score_select reads the key rows of the candidate range once per KV
+    # Algorithmic bytes. The score stage reads the key rows of the candidate range once per KV
     # head plus the queries; the whole step reads all of K, the distinct V rows of the sets,
     # the queries, and writes the outputs and index sets.
     rmax = max(0, w.n - 1 - w.W)
@@ -238,23 +240,38 @@ def main():
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": pass_s * 1e6,
         }
-    # Decode path: score_keys; chunked path: score_topk (profiled as score_select).
-    score_name = "score_keys" if "score_keys" in prof else "score_select"
-    launches, score_ms = prof.get(score_name, (0, 0.0))
-    score_avg_s = score_ms / max(1, launches) / 1e3
-    achieved = score_bytes / score_avg_s / 1e9 if launches else None
-    # The recorded counters are those of score_keys without the mass epilogue: other kernels
-    # (the mass variant, score_topk on the chunked path) report no traffic.
-    traffic = recorded_traffic(w.name) if score_name == "score_keys" and not args.mass else None
-    if "mfma_bound" not in prof and not args.dense:
+    if "decode" in prof and not args.dense:
+        # Decode path: one kernel is the whole step (K stream, selection, set assembly, attend),
+        # so its algorithmic bytes are the step's.
+        launches, dec_ms = prof["decode"]
+        dec_avg_s = dec_ms / max(1, launches) / 1e3
+        achieved = step_bytes / dec_avg_s / 1e9
+        # The recorded counters are those of the kernel without the mass diagnostic.
+        traffic = recorded_traffic(w.name) if not args.mass else None
         roofline = {
-            "kernel": "score_keys (score stage)" if score_name == "score_keys" else "score_topk (score stage)",
+            "kernel": "decode (the whole step: scores, selection, set, attend)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": step_bytes,
+            "avg_launch_us": dec_avg_s * 1e6,
+        }
+    elif "mfma_bound" not in prof and not args.dense:
+        # Chunked path: score_topk (profiled as score_select) is the score stage.
+        launches, score_ms = prof.get("score_select", (0, 0.0))
+        score_avg_s = score_ms / max(1, launches) / 1e3
+        achieved = score_bytes / score_avg_s / 1e9 if launches else None
+        roofline = {
+            "kernel": "score_topk (score stage)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": (achieved / HBM_PEAK_GBPS) if achieved else None,
-            "traffic": traffic,
+            "traffic": None,
             "algorithmic_bytes_per_launch": score_bytes,
             "avg_launch_us": score_avg_s * 1e6,
         }

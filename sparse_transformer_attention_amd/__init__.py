@@ -208,6 +208,7 @@ def attention_on_subset(p: Params, q, k, v, idx, out, stream=None):
 
 
 def alloc_workspace(p: Params, device="cuda"):
+    """A workspace for problem p (uninitialised: the library needs none)."""
     nbytes = workspace_size(p)
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device) if nbytes else None
 

@@ -33,6 +33,7 @@ struct Plan {
     int64_t nwg;          // score_topk workgroups
     int64_t lmax;         // candidate slots per query (wpu * seg)
     int seg;              // keys per segment: topk (score_topk) or kMfmaSeg (MFMA passes)
+    size_t slots_offset;  // byte offset of the per-query slot words (after the header)
     size_t lists_offset;  // byte offset of the lists in the workspace
     size_t ws_bytes;      // total workspace
     // Decode path (score_keys, then finish reading its tile summaries): rows per unit covered
@@ -52,7 +53,13 @@ struct Plan {
     int tile_rows;
     size_t best1_offset, rest_offset, bmax_offset, scratch_offset;
     size_t zsum_offset;   // mass diagnostic: [units][nblk][G] (largest score, sum) float pairs
+    size_t summ_offset;   // decode kernel: block records [units][G][nblk][4] 64-bit words
 };
+
+// Every plan's workspace starts with this header: the decode kernel's arrival counters (one
+// 32-bit word per unit, at most kHeaderBytes / 4 units). Calls leave it zero; nothing else is
+// stored there.
+constexpr size_t kHeaderBytes = 64 * 1024;
 
 // Launchers (enqueue only; return the hipError_t of the last launch).
 hipError_t launch_score_select(const Plan &pl, const void *q, const void *k, void *ws,
@@ -70,6 +77,11 @@ size_t topk_lds_bytes(const Plan &pl);
 // mass: also the per-block sums of the mass diagnostic (zsum_offset).
 hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
                              bool mass = false);
+// Decode path in one kernel: scores, block records, and per unit in its last-arriving workgroup
+// the exact top-k', out_idx and (out != nullptr) the restricted softmax times V (mass != nullptr:
+// also the mass diagnostic).
+hipError_t launch_decode(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
+                         int32_t *out_idx, float *out, float *mass, hipStream_t s);
 // Query blocks of 16 per wavefront of the two MFMA passes (16 * QB * kMfmaWaves query vectors per
 // workgroup).
 // Bound pass, per d. Measured: 3 at d = 64 (more products per operand read, 2 wavefronts per

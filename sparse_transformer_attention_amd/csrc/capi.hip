@@ -10,13 +10,15 @@
 #include "ca_internal.h"
 #include "condensate.h"
 
+static_assert(ca::kHeaderBytes == CA_WORKSPACE_HEADER, "workspace header size");
+
 namespace {
 
 // ---- measurement hooks: HIP events around each launch while profiling is on ----------------
-enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_BOUND = 3, K_CAND = 4, K_KEYS = 5, K_WINDOW = 6,
+enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_BOUND = 3, K_CAND = 4, K_DECODE = 5, K_WINDOW = 6,
        K_DENSE = 7, K_COUNT = 8 };
 const char *const kKernelNames[K_COUNT] = {"score_select", "finish", "attend", "mfma_bound", "mfma_cand",
-                                           "score_keys", "mfma_window", "dense"};
+                                           "decode", "mfma_window", "dense"};
 
 struct Profiler {
     std::mutex mu;
@@ -87,6 +89,12 @@ constexpr int kStreamBlockRows = 256;    // score_keys rows per workgroup
 constexpr double kStreamKeysMax = 1024.0 * 1024 * 1024;  // key buffer budget (bytes)
 constexpr int64_t kMfmaMinVectors = 64;  // query vectors per KV head for the MFMA passes
 constexpr int kMfmaMaxTopk = 128;        // classes of the MFMA bound
+// Decode kernel: one finisher workgroup per unit stays resident for the whole launch (it waits
+// for the unit's records), so their number stays far below what the CUs hold at once; one
+// 64-bit epoch word per unit in the workspace header.
+constexpr int64_t kDecodeMaxUnits = 256;
+constexpr int kDecodeMaxTopk = 256;      // selected rows per query the finisher holds in LDS
+static_assert(kDecodeMaxUnits * 8 <= (int64_t)ca::kHeaderBytes, "epoch words in the header");
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -164,8 +172,9 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         P.lmax = (int64_t)P.wpu * P.seg;
         P.nwg = 0;
         const size_t slot_bytes = ((size_t)(3 * P.nqv * P.wpu) * sizeof(uint32_t) + 255) & ~(size_t)255;
-        P.lists_offset = slot_bytes;
-        P.win_offset = (slot_bytes + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) + 255) & ~(size_t)255;
+        P.slots_offset = ca::kHeaderBytes;
+        P.lists_offset = P.slots_offset + slot_bytes;
+        P.win_offset = (P.lists_offset + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) + 255) & ~(size_t)255;
         P.ws_bytes = P.win_offset + (size_t)P.nqv * (size_t)(P.d + 2) * sizeof(float);
         return CA_OK;
     }
@@ -173,28 +182,26 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         // Blocks of 256 rows from row 0 cover rows 1..rmax.
         const int64_t nblk = (P.rmax + kStreamBlockRows) / kStreamBlockRows;
         const double kb = (double)P.units * (double)(nblk * kStreamBlockRows) * P.G * 4.0;
-        // (Index math of score_keys in 32 bits.)
-        if (kb <= kStreamKeysMax && P.units * nblk < ((int64_t)1 << 31) && nvec < ((int64_t)1 << 31)) {
+        // (Index math of the decode kernel in 32 bits; one arrival counter per unit in the
+        // workspace header.)
+        const int64_t wpb = (nblk + 1) / 2;
+        if (kb <= kStreamKeysMax && P.units * nblk < ((int64_t)1 << 31) && nvec < ((int64_t)1 << 31) &&
+            P.units <= kDecodeMaxUnits && P.topk <= kDecodeMaxTopk &&
+            P.units * (wpb + 1) < ((int64_t)1 << 31)) {
             P.stream = true;
             P.nblk = (int)nblk;
             P.rstride = nblk * kStreamBlockRows;
             P.wpu = 1;
-            P.nwg = P.units * P.nblk;
-            if (P.nwg > (int64_t)UINT32_MAX / 256)
-                return fail(CA_ERR_UNSUPPORTED, "problem too large for one launch");
+            P.nwg = P.units * (wpb + 1);
             P.lmax = 0;
             P.lists_offset = 0;
-            // Tiles of 4 rows-per-load: 16 rows with 16 lanes per row (rows of >= 256 bytes),
-            // else 32.
             P.tile_rows = row_bytes >= 256 ? 16 : 32;
             auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-            const size_t ntiles = (size_t)P.units * P.G * (P.rstride / P.tile_rows);
-            P.best1_offset = 0;
-            P.rest_offset = P.best1_offset + up(ntiles * sizeof(uint32_t));
-            P.bmax_offset = P.rest_offset + up(ntiles * 2 * sizeof(uint32_t));
-            P.scratch_offset = P.bmax_offset + up((size_t)P.units * P.nblk * P.G * sizeof(uint32_t));
-            P.zsum_offset = up(P.scratch_offset + (size_t)P.nqv * (size_t)P.rstride * sizeof(uint32_t));
-            P.ws_bytes = P.zsum_offset + (size_t)P.units * P.nblk * P.G * 2 * sizeof(float);
+            const size_t rq = (size_t)P.units * P.G * (size_t)P.nblk;  // (unit, query, block) records
+            P.summ_offset = ca::kHeaderBytes;
+            P.zsum_offset = up(P.summ_offset + rq * 4 * sizeof(uint64_t));
+            P.scratch_offset = up(P.zsum_offset + rq * 2 * sizeof(float));
+            P.ws_bytes = P.scratch_offset + (size_t)P.units * P.G * (size_t)P.rstride * sizeof(uint32_t);
             return CA_OK;
         }
     }
@@ -213,8 +220,9 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     const double list_bytes = (double)P.nqv * (double)P.lmax * 8.0;
     if (list_bytes > 9.0e18) return fail(CA_ERR_UNSUPPORTED, "workspace size overflows");
     const size_t slot_bytes = ((size_t)(3 * P.nqv * P.wpu) * sizeof(uint32_t) + 255) & ~(size_t)255;
-    P.lists_offset = slot_bytes;
-    P.ws_bytes = P.candidates ? slot_bytes + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) : 0;
+    P.slots_offset = ca::kHeaderBytes;
+    P.lists_offset = P.slots_offset + slot_bytes;
+    P.ws_bytes = P.candidates ? P.lists_offset + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) : 0;
     if (ca::topk_lds_bytes(P) > 64 * 1024)
         return fail(CA_ERR_UNSUPPORTED, "selection buffers exceed the LDS budget");
     return CA_OK;
@@ -248,10 +256,12 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
             if (e != hipSuccess) return hip_fail(e, "mfma_window launch");
         }
     } else if (pl.candidates && pl.stream) {
-        ProfScope ps(K_KEYS, s);
-        e = ca::launch_score_keys(pl, q, k, ws, s, mass != nullptr);
-        ps.done();
-        if (e != hipSuccess) return hip_fail(e, "score_keys launch");
+        // One kernel: scores, selection, set assembly and attend.
+        ProfScope pd(K_DECODE, s);
+        e = ca::launch_decode(pl, q, k, v, ws, out_idx, out, mass, s);
+        pd.done();
+        if (e != hipSuccess) return hip_fail(e, "decode launch");
+        return CA_OK;
     } else if (pl.candidates) {
         ProfScope ps(K_SCORE, s);
         e = ca::launch_score_select(pl, q, k, ws, s);

@@ -880,8 +880,8 @@ hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void
     a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g; a.W = pl.W; a.topk = pl.topk;
     a.nvec = (uint32_t)(pl.g * pl.nq);
     char *w = static_cast<char *>(ws);
-    a.tau = reinterpret_cast<uint32_t *>(w);
-    a.cnt = reinterpret_cast<uint32_t *>(w) + 2 * pl.nqv * pl.wpu;
+    a.tau = reinterpret_cast<uint32_t *>(w + pl.slots_offset);
+    a.cnt = reinterpret_cast<uint32_t *>(w + pl.slots_offset) + 2 * pl.nqv * pl.wpu;
     a.lists = reinterpret_cast<uint64_t *>(w + pl.lists_offset);
     const bool cand = pass != 0;
     const int qb_bound = pl.d == 128 ? kMfmaQBBound128 : kMfmaQBBound64;

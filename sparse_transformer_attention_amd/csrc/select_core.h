@@ -131,6 +131,49 @@ __device__ __forceinline__ uint32_t wave_keep_top_u64(const uint64_t (&kr)[E], i
     return wave_min_u32_dpp(tmin);
 }
 
+// Maximum / minimum of 64-bit values over the lanes of a wavefront (uniform result).
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t x) {
+    const uint32_t hi = (uint32_t)(x >> 32);
+    const uint32_t hmax = wave_max_u32_dpp(hi);
+    const uint32_t lmax = wave_max_u32_dpp(hi == hmax ? (uint32_t)x : 0u);
+    return ((uint64_t)hmax << 32) | lmax;
+}
+__device__ __forceinline__ uint64_t wave_min_u64_dpp(uint64_t x) {
+    const uint32_t hi = (uint32_t)(x >> 32);
+    const uint32_t hmin = wave_min_u32_dpp(hi);
+    const uint32_t lmin = wave_min_u32_dpp(hi == hmin ? (uint32_t)x : 0xFFFFFFFFu);
+    return ((uint64_t)hmin << 32) | lmin;
+}
+
+// A value T that exactly `keep` of the wavefront's distinct non-zero keys kr[0..E) reach (0 =
+// empty; at least `keep` keys, keep >= 1): the keys >= T are the top `keep`. Found bit by bit
+// from the highest bit where the keys differ, each step counting the keys that reach the
+// candidate value with ballots (no LDS); it stops as soon as exactly `keep` reach it.
+template <int E>
+__device__ __forceinline__ uint64_t wave_kth_u64(const uint64_t (&kr)[E], int keep) {
+    uint64_t mx = 0ull, mn = ~0ull;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (kr[e]) { mx = kr[e] > mx ? kr[e] : mx; mn = kr[e] < mn ? kr[e] : mn; }
+    }
+    mx = wave_max_u64_dpp(mx);
+    mn = wave_min_u64_dpp(mn);
+    if (mx == mn) return mx;
+    const int hb = 63 - __builtin_clzll(mx ^ mn);
+    uint64_t t = hb >= 63 ? 0ull : (mx >> (hb + 1)) << (hb + 1);
+    for (int bit = hb; bit >= 0; --bit) {
+        const uint64_t c = t | (1ull << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(kr[e] >= c));
+        if (cnt >= keep) {
+            t = c;
+            if (cnt == keep) break;
+        }
+    }
+    return t;
+}
+
 // A value that at least `keep` of the wavefront's non-zero values v[0..E) reach, close to their
 // keep-th largest: the largest P whose bits above the highest bit hb where the values differ are
 // theirs, whose bits below lb = hb - 9 are 0, and which `keep` values reach (the lower edge of the

@@ -350,7 +350,7 @@ size_t topk_lds_bytes(const Plan &pl) {
 
 hipError_t launch_score_select(const Plan &pl, const void *q, const void *k, void *ws,
                                hipStream_t s) {
-    uint32_t *tau = static_cast<uint32_t *>(ws);
+    uint32_t *tau = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.slots_offset);
     const int64_t nslots = pl.nqv * pl.wpu;
     const int64_t cblocks = (2 * nslots + 255) / 256;
     hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)(cblocks < 1024 ? cblocks : 1024)), dim3(256),

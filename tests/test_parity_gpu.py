@@ -352,3 +352,66 @@ def test_full_size_decode_131k_other_windows(name):
     announce(f"full-size {name}")
     x, out, idx = run_full_size(w)
     check_rows(w, to_host(x), out.cpu().numpy(), idx.cpu().numpy(), [(0, h, 0) for h in range(w.heads)])
+
+
+def test_workspace_reused_across_calls_shapes_and_paths():
+    """One workspace, filled with random bytes before its first use, serves a sequence of calls
+    on changing inputs: two decode shapes (the one-kernel decode path, whose records carry a
+    per-call tag) and a bf16 prefill (the matrix-core path) in between. Every call's sets and
+    outputs must match the oracle's."""
+    shapes = {
+        "A": W_(heads=8, kv_heads=2, n=5000, nq=1, W=64, topk=32),
+        "B": W_(heads=4, kv_heads=1, n=9000, nq=2, W=40, topk=48),
+        "C": W_(heads=2, kv_heads=2, n=1500, nq=300, W=64, topk=32),
+    }
+    need = max(ca.workspace_size(ca.params(w.batch, w.heads, w.kv_heads, w.d, w.n, w.nq, w.W, w.topk, "bf16"))
+               for w in shapes.values())
+    g = torch.Generator(device="cuda").manual_seed(5)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda", generator=g)
+    for step, (name, seed) in enumerate([("A", 1), ("B", 2), ("A", 3), ("C", 4), ("A", 5), ("B", 6), ("A", 5)]):
+        w = shapes[name]
+        x = synth.make_inputs(w, seed=seed)
+        announce(f"workspace reuse step {step} shape {name}")
+        q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
+        out, idx = ca.condensate(q, k, v, w.W, w.topk, ws=ws)
+        torch.cuda.synchronize()
+        out, idx = out.cpu().numpy(), idx.cpu().numpy()
+        ref_idx, _, ref_diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+        compare_sets(idx, ref_idx, ref_diag, x["q"], x["k"], w.W, w.topk)
+        assert_outputs(out, oracle.restricted(x["q"], x["k"], x["v"], idx), w.torch_dtype)
+
+
+def test_graph_replays_take_fresh_inputs():
+    """A decode call captured in a graph and replayed on new inputs copied into the captured
+    buffers (the kernel's tags come from the workspace, not from the launch): every replay
+    equals an eager call on the same inputs, with the program's own work between replays."""
+    w = W_(heads=8, kv_heads=2, n=6000, nq=1, W=64, topk=32)
+    xs = [synth.make_inputs(w, seed=s) for s in (11, 12, 13)]
+    q, k, v = (xs[0][t].cuda() for t in ("q", "k", "v"))
+    p = ca.params_for(q, k, w.W, w.topk)
+    ws = ca.alloc_workspace(p)
+    out = torch.empty((w.batch, w.heads, w.nq, w.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.batch, w.heads, w.nq, w.set_cap), dtype=torch.int32, device="cuda")
+    announce("graph capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ca.condensate_attention_ex(p, q, k, v, out, idx, ws)   # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ca.condensate_attention_ex(p, q, k, v, out, idx, ws)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        x = xs[rep % 3]
+        q.copy_(x["q"]); k.copy_(x["k"]); v.copy_(x["v"])
+        graph.replay()
+        torch.cuda.synchronize()
+        got_out, got_idx = out.clone(), idx.clone()
+        eager_out, eager_idx = ca.condensate(q, k, v, w.W, w.topk)
+        torch.cuda.synchronize()
+        assert torch.equal(got_idx, eager_idx), f"replay {rep}: sets differ from the eager call"
+        assert torch.equal(got_out.view(torch.int32), eager_out.view(torch.int32)), f"replay {rep}: outputs differ"
+    ref_idx, _, ref_diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    compare_sets(got_idx.cpu().numpy(), ref_idx, ref_diag, x["q"], x["k"], w.W, w.topk)
