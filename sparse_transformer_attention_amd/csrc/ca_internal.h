@@ -53,12 +53,11 @@ struct Plan {
     int tile_rows;
     size_t best1_offset, rest_offset, bmax_offset, scratch_offset;
     size_t zsum_offset;   // mass diagnostic: [units][nblk][G] (largest score, sum) float pairs
-    size_t summ_offset;   // decode kernel: block records [units][G][nblk][4] 64-bit words
+    size_t summ_offset;   // decode kernel: block records [units][G][nblk][8] 64-bit words
 };
 
-// Every plan's workspace starts with this header: the decode kernel's arrival counters (one
-// 32-bit word per unit, at most kHeaderBytes / 4 units). Calls leave it zero; nothing else is
-// stored there.
+// Every plan's workspace starts with this header: the decode kernel's epoch words (one 64-bit
+// word per unit, at most kHeaderBytes / 8 units). Nothing else is stored there.
 constexpr size_t kHeaderBytes = 64 * 1024;
 
 // Launchers (enqueue only; return the hipError_t of the last launch).

@@ -10,8 +10,6 @@
 #include "ca_internal.h"
 #include "condensate.h"
 
-static_assert(ca::kHeaderBytes == CA_WORKSPACE_HEADER, "workspace header size");
-
 namespace {
 
 // ---- measurement hooks: HIP events around each launch while profiling is on ----------------
@@ -89,12 +87,7 @@ constexpr int kStreamBlockRows = 256;    // score_keys rows per workgroup
 constexpr double kStreamKeysMax = 1024.0 * 1024 * 1024;  // key buffer budget (bytes)
 constexpr int64_t kMfmaMinVectors = 64;  // query vectors per KV head for the MFMA passes
 constexpr int kMfmaMaxTopk = 128;        // classes of the MFMA bound
-// Decode kernel: one finisher workgroup per unit stays resident for the whole launch (it waits
-// for the unit's records), so their number stays far below what the CUs hold at once; one
-// 64-bit epoch word per unit in the workspace header.
-constexpr int64_t kDecodeMaxUnits = 256;
-constexpr int kDecodeMaxTopk = 256;      // selected rows per query the finisher holds in LDS
-static_assert(kDecodeMaxUnits * 8 <= (int64_t)ca::kHeaderBytes, "epoch words in the header");
+constexpr int kDecodeMaxTopk = 256;      // selected rows per query the finish kernel holds in LDS
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -172,7 +165,7 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         P.lmax = (int64_t)P.wpu * P.seg;
         P.nwg = 0;
         const size_t slot_bytes = ((size_t)(3 * P.nqv * P.wpu) * sizeof(uint32_t) + 255) & ~(size_t)255;
-        P.slots_offset = ca::kHeaderBytes;
+        P.slots_offset = 0;
         P.lists_offset = P.slots_offset + slot_bytes;
         P.win_offset = (P.lists_offset + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) + 255) & ~(size_t)255;
         P.ws_bytes = P.win_offset + (size_t)P.nqv * (size_t)(P.d + 2) * sizeof(float);
@@ -182,25 +175,23 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         // Blocks of 256 rows from row 0 cover rows 1..rmax.
         const int64_t nblk = (P.rmax + kStreamBlockRows) / kStreamBlockRows;
         const double kb = (double)P.units * (double)(nblk * kStreamBlockRows) * P.G * 4.0;
-        // (Index math of the decode kernel in 32 bits; one arrival counter per unit in the
-        // workspace header.)
+        // (Index math of the decode kernels in 32 bits.)
         const int64_t wpb = (nblk + 1) / 2;
         if (kb <= kStreamKeysMax && P.units * nblk < ((int64_t)1 << 31) && nvec < ((int64_t)1 << 31) &&
-            P.units <= kDecodeMaxUnits && P.topk <= kDecodeMaxTopk &&
-            P.units * (wpb + 1) < ((int64_t)1 << 31)) {
+            P.topk <= kDecodeMaxTopk && P.units * wpb < ((int64_t)1 << 31) &&
+            P.units * P.G < ((int64_t)1 << 31)) {
             P.stream = true;
             P.nblk = (int)nblk;
             P.rstride = nblk * kStreamBlockRows;
             P.wpu = 1;
-            P.nwg = P.units * (wpb + 1);
+            P.nwg = P.units * wpb;
             P.lmax = 0;
             P.lists_offset = 0;
             P.tile_rows = row_bytes >= 256 ? 16 : 32;
             auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
             const size_t rq = (size_t)P.units * P.G * (size_t)P.nblk;  // (unit, query, block) records
-            P.summ_offset = ca::kHeaderBytes;
-            P.zsum_offset = up(P.summ_offset + rq * 4 * sizeof(uint64_t));
-            P.scratch_offset = up(P.zsum_offset + rq * 2 * sizeof(float));
+            P.summ_offset = 0;
+            P.scratch_offset = up(P.summ_offset + rq * 2 * sizeof(uint4));
             P.ws_bytes = P.scratch_offset + (size_t)P.units * P.G * (size_t)P.rstride * sizeof(uint32_t);
             return CA_OK;
         }
@@ -220,7 +211,7 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     const double list_bytes = (double)P.nqv * (double)P.lmax * 8.0;
     if (list_bytes > 9.0e18) return fail(CA_ERR_UNSUPPORTED, "workspace size overflows");
     const size_t slot_bytes = ((size_t)(3 * P.nqv * P.wpu) * sizeof(uint32_t) + 255) & ~(size_t)255;
-    P.slots_offset = ca::kHeaderBytes;
+    P.slots_offset = 0;
     P.lists_offset = P.slots_offset + slot_bytes;
     P.ws_bytes = P.candidates ? P.lists_offset + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) : 0;
     if (ca::topk_lds_bytes(P) > 64 * 1024)

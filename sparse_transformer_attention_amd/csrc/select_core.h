@@ -174,6 +174,35 @@ __device__ __forceinline__ uint64_t wave_kth_u64(const uint64_t (&kr)[E], int ke
     return t;
 }
 
+// A value t that at least `keep` of the wavefront's non-zero values v[0..E) reach (at least `keep`
+// of them must be non-zero), found bit by bit from the highest bit where they differ; the
+// search stops as soon as at most keep + slack values reach t, so without equal values near the
+// keep-th largest that many at most reach it.
+template <int E>
+__device__ __forceinline__ uint32_t wave_loose_kth_u32(const uint32_t (&v)[E], int keep, int slack) {
+    uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (v[e]) { mx = v[e] > mx ? v[e] : mx; mn = v[e] < mn ? v[e] : mn; }
+    }
+    mx = wave_max_u32_dpp(mx);
+    mn = wave_min_u32_dpp(mn);
+    if (mx == mn) return mx;
+    const int hb = 31 - __builtin_clz(mx ^ mn);
+    uint32_t t = hb >= 31 ? 0u : (mx >> (hb + 1)) << (hb + 1);
+    for (int bit = hb; bit >= 0; --bit) {
+        const uint32_t c = t | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(v[e] >= c));
+        if (cnt >= keep) {
+            t = c;
+            if (cnt <= keep + slack) break;
+        }
+    }
+    return t;
+}
+
 // A value that at least `keep` of the wavefront's non-zero values v[0..E) reach, close to their
 // keep-th largest: the largest P whose bits above the highest bit hb where the values differ are
 // theirs, whose bits below lb = hb - 9 are 0, and which `keep` values reach (the lower edge of the
