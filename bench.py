@@ -9,7 +9,7 @@ step (32 query heads, 8 KV heads, d=128, bf16, W=256, k=64). Distinct KV buffer 
 between steps so that the key stream comes from HBM and not from the 256 MB last-level cache.
 
 Prints one JSON line: query vectors/s from a clean timed loop, the step's algorithmic HBM GB/s,
-the roofline of the dominant kernel (on the decode path the one kernel that is the whole step;
+the roofline of the dominant kernel (on the decode path decode_stream, which reads every key row;
 on the prefill paths the score stage; durations from HIP events the library records around its
 own launches on the stream it uses, in a second pass over the same steps), and the CPU oracle
 timed on the host.
@@ -30,12 +30,12 @@ sys.path.insert(0, ROOT)
 METRIC = "condensate-attn decode queries/sec + achieved HBM GB/s at 131K ctx (1 GPU)"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of the chip
-# HBM bytes per launch of the decode kernel (the whole step on this workload) from rocprofv3
+# HBM bytes per launch of decode_stream (the dominant kernel of the decode step) from rocprofv3
 # FETCH_SIZE / WRITE_SIZE counters, valid while the kernel's sources hash to the recorded value.
-COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_decode_131k_gqa_bf16_counters.md")
+COUNTERS = os.path.join(ROOT, "profiles", "decode_stream_decode_131k_gqa_bf16_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_transformer_attention_amd", "csrc", f)
-                  for f in ("decode_kernels.hip", "attend_core.h", "merge_core.h", "score_core.h",
-                            "select_core.h", "device_utils.h", "ca_internal.h")]
+                  for f in ("decode_stream.hip", "decode_core.h", "score_core.h", "device_utils.h",
+                            "ca_internal.h")]
 
 
 def kernel_sources_sha() -> str:
@@ -240,23 +240,23 @@ def main():
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": pass_s * 1e6,
         }
-    if "decode" in prof and not args.dense:
-        # Decode path: one kernel is the whole step (K stream, selection, set assembly, attend),
-        # so its algorithmic bytes are the step's.
-        launches, dec_ms = prof["decode"]
+    if "decode_stream" in prof and not args.dense:
+        # Decode path: decode_stream reads every candidate key row once (the score stage);
+        # decode_finish (selection, set assembly, attend) follows it.
+        launches, dec_ms = prof["decode_stream"]
         dec_avg_s = dec_ms / max(1, launches) / 1e3
-        achieved = step_bytes / dec_avg_s / 1e9
+        achieved = score_bytes / dec_avg_s / 1e9
         # The recorded counters are those of the kernel without the mass diagnostic.
         traffic = recorded_traffic(w.name) if not args.mass else None
         roofline = {
-            "kernel": "decode (the whole step: scores, selection, set, attend)",
+            "kernel": "decode_stream (score stage: every key row once, block records)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": step_bytes,
+            "algorithmic_bytes_per_launch": score_bytes,
             "avg_launch_us": dec_avg_s * 1e6,
         }
     elif "mfma_bound" not in prof and not args.dense:

@@ -32,8 +32,8 @@
  *   - Nothing is thrown across this ABI. Calls on different streams may run concurrently as
  *     long as they do not share a workspace.
  *
- * Supported: d in {64, 128}; n < 2^31; heads % kv_heads == 0; W >= 1; 0 <= topk <= 512;
- * 1 + W + topk <= CA_MAX_SET.
+ * Supported: d in {64, 128}; n < 2^31; batch * heads * nq < 2^31; heads % kv_heads == 0; W >= 1;
+ * 0 <= topk <= 512; 1 + W + topk <= CA_MAX_SET.
  */
 #ifndef CONDENSATE_H
 #define CONDENSATE_H
@@ -69,15 +69,16 @@ typedef struct {
     int32_t dtype;     /* ca_dtype of q, k, v */
     int32_t chunk;     /* scoring strategy. 0 = automatic: bf16 problems with many query
                           vectors per KV head take the matrix-core passes; decode-shaped
-                          problems (at most 256 units of up to 4 query vectors per KV head,
-                          topk <= 256, and a fallback key buffer of 4 bytes per query vector
-                          and cache row within 1 GiB) take one kernel that streams K once,
-                          keeps block records of the scores and, in one finisher workgroup per
-                          unit, selects and attends; anything else the chunked select below
-                          with 256-row chunks. 256, 512 or 1024 = always the chunked select (one
-                          pass that keeps running top-k lists per chunk of that many key rows;
-                          a hint: halved while its buffers would exceed 64 KiB of LDS). Results
-                          do not depend on it. */
+                          problems (topk <= 256 and a fallback key buffer of 4 bytes per query
+                          vector and cache row within 1 GiB) take two kernels: one streams K
+                          once and keeps a record of each block of 256 rows per query vector
+                          (its four best rows and a bound on the rest), the other selects from
+                          the records, assembles C_i and attends, one workgroup per query
+                          vector; anything else the chunked select below with 256-row chunks.
+                          256, 512 or 1024 = always the chunked select (one pass that keeps
+                          running top-k lists per chunk of that many key rows; a hint: halved
+                          while its buffers would exceed 64 KiB of LDS). Results do not depend
+                          on it. */
 } ca_params;
 
 /* The one-call form, as the method is usually stated: float32 q/k/v, batch 1, every position
@@ -91,16 +92,13 @@ int ca_condensate_attention(const void *q, const void *k, const void *v, int64_t
 /* Bytes of device workspace that ca_condensate_attention_ex / ca_condensate_select /
  * ca_condensate_attention_mass_ex need for problem p (may be 0). Host only. The workspace needs
  * no initialisation and may serve any sequence of problems whose size it covers: each call
- * clears or tags what it relies on, on the call's stream. Its first CA_WORKSPACE_HEADER bytes
- * hold per-unit epoch words of the decode kernel (records of one call are told from those of
- * earlier calls by them); no call stores anything else there. Calls that share a workspace
- * must be ordered (same stream, or events).
- * Size: on decode-shaped problems about 40 bytes per (unit, query vector of the unit, block of
- * 256 cache rows) for block records, plus 4 bytes per query vector and cache row for the exact
- * fallback's keys (written only when a query's candidates exceed what the kernel holds in LDS:
- * exact ties at the threshold, dense clusters of high scores): 16 MiB at 131,072 rows and 32
- * query vectors, 512 MiB at 1,048,576 rows and 128 query vectors. */
-#define CA_WORKSPACE_HEADER 65536
+ * writes what it reads, or clears it, on the call's stream. Calls that share a workspace must
+ * be ordered (same stream, or events).
+ * Size: on decode-shaped problems 32 bytes per (query vector, block of 256 cache rows) for the
+ * block records, plus 4 bytes per query vector and cache row for the exact fallback's keys
+ * (written only when a query's candidates exceed what the kernel holds in LDS: exact ties at
+ * the threshold, dense clusters of high scores): 16.5 MiB at 131,072 rows and 32 query vectors,
+ * 528 MiB at 1,048,576 rows and 128 query vectors. */
 int ca_workspace_size(const ca_params *p, size_t *bytes);
 
 /* Full method, asynchronous on `stream`, caller-provided workspace (ws may be NULL only if
@@ -151,8 +149,9 @@ int ca_attention_on_subset(const ca_params *p, const void *q, const void *k, con
  * kernel name (launches, summed milliseconds) into out[0..capacity), setting *count to the
  * number of kernels seen. Not meant to be used from several threads at once. */
 typedef struct {
-    const char *kernel;  /* static name: "decode", "score_select", "mfma_bound", "mfma_cand",
-                            "mfma_window", "finish", "attend" or "dense" */
+    const char *kernel;  /* static name: "decode_stream", "decode_finish", "score_select",
+                            "mfma_bound", "mfma_cand", "mfma_window", "finish", "attend" or
+                            "dense" */
     int64_t launches;
     double total_ms;
 } ca_kernel_time;

@@ -247,7 +247,7 @@ def profile_start(reserve_launches: int = 0):
 
 def profile_stop() -> dict:
     """Stop profiling; returns {kernel name: (launches, total milliseconds)}."""
-    arr = (KernelTime * 8)()
+    arr = (KernelTime * 16)()
     n = ctypes.c_int32(0)
-    _check(load().ca_profile_stop(arr, 8, ctypes.byref(n)), "ca_profile_stop")
+    _check(load().ca_profile_stop(arr, 16, ctypes.byref(n)), "ca_profile_stop")
     return {arr[i].kernel.decode(): (int(arr[i].launches), float(arr[i].total_ms)) for i in range(n.value)}

@@ -33,15 +33,13 @@ struct Plan {
     int64_t nwg;          // score_topk workgroups
     int64_t lmax;         // candidate slots per query (wpu * seg)
     int seg;              // keys per segment: topk (score_topk) or kMfmaSeg (MFMA passes)
-    size_t slots_offset;  // byte offset of the per-query slot words (after the header)
+    size_t slots_offset;  // byte offset of the per-query slot words
     size_t lists_offset;  // byte offset of the lists in the workspace
     size_t ws_bytes;      // total workspace
-    // Decode path (score_keys, then finish reading its tile summaries): rows per unit covered
-    // (rstride = 256 nblk), blocks of 256 rows per unit, rows per tile, and the offsets of the
-    // summaries [units][G][rstride / tile_rows] (best key u32; second key, offsets and the
-    // third key's upper half as one 8-byte word), the block maxima [units][nblk][G] and the
-    // finish kernel's scratch keys
-    // [nqv][rstride] (written only when a query's candidates exceed what LDS holds).
+    // Decode path (decode_stream, then decode_finish reading its block records): blocks of 256
+    // rows per unit (nblk, rstride = 256 nblk rows covered), the records [units][G][nblk] of 32
+    // bytes at summ_offset and the fallback's scratch keys [units][G][rstride] at scratch_offset
+    // (written only for a query whose candidates exceed what LDS holds).
     bool stream;
     // Prefill path with bf16 inputs (mfma_select bound + cand, then finish over the segments):
     // taus [nqv] in the first words of the workspace, the lengths and lists as above with
@@ -50,37 +48,29 @@ struct Plan {
     size_t win_offset;    // MFMA path: anchor-and-window partials [nqv][d + 2] floats
     int64_t rstride;
     int nblk;
-    int tile_rows;
-    size_t best1_offset, rest_offset, bmax_offset, scratch_offset;
-    size_t zsum_offset;   // mass diagnostic: [units][nblk][G] (largest score, sum) float pairs
-    size_t summ_offset;   // decode kernel: block records [units][G][nblk][8] 64-bit words
+    size_t summ_offset, scratch_offset;
 };
 
-// Every plan's workspace starts with this header: the decode kernel's epoch words (one 64-bit
-// word per unit, at most kHeaderBytes / 8 units). Nothing else is stored there.
-constexpr size_t kHeaderBytes = 64 * 1024;
 
 // Launchers (enqueue only; return the hipError_t of the last launch).
 hipError_t launch_score_select(const Plan &pl, const void *q, const void *k, void *ws,
                                hipStream_t s);
 // Merge + set assembly (+ restricted softmax times V when out != nullptr), one workgroup per
-// query vector.
-// mass != nullptr (decode path only): also [nqv][4] = excluded mass, anchor, window, top-k.
+// query vector (chunked and MFMA paths).
 hipError_t launch_finish(const Plan &pl, const void *ws, const void *q, const void *k,
-                         const void *v, int32_t *out_idx, float *out, hipStream_t s,
-                         float *mass = nullptr);
+                         const void *v, int32_t *out_idx, float *out, hipStream_t s);
 // Restricted softmax times V on caller-supplied index sets.
 hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k, const void *v,
                                     const int32_t *idx, float *out, hipStream_t s);
 size_t topk_lds_bytes(const Plan &pl);
-// mass: also the per-block sums of the mass diagnostic (zsum_offset).
-hipError_t launch_score_keys(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
-                             bool mass = false);
-// Decode path in one kernel: scores, block records, and per unit in its last-arriving workgroup
-// the exact top-k', out_idx and (out != nullptr) the restricted softmax times V (mass != nullptr:
-// also the mass diagnostic).
-hipError_t launch_decode(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
-                         int32_t *out_idx, float *out, float *mass, hipStream_t s);
+// Decode path, first kernel: every key row scored once; per block of 256 rows and query vector a
+// record of its best rows (mass: also the block's softmax sums).
+hipError_t launch_decode_stream(const Plan &pl, const void *q, const void *k, void *ws, bool mass,
+                                hipStream_t s);
+// Decode path, second kernel: per query vector the exact top-k' from the records, out_idx and
+// (out != nullptr) the restricted softmax times V (mass != nullptr: also the mass diagnostic).
+hipError_t launch_decode_finish(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
+                                int32_t *out_idx, float *out, float *mass, hipStream_t s);
 // Query blocks of 16 per wavefront of the two MFMA passes (16 * QB * kMfmaWaves query vectors per
 // workgroup).
 // Bound pass, per d. Measured: 3 at d = 64 (more products per operand read, 2 wavefronts per

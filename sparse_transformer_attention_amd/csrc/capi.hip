@@ -13,10 +13,10 @@
 namespace {
 
 // ---- measurement hooks: HIP events around each launch while profiling is on ----------------
-enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_BOUND = 3, K_CAND = 4, K_DECODE = 5, K_WINDOW = 6,
-       K_DENSE = 7, K_COUNT = 8 };
+enum { K_SCORE = 0, K_FINISH = 1, K_ATTEND = 2, K_BOUND = 3, K_CAND = 4, K_DSTREAM = 5, K_WINDOW = 6,
+       K_DENSE = 7, K_DFINISH = 8, K_COUNT = 9 };
 const char *const kKernelNames[K_COUNT] = {"score_select", "finish", "attend", "mfma_bound", "mfma_cand",
-                                           "decode", "mfma_window", "dense"};
+                                           "decode_stream", "mfma_window", "dense", "decode_finish"};
 
 struct Profiler {
     std::mutex mu;
@@ -83,7 +83,7 @@ int hip_fail(hipError_t e, const char *what) {
 constexpr int kMinChunk = 256, kMaxChunk = 1024, kDefaultChunk = 256;
 constexpr int kMaxTopk = 512;            // running lists hold topk + chunk <= 1024 keys
 constexpr int64_t kTargetBlocks = 1024;  // score_topk workgroups to aim for (4 per CU)
-constexpr int kStreamBlockRows = 256;    // score_keys rows per workgroup
+constexpr int kStreamBlockRows = 256;    // key rows per block record of the decode path
 constexpr double kStreamKeysMax = 1024.0 * 1024 * 1024;  // key buffer budget (bytes)
 constexpr int64_t kMfmaMinVectors = 64;  // query vectors per KV head for the MFMA passes
 constexpr int kMfmaMaxTopk = 128;        // classes of the MFMA bound
@@ -121,6 +121,10 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     P.B = p->batch; P.Hq = p->heads; P.Hkv = p->kv_heads; P.g = p->heads / p->kv_heads;
     P.d = p->d; P.W = p->W; P.topk = p->topk; P.dtype = p->dtype; P.n = p->n; P.nq = p->nq;
     P.nqv = (int64_t)P.B * P.Hq * P.nq;
+    // (32-bit query-vector math in the kernels; grids of one workgroup per query vector.)
+    if (P.nqv >= ((int64_t)1 << 31))
+        return fail(CA_ERR_UNSUPPORTED, "batch * heads * nq = %lld query vectors exceeds 2^31 - 1",
+                    (long long)P.nqv);
     P.cap = 1 + P.W + P.topk;
     P.rmax = (P.n - 1) - P.W;
 
@@ -145,14 +149,13 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         if (ca::topk_lds_bytes(P) <= 64 * 1024 || chunk <= kMinChunk) break;
         chunk /= 2;
     }
-    // Decode-shaped problems stream K once into a key buffer (score_keys; the finish kernel
-    // reads it) when that buffer stays within kStreamKeysMax; others use the fused score_topk
-    // kernel.
+    // Decode-shaped problems stream K once (decode_stream, block records; decode_finish reads
+    // them) when the fallback's key buffer stays within kStreamKeysMax; others use the fused
+    // score_topk kernel.
     P.stream = false;
     P.mfma = false;
     P.seg = 1;
     P.win_offset = 0;
-    P.zsum_offset = 0;
     // Many bf16 query vectors per KV head: the MFMA passes (bound, then candidate lists in the
     // segment layout of the chunked path: 4 segments of kMfmaSeg keys per query). They address
     // a KV head's key rows with 32-bit byte offsets.
@@ -187,7 +190,6 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
             P.nwg = P.units * wpb;
             P.lmax = 0;
             P.lists_offset = 0;
-            P.tile_rows = row_bytes >= 256 ? 16 : 32;
             auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
             const size_t rq = (size_t)P.units * P.G * (size_t)P.nblk;  // (unit, query, block) records
             P.summ_offset = 0;
@@ -206,7 +208,7 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     P.nwg = P.wpu > 1 ? P.units * P.wpu : P.units;
     P.seg = P.topk > 0 ? P.topk : 1;
     P.lmax = (int64_t)P.wpu * P.seg;
-    if (P.nwg > (int64_t)UINT32_MAX / 256 || P.nqv > (int64_t)UINT32_MAX / 256)
+    if (P.nwg > (int64_t)UINT32_MAX / 256)
         return fail(CA_ERR_UNSUPPORTED, "problem too large for one launch");
     const double list_bytes = (double)P.nqv * (double)P.lmax * 8.0;
     if (list_bytes > 9.0e18) return fail(CA_ERR_UNSUPPORTED, "workspace size overflows");
@@ -247,11 +249,18 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
             if (e != hipSuccess) return hip_fail(e, "mfma_window launch");
         }
     } else if (pl.candidates && pl.stream) {
-        // One kernel: scores, selection, set assembly and attend.
-        ProfScope pd(K_DECODE, s);
-        e = ca::launch_decode(pl, q, k, v, ws, out_idx, out, mass, s);
-        pd.done();
-        if (e != hipSuccess) return hip_fail(e, "decode launch");
+        // Two kernels: the key stream with its block records, then per query vector the
+        // selection, set assembly and attend.
+        {
+            ProfScope pd(K_DSTREAM, s);
+            e = ca::launch_decode_stream(pl, q, k, ws, mass != nullptr, s);
+            pd.done();
+            if (e != hipSuccess) return hip_fail(e, "decode_stream launch");
+        }
+        ProfScope pf(K_DFINISH, s);
+        e = ca::launch_decode_finish(pl, q, k, v, ws, out_idx, out, mass, s);
+        pf.done();
+        if (e != hipSuccess) return hip_fail(e, "decode_finish launch");
         return CA_OK;
     } else if (pl.candidates) {
         ProfScope ps(K_SCORE, s);
@@ -260,7 +269,7 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
         if (e != hipSuccess) return hip_fail(e, "score_topk launch");
     }
     ProfScope pf(K_FINISH, s);
-    e = ca::launch_finish(pl, pl.candidates ? ws : nullptr, q, k, v, out_idx, out, s, mass);
+    e = ca::launch_finish(pl, pl.candidates ? ws : nullptr, q, k, v, out_idx, out, s);
     pf.done();
     if (e != hipSuccess) return hip_fail(e, "finish launch");
     return CA_OK;

@@ -1,308 +1,32 @@
-// Condensate attention for decode-shaped problems on gfx950 (pages of "The Condensate Theorem",
-// metaphor-xennon blog: section 2.1 Definition 1, C_i = {0} u {i-W+1..i} u Top-k_i; section
-// 2.2.3, the top-k part over R_i = {1..i-W}; section 2.3, the softmax restricted to C_i times V).
+// decode_finish: the end of the decode path on gfx950, one workgroup per query vector (pages of
+// "The Condensate Theorem", metaphor-xennon blog: section 2.1 Definition 1, C_i = {0} u
+// {i-W+1..i} u Top-k_i; section 2.2.3, the top-k part over R_i = {1..i-W}, ties to the smaller
+// position; section 2.3, the softmax restricted to C_i times V; section 3.2.2, the mass outside
+// C_i).
 //
-// Work unit: (batch, KV head, query group) with up to G query vectors reading one KV head. Two
-// kernels:
-//   decode_stream   per unit, wpb workgroups of two blocks of 256 key rows each (interleaved over
-//                   the units: workgroup s serves unit s % units). Every K row is read once
-//                   (16-byte non-temporal loads, LPR lanes per row) and dotted with the unit's G
-//                   queries in fp32 (row_key); the order-preserving 32-bit keys (0 for rows
-//                   outside R_i of a query) are staged in LDS. Per block and query, 16 lanes
-//                   reduce the block's keys to a 32-byte record: four of its rows (key, offset)
-//                   and a key X that every other row of the block stays at or below (with the
-//                   mass diagnostic also the block's largest score m_b and its sum of
-//                   exp2((s - m_b) * scale)).
-//   decode_finish   one workgroup per query vector. All of its wavefronts compute the anchor-and-
-//                   window softmax partials while the records load (one per thread). A bound T0
-//                   comes from the blocks' best keys: the k'-th largest of them (k' blocks, so k'
-//                   distinct rows, reach it: no row below it can be in the top k'). The record
-//                   rows whose ranking key (score_key << 32) | ~position reaches the bound are
-//                   gathered and cut to their exact top k' (one wavefront). A block whose X
-//                   reaches the k'-th key has rows beyond its record that may rank: those are
-//                   scored again (row_key, the same bits) and the cut repeated. C_i goes to
-//                   out_idx, and the top-k rows' partials (weights exp2((s - m) * scale), s read
-//                   back from the keys) merge with the window's into the output. Too many
-//                   candidates or such blocks (dense clusters of high scores, exact ties) switch
-//                   the query to an exact fallback: all its candidate rows scored into scratch
-//                   keys and a workgroup radix select over them.
-#include <type_traits>
-
+// The records of decode_stream and the anchor and window rows are requested first. A bound T0
+// comes from the blocks' best keys (k' blocks, so k' distinct rows, reach it: no row below it
+// can be in the top k'). The record rows whose ranking key (score_key << 32) | ~position reaches
+// the bound are gathered in a fixed order and cut to their exact top k' (one wavefront). A block
+// whose X reaches the k'-th key has rows beyond its record that may rank: those are scored again
+// (row_key, the same bits) and the cut repeated. The V rows of the top k' are requested while
+// their places in out_idx are counted; the anchor-and-window partial and the top-k partials
+// (weights exp2((s - m) * scale), s read back from the keys) merge into the output. Too many
+// candidates or such blocks (dense clusters of high scores, exact ties) switch the query to an
+// exact fallback: all its candidate rows scored into scratch keys and a workgroup radix select.
 #include "attend_core.h"
-#include "ca_internal.h"
-#include "device_utils.h"
+#include "decode_core.h"
 #include "merge_core.h"
-#include "score_core.h"
 #include "select_core.h"
 
 namespace ca {
+namespace dec {
 namespace {
 
-constexpr int kRows = 256;         // key rows per block
-constexpr int kBW = 2;             // blocks per stream workgroup
-constexpr int kNT = kBW * 256;     // threads per workgroup (both kernels)
-constexpr int kWaves = kNT / 64;
 constexpr int kCand = 1024;        // candidate keys per query held in LDS
 constexpr int kDef = 64;           // blocks whose X reaches the threshold, held in LDS
 constexpr int kResc = 8;           // such blocks scored again on the common path
 constexpr int kSelMax = 256;       // largest k' of the common path (larger: the fallback)
-
-struct DecodeArgs {
-    int64_t n, nq;
-    int Hq, Hkv, g, W, topk, cap;
-    int64_t groups;     // units per (batch, KV head)
-    int nblk;           // blocks of 256 rows per unit (rows 0 .. 256 nblk - 1)
-    uint32_t nvec;      // query vectors per KV head (g * nq)
-    int row_base;       // n - nq - W: last candidate row of vector idx is row_base + idx / g
-    uint32_t units;     // work units
-    float scale_log2e;
-    int64_t rstride;    // scratch keys per query (256 nblk)
-    uint4 *rec;         // [units][G][nblk][2] records: {k1, k2, k3, k4}, {offsets o1..o4 (8 bits
-                        // each), X, m_b, l_b (float bits; mass diagnostic only)}
-    uint32_t *scratch;  // [units][G][rstride] fallback keys
-    int32_t *out_idx;   // [nqv][cap]
-    float *out;         // [nqv][D] (null: select only)
-    float *mass;        // [nqv][4] (null: no diagnostic)
-};
-
-template <int N>
-__device__ __forceinline__ uint32_t ror_u32(uint32_t x) { return dpp_u32<0x120 + N>(x, x); }
-
-// ---- reductions over the 16 lanes of a DPP row (every lane gets the result) ----
-
-__device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
-#define CA_ROW_MAX_STEP(N)                                                            \
-    {                                                                                 \
-        const uint32_t hi = ror_u32<N>((uint32_t)(v >> 32)), lo = ror_u32<N>((uint32_t)v); \
-        const uint64_t o = ((uint64_t)hi << 32) | lo;                                 \
-        v = o > v ? o : v;                                                            \
-    }
-    CA_ROW_MAX_STEP(8) CA_ROW_MAX_STEP(4) CA_ROW_MAX_STEP(2) CA_ROW_MAX_STEP(1)
-#undef CA_ROW_MAX_STEP
-    return v;
-}
-__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
-    uint32_t o;
-    o = ror_u32<8>(v); v = o > v ? o : v;
-    o = ror_u32<4>(v); v = o > v ? o : v;
-    o = ror_u32<2>(v); v = o > v ? o : v;
-    o = ror_u32<1>(v); v = o > v ? o : v;
-    return v;
-}
-__device__ __forceinline__ float row16_sum_f32(float x) {
-    x += __uint_as_float(ror_u32<8>(__float_as_uint(x)));
-    x += __uint_as_float(ror_u32<4>(__float_as_uint(x)));
-    x += __uint_as_float(ror_u32<2>(__float_as_uint(x)));
-    x += __uint_as_float(ror_u32<1>(__float_as_uint(x)));
-    return x;
-}
-
-// Streaming layout of a key row (as in every score kernel: row_key gives the same bits).
-template <typename T, int D>
-struct StreamShape {
-    static constexpr int EB = sizeof(T);
-    static constexpr int RB = D * EB;                // bytes per key row
-    static constexpr int LPR = RB >= 256 ? 16 : 8;   // lanes per row
-    static constexpr int RPG = 64 / LPR;             // rows per wavefront load
-    static constexpr int P = RB / (16 * LPR);        // 16-byte loads per lane per row
-    static constexpr int NG = 64 / RPG;              // row groups of a wavefront's 64 rows
-    static constexpr int U = 16 / P < NG ? 16 / P : NG;  // row groups per round
-    static constexpr int TR = 4 * RPG;               // rows per staged tile
-    static_assert(P >= 1 && NG % U == 0 && U % 4 == 0, "layout");
-};
-
-// Row offset (within its block) of staged position p of a block: a staged tile of TR rows holds
-// row RPG * (p % 4) + p / 4 of the tile at position p.
-template <int TR, int RPG>
-__device__ __forceinline__ int staged_row(int p) {
-    return TR * (p / TR) + RPG * (p % 4) + (p % TR) / 4;
-}
-
-// One query vector of a unit: where it sits and what its set looks like.
-struct QInfo {
-    bool valid;
-    uint32_t qv;              // flat query vector (b*Hq + h)*nq + r
-    int i, rl, kp, wlo, base, wcount, nbq;
-};
-
-template <int G>
-__device__ __forceinline__ QInfo query_info(const DecodeArgs &a, uint32_t bk, uint32_t grp, int t) {
-    QInfo qi;
-    const uint32_t g = (uint32_t)a.g;
-    const uint32_t b = bk / (uint32_t)a.Hkv, kvh = bk - b * (uint32_t)a.Hkv;
-    const uint32_t idx = grp * G + (uint32_t)t;
-    qi.valid = idx < a.nvec;
-    const uint32_t idc = qi.valid ? idx : a.nvec - 1;
-    const uint32_t qh = idc / g, hh = idc - qh * g;
-    qi.qv = (b * (uint32_t)a.Hq + kvh * g + hh) * (uint32_t)a.nq + qh;
-    qi.i = (int)(a.n - a.nq) + (int)qh;
-    qi.rl = qi.i - a.W;
-    const int n_r = qi.rl >= 1 ? qi.rl : 0;
-    qi.kp = a.topk < n_r ? a.topk : n_r;
-    qi.wlo = qi.i - a.W + 1 > 0 ? qi.i - a.W + 1 : 0;
-    qi.base = qi.wlo > 0 ? 1 : 0;
-    qi.wcount = qi.i - qi.wlo + 1;
-    qi.nbq = qi.rl >= 1 ? (qi.rl >> 8) + 1 : 0;
-    return qi;
-}
-
-// The unit's G query slices of this lane (zero past the last query vector), stream layout.
-template <typename T, int D, int G>
-__device__ __forceinline__ void load_query_slices(const T *__restrict__ q, const DecodeArgs &a, uint32_t bk,
-                                                  uint32_t grp, int lane, uint4 (&qr)[G][StreamShape<T, D>::P]) {
-    using S = StreamShape<T, D>;
-    const uint32_t g = (uint32_t)a.g;
-    const int sl = lane % S::LPR;
-#pragma unroll
-    for (int t = 0; t < G; ++t) {
-        const uint32_t idx = grp * G + t;
-        if (idx < a.nvec) {
-            const uint32_t qh = idx / g, hh = idx - qh * g;
-            const uint4 *src = reinterpret_cast<const uint4 *>(q + (((int64_t)bk * g + hh) * a.nq + qh) * D);
-#pragma unroll
-            for (int p = 0; p < S::P; ++p) qr[t][p] = src[p * S::LPR + sl];
-        } else {
-#pragma unroll
-            for (int p = 0; p < S::P; ++p) qr[t][p] = make_uint4(0, 0, 0, 0);
-        }
-    }
-}
-
-// ---- decode_stream: keys of two blocks into LDS, then the block records ---------------------
-template <typename T, int D, int G, bool MASS>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 5 : 4))) void decode_stream_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, DecodeArgs a) {
-    __shared__ uint32_t kst[G][kBW * kRows];  // keys of the workgroup's rows, per query
-    // Workgroup s: unit s % units, its part s / units.
-    const uint32_t part = blockIdx.x / a.units;
-    const uint32_t uu = blockIdx.x - part * a.units;
-    using S = StreamShape<T, D>;
-    constexpr int LPR = S::LPR, RPG = S::RPG, P = S::P, NG = S::NG, U = S::U, TR = S::TR;
-    constexpr int WROWS = kBW * kRows;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t ng = (uint32_t)a.groups;
-    const int wg_row0 = (int)part * WROWS;
-    const int bi = wg_row0 / kRows + wave / 4;
-    const uint32_t bk = uu / ng, grp = uu - bk * ng;
-    const uint32_t g = (uint32_t)a.g;
-    const int sl = lane % LPR;
-    const bool writer = sl % (LPR / G) == 0;
-    const int my_t = sl / (LPR / G);
-    const uint32_t idx0 = grp * G;
-    const uint32_t idx_last = (idx0 + G - 1 < a.nvec ? idx0 + G - 1 : a.nvec - 1);
-    const int rl_max = a.row_base + (int)(idx_last / g);
-    const int row0 = bi * kRows;
-    const bool live = bi < a.nblk && row0 <= rl_max;
-    const int rows_end = (row0 + kRows < rl_max + 1) ? row0 + kRows : rl_max + 1;
-    const int rlo = row0 > 1 ? row0 : 1;  // row 0 (the anchor) is no candidate
-    const uint4 *kbase = reinterpret_cast<const uint4 *>(k + (int64_t)bk * a.n * D);
-    const int wrow0 = row0 + (wave % 4) * 64;
-    if (live && wrow0 < rows_end) {
-        uint4 qr[G][P];
-        load_query_slices<T, D, G>(q, a, bk, grp, lane, qr);
-        int my_rlast = 0;
-        {
-            const uint32_t idx = idx0 + my_t;
-            if (idx < a.nvec) my_rlast = a.row_base + (int)(idx / g);
-        }
-#pragma unroll
-        for (int r = 0; r < NG / U; ++r) {
-            uint4 kr[U][P];
-#pragma unroll
-            for (int uq = 0; uq < U; ++uq) {
-                int row = wrow0 + (r * U + uq) * RPG + lane / LPR;
-                row = row < rows_end ? row : rows_end - 1;
-                const uint4 *src = kbase + (int64_t)row * (P * LPR);
-#pragma unroll
-                for (int p = 0; p < P; ++p) kr[uq][p] = load_row16_nt(src + p * LPR + sl);
-            }
-#pragma unroll
-            for (int u4 = 0; u4 < U; u4 += 4) {
-                uint32_t kv4[4];
-#pragma unroll
-                for (int gg = 0; gg < 4; ++gg) {
-                    const int uq = u4 + gg;
-                    const uint32_t key = row_key<T, LPR, P, G>(kr[uq], qr, lane);
-                    const int row = wrow0 + (r * U + uq) * RPG + lane / LPR;
-                    kv4[gg] = (row >= rlo && row < rows_end && row <= my_rlast) ? key : 0u;
-                }
-                // Keys of rows tile0 + RPG*gg + lane/LPR as one 16-byte word.
-                const int tile0 = wrow0 + (r * U + u4) * RPG;
-                if (writer)
-                    *reinterpret_cast<uint4 *>(&kst[my_t][tile0 - wg_row0 + 4 * (lane / LPR)]) =
-                        make_uint4(kv4[0], kv4[1], kv4[2], kv4[3]);
-            }
-        }
-    } else {
-        for (int x = lane; x < G * 16; x += 64)
-            *reinterpret_cast<uint4 *>(&kst[x / 16][wrow0 - wg_row0 + 4 * (x % 16)]) = make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();
-    // Records: 16 lanes per (block, query); lane j takes staged positions 16j .. 16j + 15. The
-    // wavefronts without a record to write are done.
-    const int nbw = a.nblk - wg_row0 / kRows < kBW ? a.nblk - wg_row0 / kRows : kBW;
-    if (wave * 4 >= nbw * G) return;
-    const int pr = tid >> 4, j = tid & 15;
-    if (pr >= nbw * G) return;
-    const int b2 = pr / G, t = pr % G;
-    if (idx0 + t >= a.nvec) return;  // no query vector: no record
-    const uint32_t *src = &kst[t][b2 * kRows + 16 * j];
-    uint32_t kk[16];
-#pragma unroll
-    for (int w4 = 0; w4 < 4; ++w4) {
-        const uint4 x = reinterpret_cast<const uint4 *>(src)[w4];
-        kk[4 * w4] = x.x; kk[4 * w4 + 1] = x.y; kk[4 * w4 + 2] = x.z; kk[4 * w4 + 3] = x.w;
-    }
-    // This lane's two best rows as (key << 8 | 255 - offset) (ties: smaller offset first) and
-    // the largest key of its other rows.
-    uint64_t v1 = 0ull, v2 = 0ull;
-    uint32_t k3 = 0u;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const int off = staged_row<TR, RPG>(16 * j + c);
-        const uint64_t x = ((uint64_t)kk[c] << 8) | (uint32_t)(255 - off);
-        const bool b1 = x > v1, b2w = x > v2;
-        const uint32_t drop = (uint32_t)((b1 ? v2 : (b2w ? v2 : x)) >> 8);
-        k3 = drop > k3 ? drop : k3;
-        v2 = b1 ? v1 : (b2w ? x : v2);
-        v1 = b1 ? x : v1;
-    }
-    // Four rows of the block: the largest head of the 16 lanes, four times; X: the largest key
-    // left (heads and the lanes' other rows).
-    uint64_t e[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint64_t m = row16_max_u64(v1);
-        e[r] = m;
-        const bool mine = v1 == m;
-        v1 = mine ? v2 : v1;
-        v2 = mine ? 0ull : v2;
-    }
-    const uint32_t xr = row16_max_u32((uint32_t)(v1 >> 8));
-    const uint32_t x3 = row16_max_u32(k3);
-    const uint32_t X = xr > x3 ? xr : x3;
-    const uint32_t k1 = (uint32_t)(e[0] >> 8);
-    float zl = 0.f, zm = -INFINITY;
-    if constexpr (MASS) {
-        zm = k1 ? key_score(k1) : -INFINITY;
-        float zsum = 0.f;
-#pragma unroll
-        for (int c = 0; c < 16; ++c)
-            if (kk[c]) zsum += exp2f((key_score(kk[c]) - zm) * a.scale_log2e);
-        zl = row16_sum_f32(zsum);
-    }
-    const int blk = wg_row0 / kRows + b2;
-    uint4 *rec = a.rec + (((size_t)uu * G + t) * (size_t)a.nblk + blk) * 2;
-    if (j == 0) {
-        rec[0] = make_uint4(k1, (uint32_t)(e[1] >> 8), (uint32_t)(e[2] >> 8), (uint32_t)(e[3] >> 8));
-    } else if (j == 1) {
-        uint32_t offs = 0u;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) offs |= (255u - (uint32_t)(e[r] & 255u)) << (8 * r);
-        rec[1] = make_uint4(offs, X, __float_as_uint(zm), __float_as_uint(zl));
-    }
-}
 
 // Keeps the top kp of the n distinct non-zero ranking keys list[0..n) (n <= 64 E) in
 // list[0..kp) and returns a value that exactly those reach. One wavefront.
@@ -328,6 +52,7 @@ __device__ __forceinline__ uint64_t keep_top(uint64_t *list, int n, int kp) {
     wave_sync();
     return t;
 }
+
 
 
 // ---- decode_finish ---------------------------------------------------------------------------
@@ -856,53 +581,35 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
 }
 
 }  // namespace
+}  // namespace dec
 
-hipError_t launch_decode(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
-                         int32_t *out_idx, float *out, float *mass, hipStream_t s) {
-    DecodeArgs a;
-    a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g; a.W = pl.W;
-    a.topk = pl.topk; a.cap = pl.cap; a.groups = pl.groups; a.nblk = pl.nblk;
-    a.nvec = (uint32_t)(pl.g * pl.nq);
-    a.row_base = (int)(pl.n - pl.nq - pl.W);
-    a.units = (uint32_t)pl.units;
-    a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
-    a.rstride = pl.rstride;
-    char *w = static_cast<char *>(ws);
-    a.rec = reinterpret_cast<uint4 *>(w + pl.summ_offset);
-    a.scratch = reinterpret_cast<uint32_t *>(w + pl.scratch_offset);
-    a.out_idx = out_idx;
-    a.out = out;
-    a.mass = mass;
-    const bool attend = out != nullptr;
-    const uint32_t wpb = (uint32_t)((pl.nblk + kBW - 1) / kBW);
-    const dim3 sgrid((unsigned)((uint64_t)pl.units * wpb)), fgrid((unsigned)((uint64_t)pl.units * pl.G)), block(kNT);
-    hipError_t e = hipSuccess;
-#define CA_DEC(T, D, G)                                                                               \
+hipError_t launch_decode_finish(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
+                                int32_t *out_idx, float *out, float *mass, hipStream_t s) {
+    using namespace dec;
+    const DecodeArgs a = decode_args(pl, ws, out_idx, out, mass);
+    const dim3 grid((unsigned)((uint64_t)pl.units * pl.G)), block(kNT);
+#define CA_DF(T, D, G)                                                                                \
     do {                                                                                              \
         const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v); \
-        if (mass) hipLaunchKernelGGL((decode_stream_kernel<T, D, G, true>), sgrid, block, 0, s, qt, kt, a); \
-        else hipLaunchKernelGGL((decode_stream_kernel<T, D, G, false>), sgrid, block, 0, s, qt, kt, a); \
-        e = hipGetLastError();                                                                        \
-        if (e != hipSuccess) return e;                                                                \
-        if (mass) hipLaunchKernelGGL((decode_finish_kernel<T, D, G, true, true>), fgrid, block, 0, s, qt, kt, vt, a); \
-        else if (attend) hipLaunchKernelGGL((decode_finish_kernel<T, D, G, true, false>), fgrid, block, 0, s, qt, kt, vt, a); \
-        else hipLaunchKernelGGL((decode_finish_kernel<T, D, G, false, false>), fgrid, block, 0, s, qt, kt, vt, a); \
+        if (mass) hipLaunchKernelGGL((decode_finish_kernel<T, D, G, true, true>), grid, block, 0, s, qt, kt, vt, a); \
+        else if (out) hipLaunchKernelGGL((decode_finish_kernel<T, D, G, true, false>), grid, block, 0, s, qt, kt, vt, a); \
+        else hipLaunchKernelGGL((decode_finish_kernel<T, D, G, false, false>), grid, block, 0, s, qt, kt, vt, a); \
     } while (0)
-#define CA_DEC_G(T, D)                                  \
+#define CA_DF_G(T, D)                                   \
     do {                                                \
-        if (pl.G == 4) CA_DEC(T, D, 4);                 \
-        else if (pl.G == 2) CA_DEC(T, D, 2);            \
-        else CA_DEC(T, D, 1);                           \
+        if (pl.G == 4) CA_DF(T, D, 4);                  \
+        else if (pl.G == 2) CA_DF(T, D, 2);             \
+        else CA_DF(T, D, 1);                            \
     } while (0)
     if (pl.dtype == 1) {
-        if (pl.d == 128) CA_DEC_G(__bf16, 128); else CA_DEC_G(__bf16, 64);
+        if (pl.d == 128) CA_DF_G(__bf16, 128); else CA_DF_G(__bf16, 64);
     } else {
-        if (pl.d == 128) CA_DEC_G(float, 128); else CA_DEC_G(float, 64);
+        if (pl.d == 128) CA_DF_G(float, 128); else CA_DF_G(float, 64);
     }
-#undef CA_DEC_G
-#undef CA_DEC
-    (void)e;
+#undef CA_DF_G
+#undef CA_DF
     return hipGetLastError();
 }
+
 
 }  // namespace ca

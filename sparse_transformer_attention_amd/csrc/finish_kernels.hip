@@ -1,7 +1,6 @@
 // The end of the condensate-attention path on gfx950, one workgroup per query vector:
 //   merge    exact top-k' of the query's candidates (ranking keys (score_key << 32) | ~position;
-//            k' = min(k, |R_i|)): from the segments score_topk left, or from the key buffer of
-//            score_keys, reading only the tiles whose best key reaches the query's bound;
+//            k' = min(k, |R_i|)) from the segments that score_topk or the MFMA passes left;
 //   assemble C_i = {0} u top-k' u {i-W+1..i} in ascending order, written to out_idx (pages of
 //            "The Condensate Theorem", metaphor-xennon blog, section 2.1 Definition 1);
 //   attend   (optional) the restricted softmax times V on that set, straight from LDS.
@@ -25,20 +24,21 @@ struct FinishArgs {
     float scale_log2e;
     const uint32_t *cnt;    // [nqv][wpu] keys in each segment
     const uint64_t *lists;  // [nqv][wpu][seg] segments of candidate ranking keys
-    // Tile-summary path (score_keys): units of G query vectors, blocks and tiles of key rows.
-    int G, nblk, tile_shift;  // rows per tile: 1 << tile_shift
-    int64_t groups, rstride;
-    uint32_t nvec;            // query vectors per KV head (g * nq)
-    const uint32_t *best1;    // [units][G][rstride / tile_rows]
-    const uint2 *rest;        // second key; offsets of the best two (bits 0-15), third key's upper half
-    const uint32_t *bmax;     // [units][nblk][G]
-    uint32_t *scratch;        // [nqv][rstride]
-    const float *win;         // [nqv][D + 2] anchor-and-window partials (MFMA path), or null
-    // Mass diagnostic (tile-summary path; null: off): per-block sums of score_keys and the
-    // output [nqv][4] = excluded mass, anchor, window without position 0, top-k.
-    const float2 *zsum;
-    float *mass;
+    const float *win;       // [nqv][D + 2] anchor-and-window partials (MFMA path), or null
+    int64_t nqv;            // query vectors (the grid covers at least this many workgroups)
 };
+
+// Workgroup grid of one workgroup per query vector: x up to 2^16, y the rest (a launch's
+// workgroups times its width stay below 2^32 per dimension).
+inline dim3 qv_grid(int64_t nqv) {
+    const int64_t gx = nqv < 65536 ? nqv : 65536;
+    return dim3((unsigned)gx, (unsigned)((nqv + gx - 1) / gx));
+}
+
+// Query vector of this workgroup (qv_grid layout); below nqv < 2^31 (the plan's limit).
+__device__ __forceinline__ int64_t block_qv() {
+    return (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+}
 
 // Exact top-kp of n distinct non-zero ranking keys in gathered[0..n) (kp <= n <= kRankSelectMax, n <= NT,
 // so the tail of gathered[] holds a copy clear of them) by rank counting: a key is selected when
@@ -134,220 +134,13 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
     select_exact<NT>(n, (int64_t)wpu * topk, key_at, kp, js, sel, gathered, sh);
 }
 
-// Candidates from the tile summaries of score_keys. The query's bound thr is the lower edge of
-// the 10-bit radix bin that holds the k'-th largest of its block maxima (or of its tile maxima when
-// there are fewer than 2k' blocks): k' distinct rows reach it, so it is a lower bound of the
-// query's k-th key. Every key that reaches thr lies in a tile whose best key reaches it; such a
-// tile contributes its one or two best rows that reach thr, and, when its third key may reach
-// thr too, all its rows, scored again by rescore (the same bits as score_keys). The candidates go to gathered[] as ranking keys;
-// then the exact top-kp. best1/rest point at the query's tiles, bm at its first block
-// maximum (stride G); its candidate rows are 1..rl. tiles is LDS for kTileCap tile indices,
-// ovf for kOvfCap. When the candidates do not fit (ties at the bound), every passing tile is
-// scored into scratch (the query's rows) and selected from there. The other wavefronts run
-// overlap() while wavefront 0 takes the bound.
-//
-// rescore(ntl, tile_at, emit): scores every row of the tiles tile_at(0..ntl) (-1: none) for
-// this query, calling emit(key, row) for each of its candidate rows. All threads.
-constexpr int kTileCap = 1024;
-constexpr int kOvfCap = 64;
-
-template <int NT, typename Overlap, typename Rescore>
-__device__ __forceinline__ void select_tiles(const uint32_t *__restrict__ best1,
-                                             const uint2 *__restrict__ rest,
-                                             const uint32_t *__restrict__ bm, int G, int nblk,
-                                             int tile_shift, int rl, int kp, int32_t *js,
-                                             uint64_t *sel, uint64_t *gathered, int32_t *tiles,
-                                             int32_t *ovf, uint32_t *scratch,
-                                             SelectShared<NT> &sh, Overlap overlap,
-                                             Rescore rescore) {
-    static_assert(NT >= 256, "tile path: 256- or 1024-thread workgroups");
-    constexpr int E = 8;   // block maxima per lane: at most 512 (merged in groups beyond)
-    constexpr int TU = 8;  // tile maxima in flight per thread
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // 32-bit indices: a query's key rows are fewer than 2^31.
-    const int tile_rows = 1 << tile_shift;
-    const int ntiles = (rl + tile_rows) >> tile_shift;  // tiles covering rows 0..rl
-    // First tile maxima requested before the bound is known.
-    uint32_t tm[TU];
-#pragma unroll
-    for (int e = 0; e < TU; ++e) {
-        const int j = tid + NT * e;
-        tm[e] = best1[j < ntiles ? j : 0];
-    }
-    if (wave == 0) {
-        // Maxima of disjoint groups of rows: the blocks (256 rows), or the tiles when there are
-        // fewer than 2k' blocks; merged into at most 64*E groups of consecutive ones.
-        const bool by_tile = nblk < 2 * kp;
-        const uint32_t *src = by_tile ? best1 : bm;
-        const int stride = by_tile ? 1 : G;
-        const int count = by_tile ? ntiles : nblk;
-        const int per = (count + 64 * E - 1) / (64 * E);
-        const int ngr = per == 1 ? count : (int)(((uint32_t)count + per - 1) / (uint32_t)per);
-        uint32_t m[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) m[e] = 0u;
-        for (int jj = 0; jj < per; ++jj) {  // E independent loads per pass, all issued first
-            uint32_t x[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int gi = lane + 64 * e, grp = gi * per + jj;
-                x[e] = src[(gi < ngr && grp < count ? grp : 0) * stride];
-            }
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int gi = lane + 64 * e, grp = gi * per + jj;
-                if (gi < ngr && grp < count) m[e] = x[e] > m[e] ? x[e] : m[e];
-            }
-        }
-        const uint32_t thr = wave_bound_u32(m, kp);
-        if (lane == 0) { sh.pick[0] = thr > 1u ? thr : 1u; sh.pick[1] = 0u; sh.pick[2] = 0u; sh.sel_count = 0; }
-    } else {
-        overlap();
-    }
-    __syncthreads();
-    const uint32_t thr = sh.pick[0];
-    // Tiles whose best key reaches the bound, compacted into tiles[] (in any order: the
-    // selection does not depend on it). jb is uniform.
-    for (int jb = 0;; jb += NT * TU) {
-        const int j0 = jb + tid;
-#pragma unroll
-        for (int e = 0; e < TU; ++e) {
-            if (tm[e] >= thr && j0 + NT * e < ntiles) {
-                const uint32_t at = atomicAdd(&sh.pick[1], 1u);
-                if (at < (uint32_t)kTileCap) tiles[at] = j0 + NT * e;
-            }
-        }
-        if (jb + NT * TU >= ntiles) break;
-#pragma unroll
-        for (int e = 0; e < TU; ++e) {
-            const int j = j0 + NT * (TU + e);
-            tm[e] = best1[j < ntiles ? j : 0];
-        }
-    }
-    __syncthreads();
-    const int nt = (int)sh.pick[1];
-    bool fallback = nt > kTileCap;
-    if (!fallback) {
-        // Each passing tile gives its best rows that reach the bound, or, when its third key may
-        // reach it as well (its upper half is kept: compared as the largest key with that
-        // half), goes to the list of tiles scored again.
-        for (int x = tid; x < nt; x += NT) {
-            const int tile = tiles[x];
-            const uint32_t k1 = best1[tile];
-            const uint2 rs = rest[tile];
-            // Both loads complete here (kept from being moved into the branches one by one).
-            asm volatile("" ::"v"(k1), "v"(rs.x), "v"(rs.y));
-            const uint32_t k2 = rs.x, o = rs.y, k3max = (rs.y & 0xFFFF0000u) | 0xFFFFu;
-            if ((rs.y & 0xFFFF0000u) != 0u && k3max >= thr) {
-                const uint32_t at = atomicAdd(&sh.pick[2], 1u);
-                if (at < (uint32_t)kOvfCap) ovf[at] = tile;
-            } else {
-                // (Increments of 1 only: the compiler turns those into one atomic per wavefront.)
-                const uint32_t row0 = (uint32_t)(tile << tile_shift);
-                const int p1 = atomicAdd(&sh.sel_count, 1);
-                if (p1 < kGather) gathered[p1] = make_rank_key(k1, row0 + (o & 0xFFu));
-                if (k2 >= thr) {
-                    const int p2 = atomicAdd(&sh.sel_count, 1);
-                    if (p2 < kGather) gathered[p2] = make_rank_key(k2, row0 + ((o >> 8) & 0xFFu));
-                }
-            }
-        }
-        __syncthreads();
-        const int no = (int)sh.pick[2];
-        if (no > kOvfCap) {
-            fallback = true;
-        } else if (no > 0) {
-            rescore(no, [&](int i) { return ovf[i]; }, [&](uint32_t key, int row) {
-                if (key >= thr) {
-                    const int pos = atomicAdd(&sh.sel_count, 1);
-                    if (pos < kGather) gathered[pos] = make_rank_key(key, (uint32_t)row);
-                }
-            });
-            __syncthreads();
-        }
-    }
-    int n = fallback ? kGather + 1 : sh.sel_count;
-    if (n > kGather) {
-        // Too many candidates for LDS (exact ties at the bound): the keys of every passing tile
-        // into scratch, then the selection over them.
-        rescore(ntiles, [&](int i) { return best1[i] >= thr ? i : -1; },
-                [&](uint32_t key, int row) { scratch[row] = key; });
-        __threadfence_block();
-        n = kGather + 1;
-    }
-    __syncthreads();
-    if (n <= kRankSelectMax && n <= NT && n >= kp) {
-        select_by_rank<NT>(n, kp, gathered, js);
-        return;
-    }
-    // Keys from scratch for rows of passing tiles (others hold none that reach the bound).
-    auto key_at = [&](int64_t f64) -> uint64_t {
-        const int f = (int)f64;
-        if (f < 1 || f > rl || best1[f >> tile_shift] < thr) return 0ull;
-        const uint32_t kv = scratch[f];
-        return kv >= thr ? make_rank_key(kv, (uint32_t)f) : 0ull;
-    };
-    select_exact<NT>(n, (int64_t)ntiles << tile_shift, key_at, kp, js, sel, gathered, sh);
-}
-
-// Scores every row of the tiles tile_at(0..ntl) (-1: none) for the query vector in slot t of
-// unit (b, kvh, group gq) with row_key over the unit's G query vectors, as score_keys does (the
-// same bits), and calls emit(key, row) for each row in [1, rl] (key 0 never reaches a bound). RPG
-// rows per wavefront load, LPR lanes per row; one pass per NW*RPG rows. All threads.
-template <typename T, int D, int NT, typename TileAt, typename Emit>
-__device__ __forceinline__ void rescore_tiles(const T *__restrict__ q, const T *__restrict__ kb,
-                                              const FinishArgs &a, uint32_t b, uint32_t kvh, uint32_t gq,
-                                              int t, int rl, int ntl, TileAt tile_at, Emit emit) {
-    constexpr int RB = D * (int)sizeof(T);
-    constexpr int LPR = RB >= 256 ? 16 : 8, RPG = 64 / LPR, P = RB / (16 * LPR);
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int sl = lane % LPR;
-    const uint32_t g = (uint32_t)a.g, bk = b * (uint32_t)a.Hkv + kvh;
-    const int G = a.G;
-    auto body = [&](auto gc) {
-        constexpr int GC = decltype(gc)::value;
-        uint4 qr[GC][P];
-#pragma unroll
-        for (int tt = 0; tt < GC; ++tt) {
-            const uint32_t idx = gq * GC + tt;
-            if (idx < a.nvec) {
-                const uint32_t qh = idx / g, hh = idx - qh * g;
-                const uint4 *src = reinterpret_cast<const uint4 *>(q + (((size_t)bk * g + hh) * a.nq + qh) * D);
-#pragma unroll
-                for (int p = 0; p < P; ++p) qr[tt][p] = src[p * LPR + sl];
-            } else {
-#pragma unroll
-                for (int p = 0; p < P; ++p) qr[tt][p] = make_uint4(0, 0, 0, 0);
-            }
-        }
-        const bool mine = sl / (LPR / GC) == t && sl % (LPR / GC) == 0;
-        const int total = ntl << a.tile_shift;
-        for (int r0 = wave * RPG; r0 < total; r0 += NW * RPG) {
-            const int rr = r0 + lane / LPR;
-            const int tile = rr < total ? tile_at(rr >> a.tile_shift) : -1;
-            const int row = tile >= 0 ? (tile << a.tile_shift) + (rr & ((1 << a.tile_shift) - 1)) : 0;
-            const int lrow = row < a.n ? row : (int)a.n - 1;
-            const uint4 *src = reinterpret_cast<const uint4 *>(kb + (size_t)lrow * D);
-            uint4 kr[P];
-#pragma unroll
-            for (int p = 0; p < P; ++p) kr[p] = src[p * LPR + sl];
-            const uint32_t key = row_key<T, LPR, P, GC>(kr, qr, lane);
-            if (mine && tile >= 0 && row >= 1 && row <= rl) emit(key, row);
-        }
-    };
-    if (G == 4) body(std::integral_constant<int, 4>());
-    else if (G == 2) body(std::integral_constant<int, 2>());
-    else body(std::integral_constant<int, 1>());
-}
-
 // Rows per lane in flight in the attend phase (rows past the set's end are loaded as clamped
 // duplicates, so these match the common sizes: 15 wavefronts x 4 rows x 5 cover the anchor and
 // a window of up to 299 rows of 256 bytes in one round, 4 x 4 x 4 a top-64 part).
 constexpr int kWindowU = 5;
 constexpr int kTopU = 4;  // rows per lane in flight in the top-k part
 
-template <typename T, int D, int NT, bool ATTEND, bool TILES>
+template <typename T, int D, int NT, bool ATTEND>
 __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                     const T *__restrict__ v,
                                                     int32_t *__restrict__ out_idx,
@@ -356,8 +149,6 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     extern __shared__ int32_t fsm[];  // js[2*cap] positions, then sel[topk] keys
     __shared__ SelectShared<NT> ssh;
     __shared__ uint64_t gathered[kGatherFor<NT>];
-    __shared__ int32_t tile_idx[TILES ? kTileCap : 1];
-    __shared__ int32_t ovf_idx[TILES ? kOvfCap : 1];
     // Softmax partials: [0, NW) the anchor and window rows (wavefronts 1..NW-1 when wavefront 0
     // takes the bound), [NW, 2NW) the top-k rows.
     __shared__ SoftmaxPartials<D, ATTEND ? 2 * NW : 1> part;
@@ -366,8 +157,9 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Query vector qv = (b*Hq + h)*nq + r (32-bit math: the plan keeps qv below 2^24).
-    const int64_t qv = blockIdx.x;
+    // Query vector qv = (b*Hq + h)*nq + r (32-bit math: the plan keeps qv below 2^31).
+    const int64_t qv = block_qv();
+    if (qv >= a.nqv) return;
     const uint32_t nq32 = (uint32_t)a.nq, hq32 = (uint32_t)a.Hq, g32 = (uint32_t)a.g;
     const uint32_t bh = (uint32_t)qv / nq32;
     const int64_t r = (uint32_t)qv - bh * nq32;
@@ -387,12 +179,6 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     // js layout: [0 if the anchor is separate][top-k' ascending][window ascending]
     const int base = wlo > 0 ? 1 : 0;
     const int wcount = (int)(i - wlo + 1);
-    // Tile-summary path: unit and slot of this query vector (vector index r*g + (h - kvh*g) of
-    // its KV head).
-    const uint32_t idx = (uint32_t)r * g32 + (h - kvh * g32);
-    const uint32_t gq = TILES ? idx / (uint32_t)a.G : 0u;
-    const int64_t u = ((int64_t)b * a.Hkv + kvh) * a.groups + gq;
-    const int t = (int)(idx - gq * (uint32_t)(TILES ? a.G : 0));
 
     // Attend over the anchor and the window: the rows are known from the start, so they are
     // processed by the wavefronts that do not take the bound (all of them when there is no
@@ -425,19 +211,8 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     };
     if (kp > 0) {
         auto overlap = [&]() { window_part(wave - 1, NW - 1); };
-        if constexpr (TILES) {
-            const size_t qt = ((size_t)u * a.G + t) * (size_t)(a.rstride >> a.tile_shift);
-            select_tiles<NT>(a.best1 + qt, a.rest + qt,
-                             a.bmax + (size_t)u * a.nblk * a.G + t, a.G, a.nblk, a.tile_shift,
-                             (int)rl, kp, js + base, sel, gathered, tile_idx, ovf_idx,
-                             a.scratch + qv * a.rstride, ssh, overlap,
-                             [&](int ntl, auto tile_at, auto emit) {
-                                 rescore_tiles<T, D, NT>(q, kb, a, b, kvh, gq, t, (int)rl, ntl, tile_at, emit);
-                             });
-        } else {
-            select_segments<NT>(a.cnt + qv * a.wpu, a.lists + qv * a.wpu * a.seg, a.wpu, a.seg,
-                                kp, js + base, sel, gathered, ssh, overlap);
-        }
+        select_segments<NT>(a.cnt + qv * a.wpu, a.lists + qv * a.wpu * a.seg, a.wpu, a.seg,
+                            kp, js + base, sel, gathered, ssh, overlap);
     } else {
         window_part(wave, NW);
     }
@@ -459,55 +234,6 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
         // Window partials: NW-1 (from mfma_window), 1..NW-1 (wavefront 0 took the bound) or
         // 0..NW-1; top-k partials NW..2NW-1.
         const int p0 = pre_win ? NW - 1 : (kp > 0 ? 1 : 0);
-        if constexpr (TILES) {
-            if (a.mass && tid < 64) {
-                // Mass diagnostic (pages of "The Condensate Theorem", metaphor-xennon blog:
-                // section 3.2.2, the full-softmax mass outside C_i; sections 2.2.1-2.2.3, the
-                // parts of C_i). Sum over the candidate rows R_i from score_keys' per-block
-                // sums; the window part (with row 0) and the top-k part from the partials above;
-                // row 0's own weight from its score. All relative to one maximum M.
-                const float2 *zs = a.zsum + (size_t)u * a.nblk * a.G + t;
-                float ml = -INFINITY, ll = 0.f;  // this lane's blocks lane, lane + 64, ...
-                for (int blk = lane; blk < a.nblk; blk += 64) {
-                    const float2 z = zs[(size_t)blk * a.G];
-                    if (z.x != -INFINITY) {
-                        const float mn = fmaxf(ml, z.x);
-                        ll = (ml == -INFINITY ? 0.f : ll * exp2f((ml - mn) * a.scale_log2e)) +
-                             z.y * exp2f((z.x - mn) * a.scale_log2e);
-                        ml = mn;
-                    }
-                }
-                const float mr = wave_max_f32_dpp(ml);
-                const float lr = wave_sum_f32_dpp(ml == -INFINITY ? 0.f : ll * exp2f((ml - mr) * a.scale_log2e));
-                auto range = [&](int q0, int q1, float &mx, float &sm) {
-                    const int pc = lane < 2 * NW ? lane : 2 * NW - 1;
-                    const float pm = lane >= q0 && lane < q1 ? part.m[pc] : -INFINITY;
-                    const float pl = lane >= q0 && lane < q1 ? part.l[pc] : 0.f;
-                    mx = wave_max_f32_dpp(pm);
-                    sm = wave_sum_f32_dpp(pm == -INFINITY ? 0.f : pl * exp2f((pm - mx) * a.scale_log2e));
-                };
-                float mw, lw, mt = -INFINITY, lt = 0.f;
-                range(p0, NW, mw, lw);
-                if (kp > 0) range(NW, NW + top_waves, mt, lt);
-                using S = AttendShape<D, T>;
-                const uint4 k0 = reinterpret_cast<const uint4 *>(kb)[lane % S::LPR];
-                const float s0 = row_sum<S::LPR>(dot16(k0, qs, 0.f, T()));
-                const float mg = fmaxf(mr, mw);
-                auto rel = [&](float mx, float sm) {
-                    return mx == -INFINITY ? 0.f : sm * exp2f((mx - mg) * a.scale_log2e);
-                };
-                const float zr = rel(mr, lr), zw = rel(mw, lw), zt = rel(mt, lt);
-                const float z0 = exp2f((s0 - mg) * a.scale_log2e);
-                const float zf = zr + zw;
-                if (lane == 0) {
-                    float *mo = a.mass + qv * 4;
-                    mo[0] = fmaxf(zr - zt, 0.f) / zf;
-                    mo[1] = z0 / zf;
-                    mo[2] = fmaxf(zw - z0, 0.f) / zf;
-                    mo[3] = zt / zf;
-                }
-            }
-        }
         merge_partials<NT, D>(part, p0, kp > 0 ? NW + top_waves : NW, a.scale_log2e, out + qv * D);
     }
 }
@@ -524,7 +250,8 @@ __global__ __launch_bounds__(NT) void attend_kernel(const T *__restrict__ q, con
     __shared__ SoftmaxPartials<D, NW> part;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t qv = blockIdx.x;  // (b*Hq + h)*nq + r, below 2^24
+    const int64_t qv = block_qv();  // (b*Hq + h)*nq + r, below 2^31
+    if (qv >= a.nqv) return;
     const uint32_t nq32 = (uint32_t)a.nq, hq32 = (uint32_t)a.Hq;
     const uint32_t bh = (uint32_t)qv / nq32;
     const int64_t r = (uint32_t)qv - bh * nq32;
@@ -571,17 +298,9 @@ FinishArgs finish_args(const Plan &pl, const void *ws) {
     a.cnt = ws ? reinterpret_cast<const uint32_t *>(static_cast<const char *>(ws) + pl.slots_offset) + 2 * pl.nqv * pl.wpu
                : nullptr;
     a.lists = ws ? reinterpret_cast<const uint64_t *>(static_cast<const char *>(ws) + pl.lists_offset) : nullptr;
-    a.G = pl.G; a.nblk = pl.nblk; a.tile_shift = pl.tile_rows == 32 ? 5 : 4; a.groups = pl.groups; a.rstride = pl.rstride;
     const char *wb = static_cast<const char *>(ws);
-    const bool sm = ws && pl.stream;
-    a.best1 = sm ? reinterpret_cast<const uint32_t *>(wb + pl.best1_offset) : nullptr;
-    a.rest = sm ? reinterpret_cast<const uint2 *>(wb + pl.rest_offset) : nullptr;
-    a.bmax = sm ? reinterpret_cast<const uint32_t *>(wb + pl.bmax_offset) : nullptr;
-    a.scratch = sm ? reinterpret_cast<uint32_t *>(const_cast<char *>(wb) + pl.scratch_offset) : nullptr;
-    a.nvec = (uint32_t)(pl.g * pl.nq);
     a.win = ws && pl.mfma ? reinterpret_cast<const float *>(wb + pl.win_offset) : nullptr;
-    a.zsum = sm ? reinterpret_cast<const float2 *>(wb + pl.zsum_offset) : nullptr;
-    a.mass = nullptr;
+    a.nqv = pl.nqv;
     return a;
 }
 
@@ -592,29 +311,23 @@ constexpr int64_t kWideBelow = 4096;
 
 template <typename T, int D, bool ATTEND>
 hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const void *k,
-                           const void *v, int32_t *out_idx, float *out, hipStream_t s, float *mass) {
-    FinishArgs a = finish_args(pl, ws);
-    a.mass = mass;
+                           const void *v, int32_t *out_idx, float *out, hipStream_t s) {
+    const FinishArgs a = finish_args(pl, ws);
     const size_t shmem = (size_t)pl.cap * (2 * sizeof(int32_t)) + (size_t)pl.topk * sizeof(uint64_t);
-    const bool tiles = pl.stream && ws != nullptr;
-    const dim3 grid((unsigned)pl.nqv);
+    const dim3 grid = qv_grid(pl.nqv);
     const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v);
-    const size_t fixed1024 = kGather * sizeof(uint64_t) + sizeof(SelectShared<1024>) +
-                             (kTileCap + kOvfCap) * sizeof(int32_t) + sizeof(SoftmaxPartials<D, 32>);
+    const size_t fixed1024 = kGather * sizeof(uint64_t) + sizeof(SelectShared<1024>) + sizeof(SoftmaxPartials<D, 32>);
     const bool wide = pl.nqv < kWideBelow && shmem + fixed1024 <= 64 * 1024;
-#define CA_LAUNCH_FIN(NT, TILES)                                                                  \
-    hipLaunchKernelGGL((finish_kernel<T, D, NT, ATTEND, TILES>), grid, dim3(NT), shmem, s, qt, kt, vt, \
-                       out_idx, out, a)
+#define CA_LAUNCH_FIN(NT)                                                                          \
+    hipLaunchKernelGGL((finish_kernel<T, D, NT, ATTEND>), grid, dim3(NT), shmem, s, qt, kt, vt, out_idx, out, a)
     if (wide) {
-        if (tiles) CA_LAUNCH_FIN(1024, true); else CA_LAUNCH_FIN(1024, false);
-    } else if (tiles) {
-        CA_LAUNCH_FIN(256, true);
+        CA_LAUNCH_FIN(1024);
     } else if (pl.mfma && pl.wpu * pl.seg <= kRankSelectMax && pl.topk <= 32) {
-        CA_LAUNCH_FIN(64, false);
+        CA_LAUNCH_FIN(64);
     } else if (pl.mfma && pl.wpu * pl.seg <= kRankSelectMax) {
-        CA_LAUNCH_FIN(128, false);
+        CA_LAUNCH_FIN(128);
     } else {
-        CA_LAUNCH_FIN(256, false);
+        CA_LAUNCH_FIN(256);
     }
 #undef CA_LAUNCH_FIN
     return hipGetLastError();
@@ -625,7 +338,7 @@ hipError_t launch_attend_t(const Plan &pl, const void *q, const void *k, const v
                            const int32_t *idx, float *out, hipStream_t s) {
     const FinishArgs a = finish_args(pl, nullptr);
     const size_t shmem = (size_t)pl.cap * sizeof(int32_t);
-    const dim3 grid((unsigned)pl.nqv);
+    const dim3 grid = qv_grid(pl.nqv);
     const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v);
     const bool wide = pl.nqv < kWideBelow && shmem + sizeof(SoftmaxPartials<D, 16>) <= 64 * 1024;
     if (wide)
@@ -638,10 +351,10 @@ hipError_t launch_attend_t(const Plan &pl, const void *q, const void *k, const v
 }  // namespace
 
 hipError_t launch_finish(const Plan &pl, const void *ws, const void *q, const void *k,
-                         const void *v, int32_t *out_idx, float *out, hipStream_t s, float *mass) {
+                         const void *v, int32_t *out_idx, float *out, hipStream_t s) {
     const bool attend = out != nullptr;
-#define CA_FIN(T, D) (attend ? launch_finish_t<T, D, true>(pl, ws, q, k, v, out_idx, out, s, mass) \
-                             : launch_finish_t<T, D, false>(pl, ws, q, k, v, out_idx, out, s, nullptr))
+#define CA_FIN(T, D) (attend ? launch_finish_t<T, D, true>(pl, ws, q, k, v, out_idx, out, s) \
+                             : launch_finish_t<T, D, false>(pl, ws, q, k, v, out_idx, out, s))
     if (pl.dtype == 1) return pl.d == 128 ? CA_FIN(__bf16, 128) : CA_FIN(__bf16, 64);
     return pl.d == 128 ? CA_FIN(float, 128) : CA_FIN(float, 64);
 #undef CA_FIN

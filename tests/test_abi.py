@@ -70,6 +70,8 @@ BAD = [
     (dict(chunk=128), ca.CA_ERR_INVALID_ARG, "chunk"),
     (dict(chunk=2048), ca.CA_ERR_INVALID_ARG, "chunk"),
     (dict(topk=513, W=16), ca.CA_ERR_UNSUPPORTED, "topk"),
+    # One workgroup per query vector with 32-bit query-vector math: batch * heads * nq < 2^31.
+    (dict(batch=2, heads=32, kv_heads=8, n=2**25, nq=2**25, W=64, topk=32), ca.CA_ERR_UNSUPPORTED, "query vectors"),
 ]
 
 
@@ -120,6 +122,16 @@ def test_workspace_size_rules(lib):
     for c in (0, 256, 512, 1024):
         assert ws_size(good(chunk=c))[0] == ca.CA_OK
     assert ws_size(good(topk=512, W=16))[0] == ca.CA_OK
+
+
+def test_query_vector_limit(lib):
+    # A 1M-token, 32-head prefill at d = 64 takes the matrix-core passes with 2^25 query vectors,
+    # more than one grid dimension of 256-wide workgroups holds (2^24): planned, and launched as
+    # two-dimensional grids. Up to 2^31 - 1 query vectors are accepted; beyond, nothing runs.
+    assert ws_size(good(heads=32, kv_heads=32, d=64, n=2**25, nq=2**25, W=64, topk=32))[0] == ca.CA_OK
+    assert ws_size(good(batch=63, heads=32, kv_heads=32, d=64, n=2**20, nq=2**20, W=64, topk=32))[0] == ca.CA_OK
+    rc, _ = ws_size(good(batch=64, heads=32, kv_heads=32, d=64, n=2**20, nq=2**20, W=64, topk=32))
+    assert rc == ca.CA_ERR_UNSUPPORTED and "query vectors" in ca.last_error()
 
 
 def test_mass_entry_point_rules(lib):

@@ -103,6 +103,37 @@ def test_attention_on_subset_any_order_and_padding():
     assert torch.count_nonzero(out).item() == 0
 
 
+def test_attention_on_subset_more_than_65536_query_vectors():
+    """Stage 2 with 2 x 40,000 query vectors (a grid of two rows of workgroups): a set that
+    holds only the query's own position gives its own V row back exactly (float32, one weight
+    of 1), and a set of the query and the anchor the two-row softmax."""
+    n, heads, d = 40000, 2, 64
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(1, heads, n, d, generator=g)
+    k = torch.randn(1, 1, n, d, generator=g)
+    v = torch.randn(1, 1, n, d, generator=g)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    p = ca.params(1, heads, 1, d, n, n, 1, 0, "f32")
+    pos = torch.arange(n, dtype=torch.int32).view(1, 1, n, 1).expand(1, heads, n, 1)
+    idx = torch.cat([pos, torch.full_like(pos, -1)], dim=-1).contiguous()
+    announce("subset 80000 query vectors")
+    out = torch.empty((1, heads, n, d), dtype=torch.float32, device="cuda")
+    ca.attention_on_subset(p, qc, kc, vc, idx.cuda(), out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), v.expand(1, heads, n, d))
+    idx2 = torch.cat([pos, -(pos == 0).to(torch.int32)], dim=-1).contiguous()  # no repeats
+    ca.attention_on_subset(p, qc, kc, vc, idx2.cuda(), out)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 65535, 65536, 65537, 79999])  # flat query vectors, both heads
+    s_self = (q.view(-1, d)[rows].double() * k[0, 0, rows % n].double()).sum(-1) / d ** 0.5
+    s_zero = (q.view(-1, d)[rows].double() * k[0, 0, 0].double()).sum(-1) / d ** 0.5
+    w0 = torch.sigmoid(s_zero - s_self)  # weight of position 0 (row 0 of each head: itself)
+    ref = (1 - w0)[:, None] * v[0, 0, rows % n].double() + w0[:, None] * v[0, 0, 0].double()
+    ref[rows % n == 0] = v[0, 0, 0].double()
+    got = out.view(-1, d)[torch.from_numpy(rows).cuda()].cpu().double()
+    assert torch.allclose(got, ref, rtol=1e-5, atol=1e-5)
+
+
 @pytest.mark.parametrize("chunk", [256, 512, 1024])
 def test_chunk_size_does_not_change_results(chunk):
     w = W_(heads=8, kv_heads=2, n=9000, nq=2, W=64, topk=48)
