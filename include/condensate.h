@@ -107,6 +107,18 @@ int ca_condensate_attention_ex(const ca_params *p, const void *q, const void *k,
                                float *out, int32_t *out_idx, void *ws, size_t ws_bytes,
                                void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): ca_condensate_attention_ex without a workspace argument. The workspace
+ * is a device array of the library (CA_NOSCRATCH_MAX_BYTES, one copy per GPU, held until the
+ * process ends); the call allocates nothing and records no profiling events. Problems whose
+ * ca_workspace_size() exceeds CA_NOSCRATCH_MAX_BYTES return CA_ERR_UNSUPPORTED before any HIP
+ * call (the 131,072-row, 32-query-vector decode step needs 16.5 MiB). Every call on one GPU
+ * shares that array and leaves its contents to the next: calls that overlap on one GPU (other
+ * streams, other threads) race and must not be issued. Asynchronous on `stream`. */
+#define CA_NOSCRATCH_MAX_BYTES (32 * 1024 * 1024)
+int ca_condensate_attention_noscratch(const ca_params *p, const void *q, const void *k, const void *v,
+                                      float *out, int32_t *out_idx, void *stream);
+
 /* The full method plus the mass diagnostic of the pages (metaphor-xennon blog: section 3.2.2,
  * the weight the full causal softmax puts outside C_i; sections 2.2.1-2.2.3, the parts of C_i):
  * as ca_condensate_attention_ex, and mass[batch][heads][nq][4] float32 (device pointer, owned

@@ -30,7 +30,7 @@ CA_MAX_SET = 4096
 
 EXPORTED = ("ca_condensate_attention", "ca_workspace_size", "ca_condensate_attention_ex",
             "ca_condensate_attention_mass_ex", "ca_dense_attention_ex", "ca_condensate_select",
-            "ca_attention_on_subset",
+            "ca_attention_on_subset", "ca_condensate_attention_noscratch",
             "ca_profile_start", "ca_profile_stop", "ca_status_string", "ca_last_error")
 
 
@@ -76,6 +76,7 @@ def load() -> ctypes.CDLL:
         L.ca_dense_attention_ex.argtypes = [P, vp, vp, vp, vp, vp]
         L.ca_condensate_select.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.ca_attention_on_subset.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.ca_condensate_attention_noscratch.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.ca_profile_start.argtypes = [ctypes.c_int32]
         L.ca_profile_stop.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int32)]
@@ -85,7 +86,8 @@ def load() -> ctypes.CDLL:
         L.ca_last_error.restype = ctypes.c_char_p
         for f in (L.ca_condensate_attention, L.ca_workspace_size, L.ca_condensate_attention_ex,
                   L.ca_condensate_attention_mass_ex, L.ca_dense_attention_ex, L.ca_condensate_select,
-                  L.ca_attention_on_subset, L.ca_profile_start, L.ca_profile_stop):
+                  L.ca_attention_on_subset, L.ca_condensate_attention_noscratch, L.ca_profile_start,
+                  L.ca_profile_stop):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -159,6 +161,16 @@ def condensate_attention_ex(p: Params, q, k, v, out, out_idx, ws, stream=None):
         ctypes.byref(p), _dev_ptr(q, "q", dt), _dev_ptr(k, "k", dt), _dev_ptr(v, "v", dt),
         _dev_ptr(out, "out", torch.float32), _dev_ptr(out_idx, "out_idx", torch.int32),
         _dev_ptr(ws, "ws"), ws_bytes, _stream_ptr(stream)), "ca_condensate_attention_ex")
+
+
+def condensate_attention_noscratch(p: Params, q, k, v, out, out_idx, stream=None):
+    """ca_condensate_attention_noscratch: as condensate_attention_ex with the library's own
+    device array as workspace (nothing allocated; calls on one GPU must not overlap)."""
+    dt = q.dtype
+    _check(load().ca_condensate_attention_noscratch(
+        ctypes.byref(p), _dev_ptr(q, "q", dt), _dev_ptr(k, "k", dt), _dev_ptr(v, "v", dt),
+        _dev_ptr(out, "out", torch.float32), _dev_ptr(out_idx, "out_idx", torch.int32),
+        _stream_ptr(stream)), "ca_condensate_attention_noscratch")
 
 
 def condensate_attention_mass_ex(p: Params, q, k, v, out, out_idx, mass, ws, stream=None):

@@ -39,11 +39,16 @@ struct Profiler {
 Profiler g_prof;
 
 // Brackets one launch with events when profiling is on.
+// Set while ca_condensate_attention_noscratch runs on this thread: its launches are not
+// bracketed (creating events on demand could allocate).
+thread_local bool t_no_prof = false;
+
 struct ProfScope {
     int kernel;
     hipStream_t s;
     hipEvent_t start = nullptr;
     ProfScope(int k, hipStream_t st) : kernel(k), s(st) {
+        if (t_no_prof) return;
         std::lock_guard<std::mutex> lk(g_prof.mu);
         if (!g_prof.on) return;
         start = g_prof.take();
@@ -339,6 +344,56 @@ int ca_condensate_attention_ex(const ca_params *p, const void *q, const void *k,
         return fail(CA_ERR_INVALID_ARG, "q, k, v, out and out_idx must be non-NULL");
     if ((rc = check_ws(pl, ws, ws_bytes)) != CA_OK) return rc;
     return run_path(pl, q, k, v, out_idx, out, ws, static_cast<hipStream_t>(stream));
+}
+
+// ---- the entry point that allocates nothing: the workspace is a device array of this file ----
+namespace {
+
+// One copy per GPU, held until the process ends; every call on that GPU shares it.
+static __device__ __align__(256) unsigned char scratch[CA_NOSCRATCH_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch` per device (null: not yet)
+
+// Device address of this device's copy of `scratch`, looked up on the first call on a device
+// with that device current. In host code the array's name is a host-side stand-in, never a
+// device address: only the looked-up pointer is passed to kernels.
+int scratch_for_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(CA_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(CA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return CA_OK;
+}
+
+}  // namespace
+
+int ca_condensate_attention_noscratch(const ca_params *p, const void *q, const void *k, const void *v,
+                                      float *out, int32_t *out_idx, void *stream) {
+    ca::Plan pl;
+    int rc = make_plan(p, &pl);
+    if (rc != CA_OK) return rc;
+    if (!q || !k || !v || !out || !out_idx)
+        return fail(CA_ERR_INVALID_ARG, "q, k, v, out and out_idx must be non-NULL");
+    if (pl.ws_bytes > (size_t)CA_NOSCRATCH_MAX_BYTES)
+        return fail(CA_ERR_UNSUPPORTED, "the problem needs %zu bytes of workspace, more than the %d of the "
+                                        "library's device array", pl.ws_bytes, CA_NOSCRATCH_MAX_BYTES);
+    void *ws = nullptr;
+    if (pl.ws_bytes > 0 && (rc = scratch_for_current_device(&ws)) != CA_OK) return rc;
+    t_no_prof = true;
+    rc = run_path(pl, q, k, v, out_idx, out, ws, static_cast<hipStream_t>(stream));
+    t_no_prof = false;
+    return rc;
 }
 
 int ca_condensate_attention_mass_ex(const ca_params *p, const void *q, const void *k,

@@ -134,6 +134,23 @@ def test_query_vector_limit(lib):
     assert rc == ca.CA_ERR_UNSUPPORTED and "query vectors" in ca.last_error()
 
 
+def test_noscratch_entry_point_rules(lib):
+    vp = ctypes.c_void_p(16)
+    # Validation first, as every entry point.
+    p = good(batch=0)
+    assert lib.ca_condensate_attention_noscratch(ctypes.byref(p), vp, vp, vp, vp, vp, None) == ca.CA_ERR_INVALID_ARG
+    p = good()
+    assert lib.ca_condensate_attention_noscratch(ctypes.byref(p), None, vp, vp, vp, vp, None) == ca.CA_ERR_INVALID_ARG
+    # A problem whose workspace exceeds the library's device array: refused before any HIP call.
+    big = good(n=1 << 20, batch=4, topk=128)
+    rc, need = ws_size(big)
+    assert rc == ca.CA_OK and need > 32 * 1024 * 1024
+    assert lib.ca_condensate_attention_noscratch(ctypes.byref(big), vp, vp, vp, vp, vp, None) == ca.CA_ERR_UNSUPPORTED
+    assert "device array" in ca.last_error()
+    # The 131K GQA decode step fits.
+    assert ws_size(good())[1] <= 32 * 1024 * 1024
+
+
 def test_mass_entry_point_rules(lib):
     """The mass diagnostic runs on the streaming decode path only; other plans, missing
     pointers and short workspaces are rejected on the host."""
