@@ -34,8 +34,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of the chip
 # FETCH_SIZE / WRITE_SIZE counters, valid while the kernel's sources hash to the recorded value.
 COUNTERS = os.path.join(ROOT, "profiles", "decode_stream_decode_131k_gqa_bf16_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_transformer_attention_amd", "csrc", f)
-                  for f in ("decode_stream.hip", "decode_core.h", "score_core.h", "device_utils.h",
-                            "ca_internal.h")]
+                  for f in ("decode_stream.hip", "decode_core.h", "score_core.h", "device_utils.h")]
 
 
 def kernel_sources_sha() -> str:

@@ -308,14 +308,12 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
                 kk[e] = make_rank_key(ks[e], (uint32_t)blk * kRows + ((offs >> (8 * e)) & 255u));
                 ok[e] = has && ks[e] != 0u && kk[e] >= thr;
             }
-            // X reaches the threshold's score key: rows beyond the record may rank.
-            const bool okd = has && X != 0u && X >= (uint32_t)(thr >> 32);
-            append_all<D, 4>(sh, ok, kk, okd, ((uint64_t)X << 32) | (uint32_t)blk, offs);
+            append_all<D, 4>(sh, ok, kk, false, 0ull, 0u);
             if (tid == 0) sh.thr = thr;
         }
         __syncthreads();
         if (wave == 0) {
-            if (sh.n > kCand || sh.ndef > kDef) {
+            if (sh.n > kCand) {
                 if (lane == 0) sh.flag = 1;
             } else if (!sh.flag) {
                 cut_exact<D>(sh, kp);
@@ -324,6 +322,22 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
             }
         }
         __syncthreads();
+        if (sh.flag) break;
+        {
+            // Blocks whose X reaches the round's final threshold's score key: rows beyond the
+            // record may rank.
+            const uint32_t X = rb.y;
+            const bool no[1] = {false};
+            const uint64_t nk[1] = {0ull};
+            const bool okd = has && X != 0u && X >= (uint32_t)(sh.thr >> 32);
+            append_all<D, 1>(sh, no, nk, okd, ((uint64_t)X << 32) | (uint32_t)blk, rb.x);
+        }
+        __syncthreads();
+        if (sh.ndef > kDef) {
+            __syncthreads();
+            if (tid == 0) sh.flag = 1;
+            __syncthreads();
+        }
         if (sh.flag) break;
     }
     // Blocks whose rows beyond their record may still rank: scored again, all wavefronts on one

@@ -103,9 +103,4 @@ __device__ __forceinline__ uint32_t row_key(const uint4 (&kr)[P], const uint4 (&
     return score_key(reduce_row<LPR, G>(acc, lane));
 }
 
-// Adds the NS (key, row) results a lane holds to its query's running list. First chunk of a
-// unit (direct): the lists are empty and there is no threshold yet, so the key of row r goes to
-// position r - row0 (0 when r is no candidate of the query). Otherwise the keys that reach the
-// query's threshold are appended: one LDS atomic per query and call, positions from the
-// ballots.
 }  // namespace ca

@@ -122,6 +122,14 @@ WORKLOADS = {
     "decode_131k_gqa_w1024_bf16": Workload(
         "decode_131k_gqa_w1024_bf16", batch=1, heads=32, kv_heads=8, d=128, n=131072, nq=1,
         dtype="bf16", W=1024, topk=64, q_scale=2.0, needles_per_kv_head=64),
+    # The 4K x 32K prefill chunk with the shallow layers' window (W = 1024) and the deep
+    # layers' (W = 64).
+    "prefill_chunk_4k_32k_w1024_bf16": Workload(
+        "prefill_chunk_4k_32k_w1024_bf16", batch=1, heads=32, kv_heads=32, d=128, n=32768, nq=4096,
+        dtype="bf16", W=1024, topk=64, q_scale=1.0, needles_per_kv_head=256, mode="prefill"),
+    "prefill_chunk_4k_32k_w64_bf16": Workload(
+        "prefill_chunk_4k_32k_w64_bf16", batch=1, heads=32, kv_heads=32, d=128, n=32768, nq=4096,
+        dtype="bf16", W=64, topk=64, q_scale=1.0, needles_per_kv_head=256, mode="prefill"),
 }
 
 WORKLOAD_ORDER = list(WORKLOADS)

@@ -46,6 +46,12 @@ SHAPES = {
     "many_vectors_wave128": W_(heads=8, kv_heads=8, n=1024, nq=520, W=64, topk=64),
     # 8 query heads per KV head, batch 2: the vectors of a KV head interleave heads and rows.
     "gqa8_b2_d128": W_(batch=2, heads=16, kv_heads=2, n=1800, nq=90, W=40, topk=24),
+    # The windows of the pages' per-layer schedule (sections 6.1-6.2): W = 1024 (1,025-row
+    # anchor-and-window sets in mfma_window and finish), 256 and 64.
+    "window_1024_mha": W_(heads=2, kv_heads=2, n=3000, nq=800, W=1024, topk=64),
+    "window_1024_gqa4_d64": W_(d=64, heads=8, kv_heads=2, n=2600, nq=300, W=1024, topk=32),
+    "window_256_gqa2": W_(heads=4, kv_heads=2, n=2000, nq=500, W=256, topk=64),
+    "window_64_gqa4_d64": W_(d=64, heads=8, kv_heads=2, n=2400, nq=400, W=64, topk=32),
 }
 
 

@@ -376,6 +376,46 @@ def test_full_size_prefill_131k_stratified_9k_rows():
     assert_outputs(g_out, ref, w.torch_dtype)
 
 
+@pytest.mark.parametrize("name", ["prefill_chunk_4k_32k_w1024_bf16", "prefill_chunk_4k_32k_w64_bf16"])
+def test_full_size_prefill_chunk_4k_32k_other_windows_2k_rows(name):
+    """The 4K x 32K prefill chunk on the MFMA path with W = 1024 and W = 64, in the launch
+    configuration of the benchmark: per head the first and last 16 rows and 32 uniform draws
+    (2,048 rows over the 32 heads)."""
+    w = synth.WORKLOADS[name]
+    g = np.random.default_rng(5)
+    rows = sorted({(0, h, int(r)) for h in range(w.heads)
+                   for r in list(range(16)) + list(range(w.nq - 16, w.nq)) + list(g.integers(16, w.nq - 16, 32))})
+    announce(f"full-size {name} ({len(rows)} rows)")
+    ca.profile_start(8)
+    x, out, idx = run_full_size(w)
+    prof = ca.profile_stop()
+    assert "mfma_cand" in prof and "mfma_window" in prof, sorted(prof)
+    out_np, idx_np = out.cpu().numpy(), idx.cpu().numpy()
+    xh = to_host(x)
+    del x, out, idx
+    check_rows(w, xh, out_np, idx_np, rows)
+
+
+@pytest.mark.parametrize("W,topk", [(3000, 256), (3000, 512)])
+def test_decode_near_the_limits(W, topk):
+    """Decode with a 3,000-row window: topk = 256, the largest of the two-kernel decode path
+    (1 + W + k = 3,257 entries per set), and topk = 512, the largest of the library (the chunked
+    path; 3,513 entries)."""
+    w = W_(heads=8, kv_heads=2, n=24000, nq=2, W=W, topk=topk, needles_per_kv_head=32)
+    x = synth.make_inputs(w, seed=31)
+    q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
+    announce(f"decode near the limits W={W} topk={topk}")
+    ca.profile_start(8)
+    out, idx = ca.condensate(q, k, v, w.W, w.topk)
+    torch.cuda.synchronize()
+    prof = ca.profile_stop()
+    assert ("decode_finish" in prof) == (topk <= 256), sorted(prof)
+    ref_idx, _, ref_diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    idx_np = idx.cpu().numpy()
+    compare_sets(idx_np, ref_idx, ref_diag, x["q"], x["k"], w.W, w.topk)
+    assert_outputs(out.cpu().numpy(), oracle.restricted(x["q"], x["k"], x["v"], idx_np), w.torch_dtype)
+
+
 @pytest.mark.parametrize("name", ["decode_131k_gqa_w64_bf16", "decode_131k_gqa_w1024_bf16"])
 def test_full_size_decode_131k_other_windows(name):
     """The 131K GQA decode with W = 64 and W = 1024; every query vector checked."""
@@ -387,8 +427,8 @@ def test_full_size_decode_131k_other_windows(name):
 
 def test_workspace_reused_across_calls_shapes_and_paths():
     """One workspace, filled with random bytes before its first use, serves a sequence of calls
-    on changing inputs: two decode shapes (the one-kernel decode path, whose records carry a
-    per-call tag) and a bf16 prefill (the matrix-core path) in between. Every call's sets and
+    on changing inputs: two decode shapes (the two-kernel decode path, whose records the second
+    kernel reads) and a bf16 prefill (the matrix-core path) in between. Every call's sets and
     outputs must match the oracle's."""
     shapes = {
         "A": W_(heads=8, kv_heads=2, n=5000, nq=1, W=64, topk=32),
