@@ -68,7 +68,7 @@ struct FinShared {
     } x;
     uint64_t def[kDef];   // blocks whose X reached the threshold: X << 32 | block
     uint32_t doff[kDef];  // and their records' row offsets
-    SoftmaxPartials<D, 2 * kWaves> part;  // [0, kWaves) anchor and window, then the top-k rows
+    SoftmaxPartials<D, 2 * kWaves> part;  // [0, kWaves-1) anchor and window, then the top-k rows
     int wc[kWaves], wd[kWaves];           // per-wavefront counts of an append
     uint32_t tw[kWaves];                  // per-wavefront bounds
     uint32_t tb;                          // the single wavefront's bound
@@ -209,12 +209,15 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
     static_assert(kDef <= 64 && kCand <= 64 * 16, "one wavefront holds the lists");
     using AS = AttendShape<D, T>;
     using S = StreamShape<T, D>;
-    constexpr int UW = 9;  // window rows per lane requested before the selection (9 * 32 >= 257)
+    constexpr int UW = 10;  // window rows per lane requested before the selection (10 * 28 >= 257)
     __shared__ FinShared<D> sh;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t uu = blockIdx.x / G;
-    const int t = (int)(blockIdx.x - uu * G);
+    // Workgroup b serves query t = b / units of unit b % units: with the stream's interleaved
+    // order (workgroups are dealt to the 8 XCDs in turn) it runs on the XCD whose L2 took the
+    // unit's records when units is a multiple of 8.
+    const int t = (int)(blockIdx.x / a.units);
+    const uint32_t uu = blockIdx.x - (uint32_t)t * a.units;
     const uint32_t ng = (uint32_t)a.groups;
     const uint32_t bk = uu / ng, grp = uu - bk * ng;
     const QInfo qi = query_info<G>(a, bk, grp, t);
@@ -233,9 +236,29 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
     const uint4 qs = reinterpret_cast<const uint4 *>(q + (size_t)qi.qv * D)[lane % AS::LPR];
     const int wn = qi.base + qi.wcount;  // anchor and window rows
     auto row_at = [&](int c) -> size_t { return c < qi.base ? 0 : (size_t)(qi.wlo - qi.base + c); };
-    const int wstep = kWaves * AS::RPW;
+    // Anchor and window on wavefronts 1..kWaves-1 (partials 0..kWaves-2), computed while
+    // wavefront 0 makes the first round's cut.
+    constexpr int NWW = kWaves - 1;
+    const int wstep = NWW * AS::RPW;
+    const int wv = wave - 1;
     RowSlices<D, T, UW> rs;
-    if constexpr (ATTEND) load_rows<D, T, UW>(rs, kb, vb, row_at, wn, wave * AS::RPW, wstep);
+    if (ATTEND && wave > 0) load_rows<D, T, UW>(rs, kb, vb, row_at, wn, wv * AS::RPW, wstep);
+    bool win_done = !ATTEND;
+    auto window_partial = [&]() {
+        if constexpr (ATTEND) {
+            if (wave > 0) {
+                SlotState<D, T> st;
+                auto use = [&](int c) { return c < wn; };
+                accumulate_rows<D, T, UW>(st, rs, qs, use, wv * AS::RPW, wstep, a.scale_log2e);
+                for (int c0 = wv * AS::RPW + UW * wstep; c0 < wn; c0 += UW * wstep) {
+                    load_rows<D, T, UW>(rs, kb, vb, row_at, wn, c0, wstep);
+                    accumulate_rows<D, T, UW>(st, rs, qs, use, c0, wstep, a.scale_log2e);
+                }
+                store_wave_partial<D, T>(st, a.scale_log2e, sh.part, wv);
+            }
+        }
+        win_done = true;
+    };
     if (tid == 0) {
         sh.n = 0;
         sh.ndef = 0;
@@ -320,7 +343,10 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
                 wave_sync();
                 filter_deferred<D>(sh);
             }
+        } else if (!win_done) {
+            window_partial();
         }
+        win_done = true;
         __syncthreads();
         if (sh.flag) break;
         {
@@ -458,11 +484,20 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
     if (ATTEND && kp > 0) request(wave * AS::RPW);
     if (kp <= 64) {
         if (wave == kWaves - 1) {
-            // One candidate per lane; every position broadcast in turn.
-            const uint32_t pos = lane < kp ? (uint32_t)rank_key_pos(sh.cand[lane]) : 0xFFFFFFFFu;
-            int rank = 0;
-            for (int j = 0; j < kp; ++j) rank += __builtin_amdgcn_readlane(pos, j) < pos;
-            if (lane < kp) row[qi.base + rank] = (int32_t)pos;
+            // One candidate per lane (0xFFFFFFFF past k'): a bitonic sort across the wavefront
+            // leaves the c-th smallest position in lane c.
+            uint32_t pos = lane < kp ? (uint32_t)rank_key_pos(sh.cand[lane]) : 0xFFFFFFFFu;
+#pragma unroll
+            for (int kk = 2; kk <= 64; kk <<= 1) {
+#pragma unroll
+                for (int j = kk >> 1; j > 0; j >>= 1) {
+                    const uint32_t other = (uint32_t)__shfl_xor((int)pos, j);
+                    const bool up = (lane & kk) == 0, low = (lane & j) == 0;
+                    const uint32_t lo = other < pos ? other : pos, hi = other < pos ? pos : other;
+                    pos = (low == up) ? lo : hi;
+                }
+            }
+            if (lane < kp) row[qi.base + lane] = (int32_t)pos;
         }
     } else {
         const int kp8 = (kp + 7) & ~7;
@@ -486,17 +521,7 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
         }
     }
     if constexpr (ATTEND) {
-        // Anchor and window: the requested rows, then any beyond them (long windows).
-        {
-            SlotState<D, T> st;
-            auto use = [&](int c) { return c < wn; };
-            accumulate_rows<D, T, UW>(st, rs, qs, use, wave * AS::RPW, wstep, a.scale_log2e);
-            for (int c0 = wave * AS::RPW + UW * wstep; c0 < wn; c0 += UW * wstep) {
-                load_rows<D, T, UW>(rs, kb, vb, row_at, wn, c0, wstep);
-                accumulate_rows<D, T, UW>(st, rs, qs, use, c0, wstep, a.scale_log2e);
-            }
-            store_wave_partial<D, T>(st, a.scale_log2e, sh.part, wave);
-        }
+        if (!win_done) window_partial();
         // Top-k rows: weights exp2((s - m) * scale), m the largest selected score.
         float acc[AS::EPL];
 #pragma unroll
@@ -532,7 +557,7 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
         l = lane_pair_sum<32>(l);
 #pragma unroll
         for (int e = 0; e < AS::EPL; ++e) acc[e] = lane_pair_sum<32>(acc[e]);
-        const int slot_out = kWaves + wave;
+        const int slot_out = NWW + wave;
         if (lane < AS::LPR) {
 #pragma unroll
             for (int e = 0; e < AS::EPL; ++e) sh.part.acc[slot_out][cs * AS::EPL + e] = acc[e];
@@ -551,25 +576,25 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
         }
         lds_barrier();
         float *o = a.out + (size_t)qi.qv * D;
-        merge_partials<kNT, D, 2 * kWaves>(sh.part, 0, 2 * kWaves, a.scale_log2e, o);
+        merge_partials<kNT, D, 2 * kWaves>(sh.part, 0, NWW + kWaves, a.scale_log2e, o);
         if constexpr (MASS) {
             // Mass diagnostic (section 3.2.2, the full-softmax mass outside C_i; sections
             // 2.2.1-2.2.3, the parts of C_i): the candidates' part from the blocks' sums, the
             // window part (with row 0) and the top-k part from the partials, row 0 from its score;
             // all relative to one maximum.
             if (wave == 0) {
-                auto fold = [&](int p0, float *mo, float *lo) {
+                auto fold = [&](int p0, int np, float *mo, float *lo) {
                     float mx = -INFINITY;
-                    for (int p = p0; p < p0 + kWaves; ++p) mx = fmaxf(mx, sh.part.m[p]);
+                    for (int p = p0; p < p0 + np; ++p) mx = fmaxf(mx, sh.part.m[p]);
                     float sm = 0.f;
-                    for (int p = p0; p < p0 + kWaves; ++p)
+                    for (int p = p0; p < p0 + np; ++p)
                         sm += sh.part.m[p] == -INFINITY ? 0.f : sh.part.l[p] * exp2f((sh.part.m[p] - mx) * a.scale_log2e);
                     *mo = mx;
                     *lo = sm;
                 };
                 float mw, lw, mt, lt;
-                fold(0, &mw, &lw);
-                fold(kWaves, &mt, &lt);
+                fold(0, NWW, &mw, &lw);
+                fold(NWW, kWaves, &mt, &lt);
                 float mr = -INFINITY;
                 for (int p = 0; p < kWaves; ++p) mr = fmaxf(mr, sh.zm[p]);
                 float lr = 0.f;
