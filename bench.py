@@ -80,7 +80,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mass", action="store_true",
-                    help="time the call with the mass diagnostic (decode path only)")
+                    help="time the call with the mass diagnostic (decode and MFMA prefill paths)")
     ap.add_argument("--dense", action="store_true",
                     help="time dense causal attention (bf16) on the workload instead of the method")
     ap.add_argument("--calibrate-copy", action="store_true",

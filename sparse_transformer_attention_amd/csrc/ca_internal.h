@@ -46,6 +46,7 @@ struct Plan {
     // wpu = 4 segments of seg = kMfmaSeg keys per query.
     bool mfma;
     size_t win_offset;    // MFMA path: anchor-and-window partials [nqv][d + 2] floats
+    size_t zmass_offset;  // MFMA path, mass diagnostic: [nqv] (largest score, sum) over R_i
     int64_t rstride;
     int nblk;
     size_t summ_offset, scratch_offset;
@@ -57,8 +58,10 @@ hipError_t launch_score_select(const Plan &pl, const void *q, const void *k, voi
                                hipStream_t s);
 // Merge + set assembly (+ restricted softmax times V when out != nullptr), one workgroup per
 // query vector (chunked and MFMA paths).
+// mass != nullptr (MFMA path): also [nqv][4] = excluded mass, anchor, window, top-k.
 hipError_t launch_finish(const Plan &pl, const void *ws, const void *q, const void *k,
-                         const void *v, int32_t *out_idx, float *out, hipStream_t s);
+                         const void *v, int32_t *out_idx, float *out, hipStream_t s,
+                         float *mass = nullptr);
 // Restricted softmax times V on caller-supplied index sets.
 hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k, const void *v,
                                     const int32_t *idx, float *out, hipStream_t s);
@@ -83,9 +86,10 @@ constexpr int kMfmaQBCand = 4;
 constexpr int kMfmaWaves = 4;
 // The candidate pass keeps four lists of kMfmaSeg keys per query (one per lane that holds it).
 constexpr int kMfmaSeg = 64;
-// pass 0: the bound of every query; pass 1: its candidate list.
+// pass 0: the bound of every query (mass: also its softmax sum over R_i); pass 1: its candidate
+// list.
 hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
-                              int pass);
+                              int pass, bool mass = false);
 // Dense causal attention (bf16, matrix cores): the baseline the method is measured against.
 hipError_t launch_dense_attention(const Plan &pl, const void *q, const void *k, const void *v,
                                   float *out, hipStream_t s);

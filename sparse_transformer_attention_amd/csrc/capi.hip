@@ -161,6 +161,7 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     P.mfma = false;
     P.seg = 1;
     P.win_offset = 0;
+    P.zmass_offset = 0;
     // Many bf16 query vectors per KV head: the MFMA passes (bound, then candidate lists in the
     // segment layout of the chunked path: 4 segments of kMfmaSeg keys per query). They address
     // a KV head's key rows with 32-bit byte offsets.
@@ -176,7 +177,8 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         P.slots_offset = 0;
         P.lists_offset = P.slots_offset + slot_bytes;
         P.win_offset = (P.lists_offset + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) + 255) & ~(size_t)255;
-        P.ws_bytes = P.win_offset + (size_t)P.nqv * (size_t)(P.d + 2) * sizeof(float);
+        P.zmass_offset = (P.win_offset + (size_t)P.nqv * (size_t)(P.d + 2) * sizeof(float) + 255) & ~(size_t)255;
+        P.ws_bytes = P.zmass_offset + (size_t)P.nqv * 2 * sizeof(float);
         return CA_OK;
     }
     if (P.candidates && p->chunk == 0) {
@@ -240,7 +242,7 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
     hipError_t e;
     if (pl.candidates && pl.mfma) {
         ProfScope pb(K_BOUND, s);
-        e = ca::launch_mfma_select(pl, q, k, ws, s, 0);
+        e = ca::launch_mfma_select(pl, q, k, ws, s, 0, mass != nullptr);
         pb.done();
         if (e != hipSuccess) return hip_fail(e, "mfma_select (bound) launch");
         ProfScope pc(K_CAND, s);
@@ -274,7 +276,7 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
         if (e != hipSuccess) return hip_fail(e, "score_topk launch");
     }
     ProfScope pf(K_FINISH, s);
-    e = ca::launch_finish(pl, pl.candidates ? ws : nullptr, q, k, v, out_idx, out, s);
+    e = ca::launch_finish(pl, pl.candidates ? ws : nullptr, q, k, v, out_idx, out, s, mass);
     pf.done();
     if (e != hipSuccess) return hip_fail(e, "finish launch");
     return CA_OK;
@@ -402,9 +404,9 @@ int ca_condensate_attention_mass_ex(const ca_params *p, const void *q, const voi
     ca::Plan pl;
     int rc = make_plan(p, &pl);
     if (rc != CA_OK) return rc;
-    if (!(pl.candidates && pl.stream))
-        return fail(CA_ERR_UNSUPPORTED, "the mass diagnostic needs the streaming decode path "
-                                        "(chunk 0, some query with candidates, key buffer within budget)");
+    if (!(pl.candidates && (pl.stream || pl.mfma)))
+        return fail(CA_ERR_UNSUPPORTED, "the mass diagnostic needs the decode path or the matrix-core prefill "
+                                        "path (chunk 0, some query with candidates)");
     if (!q || !k || !v || !out || !out_idx || !mass)
         return fail(CA_ERR_INVALID_ARG, "q, k, v, out, out_idx and mass must be non-NULL");
     if ((rc = check_ws(pl, ws, ws_bytes)) != CA_OK) return rc;

@@ -234,6 +234,12 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
         rb = R[2 * tid + 1];
     }
     const uint4 qs = reinterpret_cast<const uint4 *>(q + (size_t)qi.qv * D)[lane % AS::LPR];
+    // Mass diagnostic: row 0's key, for its score at the end (the last wavefront, which the
+    // output merge leaves free).
+    uint4 k0 = make_uint4(0, 0, 0, 0);
+    if constexpr (MASS) {
+        if (wave == kWaves - 1) k0 = reinterpret_cast<const uint4 *>(kb)[lane % AS::LPR];
+    }
     const int wn = qi.base + qi.wcount;  // anchor and window rows
     auto row_at = [&](int c) -> size_t { return c < qi.base ? 0 : (size_t)(qi.wlo - qi.base + c); };
     // Anchor and window on wavefronts 1..kWaves-1 (partials 0..kWaves-2), computed while
@@ -581,26 +587,19 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
             // Mass diagnostic (section 3.2.2, the full-softmax mass outside C_i; sections
             // 2.2.1-2.2.3, the parts of C_i): the candidates' part from the blocks' sums, the
             // window part (with row 0) and the top-k part from the partials, row 0 from its score;
-            // all relative to one maximum.
-            if (wave == 0) {
-                auto fold = [&](int p0, int np, float *mo, float *lo) {
-                    float mx = -INFINITY;
-                    for (int p = p0; p < p0 + np; ++p) mx = fmaxf(mx, sh.part.m[p]);
-                    float sm = 0.f;
-                    for (int p = p0; p < p0 + np; ++p)
-                        sm += sh.part.m[p] == -INFINITY ? 0.f : sh.part.l[p] * exp2f((sh.part.m[p] - mx) * a.scale_log2e);
-                    *mo = mx;
-                    *lo = sm;
+            // all relative to one maximum. On the last wavefront, while the others write the
+            // output.
+            if (wave == kWaves - 1) {
+                auto fold = [&](const float *pm, const float *pl, int np, float &mx, float &sm) {
+                    const float m = lane < np ? pm[lane] : -INFINITY;
+                    const float l = lane < np ? pl[lane] : 0.f;
+                    mx = wave_max_f32_dpp(m);
+                    sm = wave_sum_f32_dpp(m == -INFINITY ? 0.f : l * exp2f((m - mx) * a.scale_log2e));
                 };
-                float mw, lw, mt, lt;
-                fold(0, NWW, &mw, &lw);
-                fold(NWW, kWaves, &mt, &lt);
-                float mr = -INFINITY;
-                for (int p = 0; p < kWaves; ++p) mr = fmaxf(mr, sh.zm[p]);
-                float lr = 0.f;
-                for (int p = 0; p < kWaves; ++p)
-                    lr += sh.zm[p] == -INFINITY ? 0.f : sh.zl[p] * exp2f((sh.zm[p] - mr) * a.scale_log2e);
-                const uint4 k0 = reinterpret_cast<const uint4 *>(kb)[lane % AS::LPR];
+                float mw, lw, mt, lt, mr, lr;
+                fold(sh.part.m, sh.part.l, NWW, mw, lw);
+                fold(sh.part.m + NWW, sh.part.l + NWW, kWaves, mt, lt);
+                fold(sh.zm, sh.zl, kWaves, mr, lr);
                 const float s0 = row_sum<AS::LPR>(dot16(k0, qs, 0.f, T()));
                 const float mgm = fmaxf(mr, mw);
                 auto rel = [&](float mx, float sm) { return mx == -INFINITY ? 0.f : sm * exp2f((mx - mgm) * a.scale_log2e); };

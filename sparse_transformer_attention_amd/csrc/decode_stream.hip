@@ -128,11 +128,14 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     const uint32_t k1 = (uint32_t)(e[0] >> 8);
     float zl = 0.f, zm = -INFINITY;
     if constexpr (MASS) {
+        // (Every term is at most 1: zm is the block's best score. The hardware exponential
+        // flushes terms below 2^-126 to zero.)
         zm = k1 ? key_score(k1) : -INFINITY;
+        const float zmc = k1 ? zm * a.scale_log2e : 0.f;
         float zsum = 0.f;
 #pragma unroll
         for (int c = 0; c < 16; ++c)
-            if (kk[c]) zsum += exp2f((key_score(kk[c]) - zm) * a.scale_log2e);
+            zsum += kk[c] ? __builtin_amdgcn_exp2f(__builtin_fmaf(key_score(kk[c]), a.scale_log2e, -zmc)) : 0.f;
         zl = row16_sum_f32(zsum);
     }
     const int blk = wg_row0 / kRows + b2;

@@ -26,6 +26,11 @@ struct FinishArgs {
     const uint64_t *lists;  // [nqv][wpu][seg] segments of candidate ranking keys
     const float *win;       // [nqv][D + 2] anchor-and-window partials (MFMA path), or null
     int64_t nqv;            // query vectors (the grid covers at least this many workgroups)
+    // Mass diagnostic (MFMA path; null: off): per query the bound pass's (reference score m,
+    // sum over R_i of exp2((s - m) * scale_log2e)), and the output [nqv][4] = excluded mass,
+    // anchor, window without position 0, top-k.
+    const float2 *zmass;
+    float *mass;
 };
 
 // Workgroup grid of one workgroup per query vector: x up to 2^16, y the rest (a launch's
@@ -234,6 +239,44 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
         // Window partials: NW-1 (from mfma_window), 1..NW-1 (wavefront 0 took the bound) or
         // 0..NW-1; top-k partials NW..2NW-1.
         const int p0 = pre_win ? NW - 1 : (kp > 0 ? 1 : 0);
+        if (a.mass && tid < 64) {
+            // Mass diagnostic (pages of "The Condensate Theorem", metaphor-xennon blog: section
+            // 3.2.2, the full-softmax mass outside C_i; sections 2.2.1-2.2.3, the parts of C_i):
+            // the sum over the candidate rows R_i from the bound pass, the window part (with
+            // row 0) and the top-k part from the partials above, row 0's own weight from its
+            // score; all relative to one maximum.
+            // (Rows of a query without candidates may enter its wavefront's sum in the bound
+            // pass; R_i is empty for it, so the sum is not read.)
+            const float2 z = kp > 0 ? a.zmass[qv] : make_float2(-INFINITY, 0.f);
+            const float mr = z.x, lr = z.y;
+            auto range = [&](int q0, int q1, float &mx, float &sm) {
+                const int pc = lane < 2 * NW ? lane : 2 * NW - 1;
+                const float pm = lane >= q0 && lane < q1 ? part.m[pc] : -INFINITY;
+                const float pl = lane >= q0 && lane < q1 ? part.l[pc] : 0.f;
+                mx = wave_max_f32_dpp(pm);
+                sm = wave_sum_f32_dpp(pm == -INFINITY ? 0.f : pl * exp2f((pm - mx) * a.scale_log2e));
+            };
+            float mw, lw, mt = -INFINITY, lt = 0.f;
+            range(p0, NW, mw, lw);
+            if (kp > 0) range(NW, NW + top_waves, mt, lt);
+            using S = AttendShape<D, T>;
+            const uint4 k0 = reinterpret_cast<const uint4 *>(kb)[lane % S::LPR];
+            const float s0 = row_sum<S::LPR>(dot16(k0, qs, 0.f, T()));
+            const float mg = fmaxf(mr, mw);
+            auto rel = [&](float mx, float sm) {
+                return mx == -INFINITY ? 0.f : sm * exp2f((mx - mg) * a.scale_log2e);
+            };
+            const float zr = rel(mr, lr), zw = rel(mw, lw), zt = rel(mt, lt);
+            const float z0 = exp2f((s0 - mg) * a.scale_log2e);
+            const float zf = zr + zw;
+            if (lane == 0) {
+                float *mo = a.mass + qv * 4;
+                mo[0] = fmaxf(zr - zt, 0.f) / zf;
+                mo[1] = z0 / zf;
+                mo[2] = fmaxf(zw - z0, 0.f) / zf;
+                mo[3] = zt / zf;
+            }
+        }
         merge_partials<NT, D>(part, p0, kp > 0 ? NW + top_waves : NW, a.scale_log2e, out + qv * D);
     }
 }
@@ -300,6 +343,8 @@ FinishArgs finish_args(const Plan &pl, const void *ws) {
     a.lists = ws ? reinterpret_cast<const uint64_t *>(static_cast<const char *>(ws) + pl.lists_offset) : nullptr;
     const char *wb = static_cast<const char *>(ws);
     a.win = ws && pl.mfma ? reinterpret_cast<const float *>(wb + pl.win_offset) : nullptr;
+    a.zmass = ws && pl.mfma ? reinterpret_cast<const float2 *>(wb + pl.zmass_offset) : nullptr;
+    a.mass = nullptr;
     a.nqv = pl.nqv;
     return a;
 }
@@ -311,8 +356,9 @@ constexpr int64_t kWideBelow = 4096;
 
 template <typename T, int D, bool ATTEND>
 hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const void *k,
-                           const void *v, int32_t *out_idx, float *out, hipStream_t s) {
-    const FinishArgs a = finish_args(pl, ws);
+                           const void *v, int32_t *out_idx, float *out, hipStream_t s, float *mass) {
+    FinishArgs a = finish_args(pl, ws);
+    a.mass = mass;
     const size_t shmem = (size_t)pl.cap * (2 * sizeof(int32_t)) + (size_t)pl.topk * sizeof(uint64_t);
     const dim3 grid = qv_grid(pl.nqv);
     const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v);
@@ -351,10 +397,10 @@ hipError_t launch_attend_t(const Plan &pl, const void *q, const void *k, const v
 }  // namespace
 
 hipError_t launch_finish(const Plan &pl, const void *ws, const void *q, const void *k,
-                         const void *v, int32_t *out_idx, float *out, hipStream_t s) {
+                         const void *v, int32_t *out_idx, float *out, hipStream_t s, float *mass) {
     const bool attend = out != nullptr;
-#define CA_FIN(T, D) (attend ? launch_finish_t<T, D, true>(pl, ws, q, k, v, out_idx, out, s) \
-                             : launch_finish_t<T, D, false>(pl, ws, q, k, v, out_idx, out, s))
+#define CA_FIN(T, D) (attend ? launch_finish_t<T, D, true>(pl, ws, q, k, v, out_idx, out, s, mass) \
+                             : launch_finish_t<T, D, false>(pl, ws, q, k, v, out_idx, out, s, nullptr))
     if (pl.dtype == 1) return pl.d == 128 ? CA_FIN(__bf16, 128) : CA_FIN(__bf16, 64);
     return pl.d == 128 ? CA_FIN(float, 128) : CA_FIN(float, 64);
 #undef CA_FIN

@@ -57,7 +57,28 @@ struct MfmaArgs {
     uint32_t *tau;         // [nqv] bound of each query (score key; 0xFFFFFFFF: no candidates)
     uint32_t *cnt;         // [nqv][4] list lengths
     uint64_t *lists;       // [nqv][4][kMfmaSeg] ranking keys: list g is kept by lane group g
+    float scale_log2e;     // log2(e) / sqrt(d)
+    float2 *zmass;         // bound pass with the mass diagnostic: [nqv] (m, l), l = sum over R_i
+                           // of exp2((s - m) * scale_log2e), m within 64 / scale_log2e of the best s
 };
+
+// Running softmax sum over a lane's scores against a reference score m: l = sum of
+// exp2((s - m) * c). The reference moves (and l is rescaled) only when a score passes it by more
+// than 64 / c, so each term stays below 2^64 and most calls take one fma and one exponential per
+// score. mc = m * c.
+__device__ __forceinline__ void softmax_fold(float &m, float &mc, float &l, float bm, float c,
+                                             const float (&s)[4], const bool (&ok)[4]) {
+    if (bm > m + 64.f / c) {
+        const float mn = bm;
+        l = m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f((m - mn) * c);
+        m = mn;
+        mc = mn * c;
+    }
+    float add = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) add += ok[r] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mc)) : 0.f;
+    l += add;
+}
 
 // Inverse of score_key for the admission test in float: keys below every finite score give
 // -inf, the "no candidates" key 0xFFFFFFFF gives +inf.
@@ -80,6 +101,13 @@ __device__ __forceinline__ uint32_t quad_sum_f32_bits(uint32_t x) {
     float y = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
     const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
     return __float_as_uint(__uint_as_float(r32[0]) + __uint_as_float(r32[1]));
+}
+// Float maximum over the same four lanes.
+__device__ __forceinline__ float quad_max_f32(float x) {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t x) {
     const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
@@ -106,7 +134,7 @@ __device__ __forceinline__ int chunk_at(int row, int c) {
     return row * (D / 8) + (c ^ chunk_swizzle<D>(row));
 }
 
-template <int D, int QB, bool CAND, bool PRE, int NWV>
+template <int D, int QB, bool CAND, bool PRE, int NWV, bool MASS = false>
 __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__restrict__ q,
                                                           const __bf16 *__restrict__ k,
                                                           MfmaArgs a) {
@@ -210,6 +238,16 @@ __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__r
     // which is all the bound needs, and the maximum costs one integer instruction per score (a
     // float maximum would first quiet each product as a possible NaN).
     int32_t m[2][4][4][QB];
+    // Mass diagnostic (bound pass): this lane's softmax sum over its candidate scores per query.
+    float zm[QB], zmc[QB], zl[QB];
+    if constexpr (MASS) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            zm[qb] = -INFINITY;
+            zmc[qb] = 0.f;
+            zl[qb] = 0.f;
+        }
+    }
     if constexpr (!CAND) {
 #pragma unroll
         for (int p = 0; p < 2; ++p)
@@ -332,6 +370,21 @@ __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__r
                         if constexpr (!INNER) v = (jb + r >= 1 && jb + r <= lim[qb]) ? v : INT32_MIN;
                         m[P][kb][r][qb] = v > m[P][kb][r][qb] ? v : m[P][kb][r][qb];
                     }
+                if constexpr (MASS) {
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        float sv[4];
+                        bool ok[4];
+                        float bm = -INFINITY;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            sv[r] = acc[qb][r];
+                            ok[r] = INNER || (jb + r >= 1 && jb + r <= lim[qb]);
+                            if (ok[r]) bm = fmaxf(bm, sv[r]);
+                        }
+                        softmax_fold(zm[qb], zmc[qb], zl[qb], bm, a.scale_log2e, sv, ok);
+                    }
+                }
             } else {
                 // About k + k/4 of a query's rows reach its bound, so a block of 16 rows
                 // holds few of them. With PRE, per query block, a test of the largest of a
@@ -482,6 +535,14 @@ __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__r
             }
             if (grp == 0 && lim[qb] != -1) a.tau[qvi[qb]] = tau;
             if (grp == 0 && lim[qb] == -1 && idx_w + qb * 16 + col < a.nvec) a.tau[qvi[qb]] = 0xFFFFFFFFu;
+            if constexpr (MASS) {
+                // The query's four lanes merged: (largest reference score, sum relative to it)
+                // over R_i.
+                const float m4 = quad_max_f32(zm[qb]);
+                const float l4 = __uint_as_float(quad_sum_f32_bits(__float_as_uint(
+                    zm[qb] == -INFINITY ? 0.f : zl[qb] * exp2f((zm[qb] - m4) * a.scale_log2e))));
+                if (grp == 0 && idx_w + qb * 16 + col < a.nvec) a.zmass[qvi[qb]] = make_float2(m4, l4);
+            }
         }
     } else {
 #pragma unroll
@@ -875,7 +936,7 @@ __global__ __launch_bounds__(256) void mfma_dense_kernel(const __bf16 *__restric
 }  // namespace
 
 hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void *ws, hipStream_t s,
-                              int pass) {
+                              int pass, bool mass) {
     MfmaArgs a;
     a.n = pl.n; a.nq = pl.nq; a.Hq = pl.Hq; a.Hkv = pl.Hkv; a.g = pl.g; a.W = pl.W; a.topk = pl.topk;
     a.nvec = (uint32_t)(pl.g * pl.nq);
@@ -883,6 +944,8 @@ hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void
     a.tau = reinterpret_cast<uint32_t *>(w + pl.slots_offset);
     a.cnt = reinterpret_cast<uint32_t *>(w + pl.slots_offset) + 2 * pl.nqv * pl.wpu;
     a.lists = reinterpret_cast<uint64_t *>(w + pl.lists_offset);
+    a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
+    a.zmass = reinterpret_cast<float2 *>(w + pl.zmass_offset);
     const bool cand = pass != 0;
     const int qb_bound = pl.d == 128 ? kMfmaQBBound128 : kMfmaQBBound64;
     const int rows = 16 * kMfmaWaves * (cand ? kMfmaQBCand : qb_bound);
@@ -898,7 +961,8 @@ hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void
     const bool pre = mean_rows > 1024 * (int64_t)pl.topk;
 #define CA_MFMA_SELECT(D)                                                                          \
     do {                                                                                           \
-        if (!cand) hipLaunchKernelGGL((mfma_select_kernel<D, D == 128 ? kMfmaQBBound128 : kMfmaQBBound64, false, false, kMfmaWaves>), grid, block, 0, s, qt, kt, a); \
+        if (!cand && mass) hipLaunchKernelGGL((mfma_select_kernel<D, D == 128 ? kMfmaQBBound128 : kMfmaQBBound64, false, false, kMfmaWaves, true>), grid, block, 0, s, qt, kt, a); \
+        else if (!cand) hipLaunchKernelGGL((mfma_select_kernel<D, D == 128 ? kMfmaQBBound128 : kMfmaQBBound64, false, false, kMfmaWaves>), grid, block, 0, s, qt, kt, a); \
         else if (pre) hipLaunchKernelGGL((mfma_select_kernel<D, kMfmaQBCand, true, true, kMfmaWaves>), grid, block, 0, s, qt, kt, a); \
         else hipLaunchKernelGGL((mfma_select_kernel<D, kMfmaQBCand, true, false, kMfmaWaves>), grid, block, 0, s, qt, kt, a); \
     } while (0)

@@ -40,9 +40,27 @@ CASES = {
 }
 
 
-def run_both(w, x):
+# bf16 with at least 64 query vectors per KV head and topk <= 128: the matrix-core prefill
+# path, where the bound pass also sums each query's softmax over R_i and finish adds the parts.
+MFMA_CASES = {
+    "mfma_mha_d128_ragged": W_(heads=2, kv_heads=2, n=2000, nq=600, W=64, topk=64),
+    # Every position a query: the first rows have no candidates (R_i empty) and share
+    # wavefronts with rows that have them.
+    "mfma_full_causal_d64": W_(d=64, heads=2, kv_heads=1, n=700, nq=700, W=16, topk=8),
+    "mfma_gqa4_d64_w1024": W_(d=64, heads=8, kv_heads=2, n=2600, nq=300, W=1024, topk=32),
+    "mfma_gqa8_b2_d128": W_(batch=2, heads=16, kv_heads=2, n=1800, nq=90, W=40, topk=24),
+}
+
+
+def run_both(w, x, path=None):
     q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
+    if path:
+        ca.profile_start(8)
     out, idx, mass = ca.condensate_mass(q, k, v, w.W, w.topk)
+    torch.cuda.synchronize()
+    if path:
+        prof = ca.profile_stop()
+        assert path in prof, f"{path} not taken: {sorted(prof)}"
     out2, idx2 = ca.condensate(q, k, v, w.W, w.topk)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
@@ -60,6 +78,35 @@ def test_mass_matches_oracle(name):
     ref = diag[..., MASS_COLS]
     assert np.allclose(mass, ref, rtol=RTOL, atol=ATOL), np.abs(mass - ref).max()
     assert np.allclose(mass.sum(axis=-1), 1.0, atol=1e-5)
+
+
+@pytest.mark.parametrize("name", list(MFMA_CASES))
+def test_mass_mfma_path_matches_oracle(name):
+    w = MFMA_CASES[name]
+    x = synth.make_inputs(w, seed=13)
+    announce(f"mass {name}")
+    _, _, mass = run_both(w, x, path="mfma_bound")
+    _, _, diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    ref = diag[..., MASS_COLS]
+    assert np.allclose(mass, ref, rtol=RTOL, atol=ATOL), np.abs(mass - ref).max()
+    assert np.allclose(mass.sum(axis=-1), 1.0, atol=1e-5)
+
+
+def test_mass_full_size_prefill_chunk_4k_32k_sampled_rows():
+    """The 4,096-position chunk at 32K context (the MFMA path at its full size): 24 rows spread
+    over heads and positions, each against the oracle row by row."""
+    w = synth.WORKLOADS["prefill_chunk_4k_32k_bf16"]
+    x = synth.make_inputs(w, device="cuda")
+    announce("mass full-size prefill chunk 4k x 32k")
+    _, _, mass = run_both(w, x, path="mfma_bound")
+    xh = {t: x[t].cpu() for t in ("q", "k", "v")}
+    g = np.random.default_rng(5)
+    rows = [(0, int(h), int(r)) for h, r in zip(g.integers(0, w.heads, 24), g.integers(0, w.nq, 24))]
+    rows += [(0, 0, 0), (0, w.heads - 1, w.nq - 1)]
+    _, _, diag = oracle.condensate(xh["q"], xh["k"], xh["v"], w.W, w.topk, rows=rows)
+    ref = diag[:, MASS_COLS]
+    got = np.stack([mass[b, h, r] for b, h, r in rows])
+    assert np.allclose(got, ref, rtol=RTOL, atol=ATOL), np.abs(got - ref).max()
 
 
 def test_mass_full_size_decode_131k_all_32_vectors():
