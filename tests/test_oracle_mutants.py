@@ -51,3 +51,20 @@ def test_pins_reject_planted_mistake(name, tmp_path):
                           os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert res.returncode != 0, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_sweep_rejects_planted_mistake(name, tmp_path):
+    """The property sweep (random shapes) alone also catches every planted mistake."""
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    csrc = tmp_path / "mutant.c"
+    csrc.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-std=c11", "-O1", "-fopenmp", "-fPIC", "-shared", "-w",
+                           "-o", str(so), str(csrc), "-lm"])
+    env = dict(os.environ, CONDENSATE_ORACLE_LIB=str(so), OMP_NUM_THREADS="2")
+    res = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                          os.path.join(ROOT, "tests", "test_oracle_sweep.py")],
+                         cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert res.returncode != 0, f"the sweep did not catch mutant {name}:\n{res.stdout[-2000:]}"
