@@ -14,11 +14,14 @@
 //
 // The exact top-k' of R_i (k' = min(k, |R_i|) <= 128) takes two passes over the same products
 // (the same instruction sequence, hence bit-identical scores):
-//   bound  For each query, one score of its candidate rows in each of the 128 classes j mod 128
-//          (the class maximum whenever the class holds a non-negative score). The classes are
-//          disjoint, so k' distinct rows reach the k'-th largest of those scores: a lower bound
-//          of the query's k'-th score. The lower edge of the 16-bit radix bin that holds it goes
-//          out as a score key.
+//   bound  For each query, one score of its candidate rows in each of 128 disjoint classes (a
+//          row's place in its pair of tiles; the class maximum whenever the class holds a
+//          non-negative score), so k' distinct rows reach the k'-th largest of those scores: a
+//          lower bound of the query's k'-th score. The lower edge of the 16-bit radix bin that
+//          holds it goes out as a score key. A bound from a subset of the rows is a lower bound
+//          too, only a looser one: with k <= 64 the pass reads KEEP of every 4 tiles (2 for
+//          k <= 32, 3 for k <= 64), trading its products for more appends in the next pass
+//          (about 1.25 k * 4 / KEEP rows reach it, within the lists' 256 entries).
 //   cand   Every candidate row whose score key reaches the bound is appended to the query's
 //          list as a ranking key (about k + k/4 of them on Gaussian data). A list that might
 //          not take another tile is cut to its exact top-k' (wave_keep_top_u64); from then on
@@ -134,7 +137,7 @@ __device__ __forceinline__ int chunk_at(int row, int c) {
     return row * (D / 8) + (c ^ chunk_swizzle<D>(row));
 }
 
-template <int D, int QB, bool CAND, bool PRE, int NWV, bool MASS = false>
+template <int D, int QB, bool CAND, bool PRE, int NWV, bool MASS = false, int KEEP = 4>
 __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__restrict__ q,
                                                           const __bf16 *__restrict__ k,
                                                           MfmaArgs a) {
@@ -213,6 +216,12 @@ __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__r
         vec_of(last, qv_last, jmax);
     }
     const int ntiles = jmax >= 1 ? jmax / kTile + 1 : 0;
+    // Step v takes tile tile_of(v): every tile, or (bound pass without the mass sum) the first
+    // KEEP of every 4.
+    constexpr int kKeep = !CAND && !MASS ? KEEP : 4;
+    static_assert(kKeep >= 2 && kKeep <= 4, "keep");
+    auto tile_of = [](int v) { return kKeep == 4 ? v : (v / kKeep) * 4 + v % kKeep; };
+    const int nsteps = (ntiles / 4) * kKeep + (ntiles % 4 < kKeep ? ntiles % 4 : kKeep);
 
     // Candidate pass: admission key of each query (a score is appended when its key reaches
     // adm, tested first as a float against tf) and the length of this lane's list of it.
@@ -278,7 +287,7 @@ __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__r
     const char *kbytes = reinterpret_cast<const char *>(kbase);
     auto issue = [&](int t, auto bufc) {
         constexpr int B = decltype(bufc)::value;
-        const int j0 = t * kTile;
+        const int j0 = tile_of(t) * kTile;
 #pragma unroll
         for (int u = 0; u < NCH; ++u) {
             const int j = j0 + lrow[u];
@@ -334,7 +343,7 @@ __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__r
     auto compute = [&](int t, auto bufc) {
         constexpr int B = decltype(bufc)::value;
         constexpr int P = B & 1;
-        const int j0 = t * kTile;
+        const int j0 = tile_of(t) * kTile;
         const bool inner = j0 >= 1 && j0 + kTile - 1 <= lim_lo;
         // Operand rows of block kb from LDS. The bound pass issues them a block ahead of their
         // products, with a scheduling barrier that keeps the compiler from moving the products
@@ -477,7 +486,7 @@ __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__r
         __builtin_amdgcn_s_waitcnt(kWaitAhead);
         asm volatile("s_barrier" ::: "memory");
         issue(t + kBuf - 1, std::integral_constant<int, (B + kBuf - 1) % kBuf>());
-        if (t <= t_wave) compute(t, bufc);
+        if (tile_of(t) <= t_wave) compute(t, bufc);
     };
     // Tiles past the last one are fetched too (clamped rows, never read), so that every wait
     // counts the same loads.
@@ -485,11 +494,11 @@ __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__r
     issue(1, std::integral_constant<int, 1>());
     issue(2, std::integral_constant<int, 2>());
     static_assert(kBuf == 4, "ring");
-    for (int t0 = 0; t0 < ntiles; t0 += kBuf) {
+    for (int t0 = 0; t0 < nsteps; t0 += kBuf) {
         step(t0, std::integral_constant<int, 0>());
-        if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 1>());
-        if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>());
-        if (t0 + 3 < ntiles) step(t0 + 3, std::integral_constant<int, 3>());
+        if (t0 + 1 < nsteps) step(t0 + 1, std::integral_constant<int, 1>());
+        if (t0 + 2 < nsteps) step(t0 + 2, std::integral_constant<int, 2>());
+        if (t0 + 3 < nsteps) step(t0 + 3, std::integral_constant<int, 3>());
     }
     // No LDS fill may outlive the workgroup.
     __builtin_amdgcn_s_waitcnt(0);
@@ -959,9 +968,13 @@ hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void
     // averaging 64K and k = 32, +4% with 30K rows and k = 64). Rows: the mean over the queries.
     const int64_t mean_rows = pl.n - pl.nq / 2 - pl.W;
     const bool pre = mean_rows > 1024 * (int64_t)pl.topk;
+    // Bound pass: tiles kept of every 4 (the mass sum needs every row).
+    const int keep = pl.topk <= 32 ? 2 : (pl.topk <= 64 ? 3 : 4);
 #define CA_MFMA_SELECT(D)                                                                          \
     do {                                                                                           \
         if (!cand && mass) hipLaunchKernelGGL((mfma_select_kernel<D, D == 128 ? kMfmaQBBound128 : kMfmaQBBound64, false, false, kMfmaWaves, true>), grid, block, 0, s, qt, kt, a); \
+        else if (!cand && keep == 2) hipLaunchKernelGGL((mfma_select_kernel<D, D == 128 ? kMfmaQBBound128 : kMfmaQBBound64, false, false, kMfmaWaves, false, 2>), grid, block, 0, s, qt, kt, a); \
+        else if (!cand && keep == 3) hipLaunchKernelGGL((mfma_select_kernel<D, D == 128 ? kMfmaQBBound128 : kMfmaQBBound64, false, false, kMfmaWaves, false, 3>), grid, block, 0, s, qt, kt, a); \
         else if (!cand) hipLaunchKernelGGL((mfma_select_kernel<D, D == 128 ? kMfmaQBBound128 : kMfmaQBBound64, false, false, kMfmaWaves>), grid, block, 0, s, qt, kt, a); \
         else if (pre) hipLaunchKernelGGL((mfma_select_kernel<D, kMfmaQBCand, true, true, kMfmaWaves>), grid, block, 0, s, qt, kt, a); \
         else hipLaunchKernelGGL((mfma_select_kernel<D, kMfmaQBCand, true, false, kMfmaWaves>), grid, block, 0, s, qt, kt, a); \
