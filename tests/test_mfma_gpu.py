@@ -2,7 +2,8 @@
 
 The library takes this path by itself for bf16 problems with at least 64 query vectors per KV
 head and topk <= 128; every test checks through the library's profiler that its two kernels
-(mfma_bound, mfma_cand) ran. Index sets must match the oracle's outside the tie band (exactly,
+(mfma_bound, mfma_cand) ran. The shapes cover the three bound-pass tilings: 2 of every 4 key
+tiles (topk <= 32), 3 of 4 (topk <= 64) and all of them (topk > 64). Index sets must match the oracle's outside the tie band (exactly,
 with integer inputs), outputs the oracle's restricted softmax on the GPU's own set.
 """
 import sys
@@ -91,6 +92,9 @@ def integer_inputs(w, seed, levels=2):
     # Over 1024 rows per kept key: the candidate pass with its block pre-test (and here the
     # pre-test lets every block of a tied bound through to the exact compare).
     dict(d=128, heads=2, kv_heads=2, n=3000, nq=64, W=30, topk=2),
+    # 32 < k <= 64: the bound pass reads 3 of every 4 tiles (k <= 32 above: 2 of 4; k = 128:
+    # every tile), and many more rows than k tie at that looser bound.
+    dict(d=128, heads=4, kv_heads=2, n=2800, nq=96, W=40, topk=48),
 ])
 def test_mfma_exact_ties_follow_the_tie_break(shape):
     """Many keys tie at the bound, so candidate lists fill and are cut to their exact top-k'
