@@ -126,11 +126,10 @@ int ca_condensate_attention_noscratch(const ca_params *p, const void *q, const v
  * outside C_i, of position 0, of the window positions other than 0, and of the top-k positions
  * (the four sum to 1; fp32 sums, so eps is resolved to about 1e-6 of the candidates' mass). The
  * candidates' part of the full normaliser is summed inside the pass that already scores every
- * candidate row (the decode path's streaming pass, the matrix-core prefill path's bound pass).
- * Only for problems that take one of those two paths (chunk = 0, some query with candidates;
- * decode: the key buffer within its budget; prefill: bf16, at least 64 query vectors per KV
- * head, topk <= 128); others return CA_ERR_UNSUPPORTED before any HIP call. The set and the
- * output are those of ca_condensate_attention_ex, bit for bit. Same workspace. */
+ * candidate row (the decode path's streaming pass, the matrix-core prefill path's bound pass,
+ * the chunked path's selection pass). Problems without any candidate row (topk = 0, or no
+ * query with i > W) return CA_ERR_UNSUPPORTED before any HIP call. The set and the output are
+ * those of ca_condensate_attention_ex, bit for bit. Same workspace. */
 int ca_condensate_attention_mass_ex(const ca_params *p, const void *q, const void *k,
                                     const void *v, float *out, int32_t *out_idx, float *mass,
                                     void *ws, size_t ws_bytes, void *stream);

@@ -238,10 +238,10 @@ def condensate(q, k, v, W: int, topk: int, chunk: int = 0, ws=None, stream=None)
     return out, out_idx
 
 
-def condensate_mass(q, k, v, W: int, topk: int, ws=None, stream=None):
+def condensate_mass(q, k, v, W: int, topk: int, chunk: int = 0, ws=None, stream=None):
     """As condensate(), with the mass diagnostic: returns (out, out_idx, mass float32
     [B][Hq][nq][4] = excluded mass, anchor, window without position 0, top-k)."""
-    p = params_for(q, k, W, topk, 0)
+    p = params_for(q, k, W, topk, chunk)
     B, Hq, nq, d = q.shape
     out = torch.empty((B, Hq, nq, d), dtype=torch.float32, device=q.device)
     out_idx = torch.empty((B, Hq, nq, 1 + W + topk), dtype=torch.int32, device=q.device)

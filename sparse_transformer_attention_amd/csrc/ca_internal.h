@@ -46,7 +46,8 @@ struct Plan {
     // wpu = 4 segments of seg = kMfmaSeg keys per query.
     bool mfma;
     size_t win_offset;    // MFMA path: anchor-and-window partials [nqv][d + 2] floats
-    size_t zmass_offset;  // MFMA path, mass diagnostic: [nqv] (largest score, sum) over R_i
+    size_t zmass_offset;  // mass diagnostic: [nqv] (MFMA path) or [nqv][wpu] (chunked path)
+                          // (reference score, sum) over R_i
     int64_t rstride;
     int nblk;
     size_t summ_offset, scratch_offset;
@@ -54,8 +55,10 @@ struct Plan {
 
 
 // Launchers (enqueue only; return the hipError_t of the last launch).
+// mass: also each workgroup's softmax sum over its rows of R_i, per query ([nqv][wpu] at
+// zmass_offset).
 hipError_t launch_score_select(const Plan &pl, const void *q, const void *k, void *ws,
-                               hipStream_t s);
+                               hipStream_t s, bool mass = false);
 // Merge + set assembly (+ restricted softmax times V when out != nullptr), one workgroup per
 // query vector (chunked and MFMA paths).
 // mass != nullptr (MFMA path): also [nqv][4] = excluded mass, anchor, window, top-k.

@@ -222,7 +222,8 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     const size_t slot_bytes = ((size_t)(3 * P.nqv * P.wpu) * sizeof(uint32_t) + 255) & ~(size_t)255;
     P.slots_offset = 0;
     P.lists_offset = P.slots_offset + slot_bytes;
-    P.ws_bytes = P.candidates ? P.lists_offset + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) : 0;
+    P.zmass_offset = (P.lists_offset + (size_t)P.nqv * (size_t)P.lmax * sizeof(uint64_t) + 255) & ~(size_t)255;
+    P.ws_bytes = P.candidates ? P.zmass_offset + (size_t)P.nqv * (size_t)P.wpu * 2 * sizeof(float) : 0;
     if (ca::topk_lds_bytes(P) > 64 * 1024)
         return fail(CA_ERR_UNSUPPORTED, "selection buffers exceed the LDS budget");
     return CA_OK;
@@ -271,7 +272,7 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
         return CA_OK;
     } else if (pl.candidates) {
         ProfScope ps(K_SCORE, s);
-        e = ca::launch_score_select(pl, q, k, ws, s);
+        e = ca::launch_score_select(pl, q, k, ws, s, mass != nullptr);
         ps.done();
         if (e != hipSuccess) return hip_fail(e, "score_topk launch");
     }
@@ -404,9 +405,9 @@ int ca_condensate_attention_mass_ex(const ca_params *p, const void *q, const voi
     ca::Plan pl;
     int rc = make_plan(p, &pl);
     if (rc != CA_OK) return rc;
-    if (!(pl.candidates && (pl.stream || pl.mfma)))
-        return fail(CA_ERR_UNSUPPORTED, "the mass diagnostic needs the decode path or the matrix-core prefill "
-                                        "path (chunk 0, some query with candidates)");
+    if (!pl.candidates)
+        return fail(CA_ERR_UNSUPPORTED, "the mass diagnostic needs a scoring pass: some query with candidates "
+                                        "(topk > 0 and i > W)");
     if (!q || !k || !v || !out || !out_idx || !mass)
         return fail(CA_ERR_INVALID_ARG, "q, k, v, out, out_idx and mass must be non-NULL");
     if ((rc = check_ws(pl, ws, ws_bytes)) != CA_OK) return rc;

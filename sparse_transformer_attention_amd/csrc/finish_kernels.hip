@@ -30,6 +30,7 @@ struct FinishArgs {
     // sum over R_i of exp2((s - m) * scale_log2e)), and the output [nqv][4] = excluded mass,
     // anchor, window without position 0, top-k.
     const float2 *zmass;
+    int zw;  // zmass entries per query: 1 (MFMA path) or wpu (chunked path)
     float *mass;
 };
 
@@ -246,9 +247,18 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
             // row 0) and the top-k part from the partials above, row 0's own weight from its
             // score; all relative to one maximum.
             // (Rows of a query without candidates may enter its wavefront's sum in the bound
-            // pass; R_i is empty for it, so the sum is not read.)
-            const float2 z = kp > 0 ? a.zmass[qv] : make_float2(-INFINITY, 0.f);
-            const float mr = z.x, lr = z.y;
+            // pass; R_i is empty for it, so the sum is not read.) The chunked path leaves one
+            // sum per workgroup of the query's unit.
+            float mr = -INFINITY, lr = 0.f;
+            for (int w0 = 0; kp > 0 && w0 < a.zw; w0 += 64) {
+                const float2 z = w0 + lane < a.zw ? a.zmass[qv * a.zw + w0 + lane] : make_float2(-INFINITY, 0.f);
+                const float mx = wave_max_f32_dpp(z.x);
+                const float sm = wave_sum_f32_dpp(z.x == -INFINITY ? 0.f : z.y * exp2f((z.x - mx) * a.scale_log2e));
+                const float mn = fmaxf(mr, mx);
+                lr = (mr == -INFINITY ? 0.f : lr * exp2f((mr - mn) * a.scale_log2e)) +
+                     (mx == -INFINITY ? 0.f : sm * exp2f((mx - mn) * a.scale_log2e));
+                mr = mn;
+            }
             auto range = [&](int q0, int q1, float &mx, float &sm) {
                 const int pc = lane < 2 * NW ? lane : 2 * NW - 1;
                 const float pm = lane >= q0 && lane < q1 ? part.m[pc] : -INFINITY;
@@ -343,7 +353,8 @@ FinishArgs finish_args(const Plan &pl, const void *ws) {
     a.lists = ws ? reinterpret_cast<const uint64_t *>(static_cast<const char *>(ws) + pl.lists_offset) : nullptr;
     const char *wb = static_cast<const char *>(ws);
     a.win = ws && pl.mfma ? reinterpret_cast<const float *>(wb + pl.win_offset) : nullptr;
-    a.zmass = ws && pl.mfma ? reinterpret_cast<const float2 *>(wb + pl.zmass_offset) : nullptr;
+    a.zmass = ws && !pl.stream ? reinterpret_cast<const float2 *>(wb + pl.zmass_offset) : nullptr;
+    a.zw = pl.mfma ? 1 : pl.wpu;
     a.mass = nullptr;
     a.nqv = pl.nqv;
     return a;

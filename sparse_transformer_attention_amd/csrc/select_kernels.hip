@@ -36,6 +36,10 @@ struct TopkArgs {
     uint32_t *top;    // [nqv][wpu] published best keys (high words), cleared first
     uint32_t *cnt;    // [nqv][wpu] keys each workgroup leaves for the query
     uint64_t *lists;  // [nqv][wpu][topk] those keys
+    // Mass diagnostic (null: off): [nqv][wpu] per workgroup and query, a reference score m and
+    // the sum of exp2((s - m) * scale_log2e) over the workgroup's rows of R_i.
+    float2 *zpart;
+    float scale_log2e;
 };
 
 constexpr int kSlotsRead = 128;  // published slots a workgroup reads (the first ones)
@@ -91,7 +95,7 @@ __device__ __forceinline__ void emit_keys(const uint32_t (&keyv)[NS], const int 
     }
 }
 
-template <typename T, int D, int G, int RE>
+template <typename T, int D, int G, int RE, bool MASS = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RE <= 12 ? 4 : 2))) void score_topk_kernel(const T *__restrict__ q,
                                                          const T *__restrict__ k, TopkArgs a) {
     // LDS: run [G][rcap] (u64), hist [4][320], query rows [G][D] (T), list lengths [G],
@@ -181,6 +185,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RE <= 12 ? 
         uint32_t tau_pub = 0u;  // k-th key published
         uint32_t best_loc = 0u; // best key seen
         uint32_t top_pub = 0u;  // best key published
+        // Mass diagnostic: this lane's running sum for its query (writer lanes only), against a
+        // reference that moves only when a score passes it by more than 64 / scale (each term
+        // below 2^64).
+        float zm = -INFINITY, zmc = 0.f, zl = 0.f;
 
         const uint4 *kbase = reinterpret_cast<const uint4 *>(k + (int64_t)bk * a.n * D);
         int64_t c = member;
@@ -218,8 +226,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RE <= 12 ? 
                         for (int p = 0; p < P; ++p) x = dot16(kr[uu][p], qr[t][p], x, T());
                         acc[t] = x;
                     }
-                    keyv[uu] = score_key(reduce_row<LPR, G>(acc, lane));
+                    const float sc = reduce_row<LPR, G>(acc, lane);
+                    keyv[uu] = score_key(sc);
                     rowv[uu] = row0 + (gi0 + 4 * uu) * RPG + lane / LPR;
+                    if (MASS && writer && rowv[uu] < rows_end && rowv[uu] <= my_rlast) {
+                        if (sc > zm + 64.f / a.scale_log2e) {
+                            zl = zm == -INFINITY ? 0.f : zl * __builtin_amdgcn_exp2f((zm - sc) * a.scale_log2e);
+                            zm = sc;
+                            zmc = sc * a.scale_log2e;
+                        }
+                        zl += __builtin_amdgcn_exp2f(__builtin_fmaf(sc, a.scale_log2e, -zmc));
+                    }
                 }
                 emit_keys<G, U>(keyv, rowv, direct, my_thr, writer, my_t, my_rlast, row0, rows_end,
                                 qmask, my_mask, rcnt, run, a.rcap, lane);
@@ -278,6 +295,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RE <= 12 ? 
             c += a.wpu;
         }
 
+        if constexpr (MASS) {
+            // Mass diagnostic: per query, the workgroup's lanes merged (each wavefront, then the
+            // four through LDS), written by the query's wavefront.
+            __shared__ float2 zred[4][G];
+#pragma unroll
+            for (int t = 0; t < G; ++t) {
+                const float mt = wave_max_f32_dpp(my_t == t ? zm : -INFINITY);
+                const float lt = wave_sum_f32_dpp(my_t == t && zm != -INFINITY
+                                                      ? zl * __builtin_amdgcn_exp2f((zm - mt) * a.scale_log2e) : 0.f);
+                if (lane == 0) zred[wave][t] = make_float2(mt, lt);
+            }
+            __syncthreads();
+            if (w_query && lane == 0) {
+                float mx = -INFINITY;
+                for (int w = 0; w < 4; ++w) mx = fmaxf(mx, zred[w][wave].x);
+                float sm = 0.f;
+                for (int w = 0; w < 4; ++w)
+                    sm += zred[w][wave].x == -INFINITY ? 0.f
+                                                        : zred[w][wave].y * exp2f((zred[w][wave].x - mx) * a.scale_log2e);
+                a.zpart[w_qv * a.wpu + member] = make_float2(mx, sm);
+            }
+        }
         // Leave the keys that reach the best visible bound (at most k of them), and their
         // count, in this workgroup's segment of the query.
         if (w_query) {
@@ -349,7 +388,7 @@ size_t topk_lds_bytes(const Plan &pl) {
 }
 
 hipError_t launch_score_select(const Plan &pl, const void *q, const void *k, void *ws,
-                               hipStream_t s) {
+                               hipStream_t s, bool mass) {
     uint32_t *tau = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pl.slots_offset);
     const int64_t nslots = pl.nqv * pl.wpu;
     const int64_t cblocks = (2 * nslots + 255) / 256;
@@ -363,11 +402,16 @@ hipError_t launch_score_select(const Plan &pl, const void *q, const void *k, voi
     a.top = tau + nslots;
     a.cnt = tau + 2 * nslots;
     a.lists = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + pl.lists_offset);
+    a.zpart = mass ? reinterpret_cast<float2 *>(static_cast<char *>(ws) + pl.zmass_offset) : nullptr;
+    a.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)pl.d));
     const size_t shmem = topk_lds_bytes(pl);
     dim3 grid((unsigned)pl.nwg), block(256);
 #define CA_LAUNCH_TK(T, D, G)                                                                     \
     do {                                                                                          \
-        if (pl.rcap == 512)                                                                       \
+        if (mass) /* (one run size for the mass variant: 24 keys per lane hold every run) */      \
+            hipLaunchKernelGGL((score_topk_kernel<T, D, G, 24, true>), grid, block, shmem, s,    \
+                               static_cast<const T *>(q), static_cast<const T *>(k), a);         \
+        else if (pl.rcap == 512)                                                                  \
             hipLaunchKernelGGL((score_topk_kernel<T, D, G, 8>), grid, block, shmem, s,           \
                                static_cast<const T *>(q), static_cast<const T *>(k), a);         \
         else if (pl.rcap == 768)                                                                  \

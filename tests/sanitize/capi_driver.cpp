@@ -117,8 +117,8 @@ int main() {
     CHECK(ca_condensate_attention_ex(&bad[1], fake, fake, fake, fo, fi, fake, bytes, nullptr) == CA_ERR_INVALID_ARG);
     CHECK(ca_condensate_attention_mass_ex(&p, fake, fake, fake, fo, fi, nullptr, fake, bytes, nullptr) == CA_ERR_INVALID_ARG);
     CHECK(ca_condensate_attention_mass_ex(&p, fake, fake, fake, fo, fi, fo, fake, bytes - 1, nullptr) == CA_ERR_WORKSPACE);
-    const ca_params chunked = P(1, 32, 8, 128, 131072, 1, 256, 64, CA_BF16, 256);
-    CHECK(ca_condensate_attention_mass_ex(&chunked, fake, fake, fake, fo, fi, fo, fake, (size_t)1 << 40, nullptr) == CA_ERR_UNSUPPORTED);
+    const ca_params no_candidates = P(1, 32, 8, 128, 131072, 1, 256, 0, CA_BF16, 256);  // topk = 0
+    CHECK(ca_condensate_attention_mass_ex(&no_candidates, fake, fake, fake, fo, fi, fo, fake, (size_t)1 << 40, nullptr) == CA_ERR_UNSUPPORTED);
     CHECK(ca_condensate_select(&p, nullptr, fake, fi, fake, bytes, nullptr) == CA_ERR_INVALID_ARG);
     CHECK(ca_condensate_select(&p, fake, fake, fi, fake, bytes - 1, nullptr) == CA_ERR_WORKSPACE);
     CHECK(ca_attention_on_subset(&p, fake, fake, fake, nullptr, fo, nullptr) == CA_ERR_INVALID_ARG);

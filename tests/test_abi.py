@@ -152,26 +152,28 @@ def test_noscratch_entry_point_rules(lib):
 
 
 def test_mass_entry_point_rules(lib):
-    """The mass diagnostic runs on the streaming decode path and the MFMA prefill path; other
-    plans, missing pointers and short workspaces are rejected on the host."""
+    """The mass diagnostic runs on every scoring path (decode, MFMA prefill, chunked); problems
+    without candidate rows, missing pointers and short workspaces are rejected on the host."""
     vp = ctypes.c_void_p(16)
-    # A decode (streaming path) and a bf16 prefill (MFMA path): a NULL mass pointer is an
-    # argument error, a short workspace a workspace error.
+    # A decode (streaming path), a bf16 prefill (MFMA path) and the chunked path: a NULL mass
+    # pointer is an argument error, a short workspace a workspace error.
     for p in (ca.Params(batch=1, heads=4, kv_heads=1, d=128, n=4000, nq=1, W=64, topk=32,
                         dtype=ca.CA_BF16, chunk=0),
               ca.Params(batch=1, heads=2, kv_heads=2, d=128, n=2000, nq=600, W=64, topk=64,
-                        dtype=ca.CA_BF16, chunk=0)):
+                        dtype=ca.CA_BF16, chunk=0),
+              ca.Params(batch=1, heads=4, kv_heads=1, d=128, n=4000, nq=1, W=64, topk=32,
+                        dtype=ca.CA_BF16, chunk=256)):
         rc, need = ws_size(p)
         assert rc == ca.CA_OK and need > 0
         assert lib.ca_condensate_attention_mass_ex(ctypes.byref(p), vp, vp, vp, vp, vp, None, vp,
                                                    need, None) == ca.CA_ERR_INVALID_ARG
         assert lib.ca_condensate_attention_mass_ex(ctypes.byref(p), vp, vp, vp, vp, vp, vp, vp,
                                                    need - 1, None) == ca.CA_ERR_WORKSPACE
-    # The chunked path (chunk = 256) and a problem without candidates (topk = 0): unsupported.
-    for q in (ca.Params(batch=1, heads=4, kv_heads=1, d=128, n=4000, nq=1, W=64, topk=32,
-                        dtype=ca.CA_BF16, chunk=256),
-              ca.Params(batch=1, heads=2, kv_heads=2, d=128, n=2000, nq=600, W=64, topk=0,
-                        dtype=ca.CA_BF16, chunk=0)):
+    # No candidate rows (topk = 0; W >= n): unsupported.
+    for q in (ca.Params(batch=1, heads=2, kv_heads=2, d=128, n=2000, nq=600, W=64, topk=0,
+                        dtype=ca.CA_BF16, chunk=0),
+              ca.Params(batch=1, heads=2, kv_heads=2, d=128, n=200, nq=200, W=300, topk=8,
+                        dtype=ca.CA_F32, chunk=256)):
         assert lib.ca_condensate_attention_mass_ex(ctypes.byref(q), vp, vp, vp, vp, vp, vp, vp,
                                                    1 << 40, None) == ca.CA_ERR_UNSUPPORTED
         assert "mass diagnostic needs" in ca.last_error()

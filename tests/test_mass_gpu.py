@@ -52,16 +52,26 @@ MFMA_CASES = {
 }
 
 
-def run_both(w, x, path=None):
+# The chunked path (chunk = 256 / 512): one sum per workgroup of a unit, merged in finish. The
+# decode-shaped cases spread a unit's chunks over many workgroups.
+CHUNKED_CASES = {
+    "chunked_decode_gqa4_bf16": (W_(n=6000, heads=8, kv_heads=2, W=64, topk=32), 256),
+    "chunked_decode_f32_multi": (W_(dtype="f32", n=3000, nq=3, W=33, topk=17), 512),
+    "chunked_prefill_bf16_d64": (W_(d=64, heads=2, kv_heads=1, n=900, nq=300, W=40, topk=24), 256),
+    "chunked_prefill_f32_early_rows": (W_(dtype="f32", d=64, heads=2, kv_heads=2, n=500, nq=500, W=16, topk=8), 256),
+}
+
+
+def run_both(w, x, path=None, chunk=0):
     q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
     if path:
         ca.profile_start(8)
-    out, idx, mass = ca.condensate_mass(q, k, v, w.W, w.topk)
+    out, idx, mass = ca.condensate_mass(q, k, v, w.W, w.topk, chunk=chunk)
     torch.cuda.synchronize()
     if path:
         prof = ca.profile_stop()
         assert path in prof, f"{path} not taken: {sorted(prof)}"
-    out2, idx2 = ca.condensate(q, k, v, w.W, w.topk)
+    out2, idx2 = ca.condensate(q, k, v, w.W, w.topk, chunk=chunk)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
     assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
@@ -86,6 +96,18 @@ def test_mass_mfma_path_matches_oracle(name):
     x = synth.make_inputs(w, seed=13)
     announce(f"mass {name}")
     _, _, mass = run_both(w, x, path="mfma_bound")
+    _, _, diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    ref = diag[..., MASS_COLS]
+    assert np.allclose(mass, ref, rtol=RTOL, atol=ATOL), np.abs(mass - ref).max()
+    assert np.allclose(mass.sum(axis=-1), 1.0, atol=1e-5)
+
+
+@pytest.mark.parametrize("name", list(CHUNKED_CASES))
+def test_mass_chunked_path_matches_oracle(name):
+    w, chunk = CHUNKED_CASES[name]
+    x = synth.make_inputs(w, seed=17)
+    announce(f"mass {name}")
+    _, _, mass = run_both(w, x, path="score_select", chunk=chunk)
     _, _, diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
     ref = diag[..., MASS_COLS]
     assert np.allclose(mass, ref, rtol=RTOL, atol=ATOL), np.abs(mass - ref).max()
