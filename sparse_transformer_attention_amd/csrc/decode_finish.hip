@@ -70,6 +70,7 @@ struct FinShared {
     uint32_t doff[kDef];  // and their records' row offsets
     SoftmaxPartials<D, 2 * kWaves> part;  // [0, kWaves-1) anchor and window, then the top-k rows
     int wc[kWaves], wd[kWaves];           // per-wavefront counts of an append
+    int anyd[kWaves];                     // per-wavefront: some block to list after the cut
     uint32_t tw[kWaves];                  // per-wavefront bounds
     uint32_t tb;                          // the single wavefront's bound
     float zm[kWaves], zl[kWaves];         // mass diagnostic: candidates' mass per wavefront
@@ -357,18 +358,26 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
         if (sh.flag) break;
         {
             // Blocks whose X reaches the round's final threshold's score key: rows beyond the
-            // record may rank.
+            // record may rank. Usually there is none, and one barrier says so.
             const uint32_t X = rb.y;
-            const bool no[1] = {false};
-            const uint64_t nk[1] = {0ull};
             const bool okd = has && X != 0u && X >= (uint32_t)(sh.thr >> 32);
-            append_all<D, 1>(sh, no, nk, okd, ((uint64_t)X << 32) | (uint32_t)blk, rb.x);
-        }
-        __syncthreads();
-        if (sh.ndef > kDef) {
-            __syncthreads();
-            if (tid == 0) sh.flag = 1;
-            __syncthreads();
+            const bool wany = __ballot(okd) != 0ull;
+            if (lane == 0) sh.anyd[wave] = wany ? 1 : 0;
+            lds_barrier();
+            int any = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) any |= sh.anyd[w];
+            if (any) {
+                const bool no[1] = {false};
+                const uint64_t nk[1] = {0ull};
+                append_all<D, 1>(sh, no, nk, okd, ((uint64_t)X << 32) | (uint32_t)blk, rb.x);
+                __syncthreads();
+                if (sh.ndef > kDef) {
+                    __syncthreads();
+                    if (tid == 0) sh.flag = 1;
+                    __syncthreads();
+                }
+            }
         }
         if (sh.flag) break;
     }
