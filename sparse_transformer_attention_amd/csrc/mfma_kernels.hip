@@ -23,7 +23,7 @@
 //          k <= 32, 3 for k <= 64), trading its products for more appends in the next pass
 //          (about 1.25 k * 4 / KEEP rows reach it, within the lists' 256 entries).
 //   cand   Every candidate row whose score key reaches the bound is appended to the query's
-//          list as a ranking key (about k + k/4 of them on Gaussian data). A list that might
+//          list as a ranking key (about 1.25 k * 4 / KEEP of them on Gaussian data). A list that might
 //          not take another tile is cut to its exact top-k' (wave_keep_top_u64); from then on
 //          only keys above the k'-th kept one are appended, since later rows have larger
 //          positions and rank lower on equal scores.
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(64 * NWV) void mfma_select_kernel(const __bf16 *__r
                     }
                 }
             } else {
-                // About k + k/4 of a query's rows reach its bound, so a block of 16 rows
+                // About 1.25 k * 4 / KEEP of a query's rows reach its bound, so a block of 16 rows
                 // holds few of them. With PRE, per query block, a test of the largest of a
                 // lane's four scores as signed integers over their bits (for tf > 0 the same
                 // order as the float compare against tf; for other tf it lets everything
@@ -963,7 +963,7 @@ hipError_t launch_mfma_select(const Plan &pl, const void *q, const void *k, void
     const dim3 grid(a.nwg), block(64 * kMfmaWaves);
     const __bf16 *qt = static_cast<const __bf16 *>(q), *kt = static_cast<const __bf16 *>(k);
     // Candidate pass: the block pre-test pays when few blocks hold a candidate, i.e. when the
-    // queries have many rows per kept key: about 1.25k of a query's rows pass, so a block of 16
+    // queries have many rows per kept key: about 1.25k of a query's rows pass the full bound, so a block of 16
     // rows x 16 queries holds one with probability about 320k / rows (measured: -13% with rows
     // averaging 64K and k = 32, +4% with 30K rows and k = 64). Rows: the mean over the queries.
     const int64_t mean_rows = pl.n - pl.nq / 2 - pl.W;
