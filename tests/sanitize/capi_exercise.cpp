@@ -1,4 +1,4 @@
-// Host driver for running the C ABI's host-side validation and planning under AddressSanitizer
+// Host program that runs the C ABI's host-side validation and planning under AddressSanitizer
 // and UndefinedBehaviorSanitizer, without a GPU: ca_workspace_size over valid shapes, limits and
 // a pseudo-random sweep of in- and out-of-range parameters (sizes up to 2^40, where the size
 // arithmetic would overflow if it were done carelessly), and every entry point's argument checks,
@@ -138,6 +138,6 @@ int main() {
         std::fprintf(stderr, "%d checks failed\n", failures);
         return 1;
     }
-    std::printf("capi driver: all checks passed\n");
+    std::printf("capi exercise: all checks passed\n");
     return 0;
 }

@@ -1,4 +1,4 @@
-/* Host driver for running the CPU oracle under AddressSanitizer and UndefinedBehaviorSanitizer.
+/* Host program that runs the CPU oracle under AddressSanitizer and UndefinedBehaviorSanitizer.
  * Small problems of every shape class (decode, prefill, GQA, bf16, W >= n, k = 0, k > |R_i|,
  * n = 1), row subsets, the restricted and full forms, and argument errors. Exit status 0 when
  * every call returned what it should and the outputs are finite. */
@@ -108,6 +108,6 @@ int main(void) {
         fprintf(stderr, "%d checks failed\n", failures);
         return 1;
     }
-    printf("oracle driver: all checks passed\n");
+    printf("oracle exercise: all checks passed\n");
     return 0;
 }

@@ -1,14 +1,14 @@
 """Host-only AddressSanitizer and UndefinedBehaviorSanitizer runs (no GPU needed):
 
-- the CPU oracle (plain C), driven by tests/sanitize/oracle_driver.c over every shape class and
+- the CPU oracle (plain C), exercised by tests/sanitize/oracle_exercise.c over every shape class and
   its argument errors;
 - the C ABI's host side (validation, planning, workspace sizes: csrc/capi.hip compiled with the
   sanitizers on its host pass only; the device code and the other objects are the library's
-  own), driven by tests/sanitize/capi_driver.cpp: valid shapes of every path, a pseudo-random
+  own), exercised by tests/sanitize/capi_exercise.cpp: valid shapes of every path, a pseudo-random
   sweep of 200,000 parameter sets with sizes up to 2^40, and every entry point's argument and
   workspace errors, which return before any HIP call.
 
-A sanitizer report makes the driver exit non-zero (no recovery) and fails the test.
+A sanitizer report makes the program exit non-zero (no recovery) and fails the test.
 """
 import os
 import shutil
@@ -36,10 +36,10 @@ def _run(exe):
 def test_oracle_under_asan_ubsan(tmp_path):
     if shutil.which("gcc") is None:
         pytest.skip("gcc not found")
-    exe = str(tmp_path / "oracle_driver")
+    exe = str(tmp_path / "oracle_exercise")
     subprocess.check_call(["gcc", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer",
                            "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fopenmp",
-                           os.path.join(SAN, "oracle_driver.c"),
+                           os.path.join(SAN, "oracle_exercise.c"),
                            os.path.join(ROOT, "oracle", "condensate_oracle.c"), "-lm", "-o", exe])
     _run(exe)
 
@@ -52,7 +52,7 @@ def test_capi_host_side_under_asan_ubsan(tmp_path):
                     if f.endswith(".hip.o") and f != "capi.hip.o") if os.path.isdir(OBJDIR) else []
     if not others:
         pytest.skip("library objects not built (run __graft_entry__.build() first)")
-    capi_o, drv_o, exe = (str(tmp_path / n) for n in ("capi.o", "driver.o", "capi_driver"))
+    capi_o, ex_o, exe = (str(tmp_path / n) for n in ("capi.o", "exercise.o", "capi_exercise"))
     # Sanitizers on the host pass only: each -fsanitize flag behind its own -Xarch_host.
     host_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
@@ -63,8 +63,8 @@ def test_capi_host_side_under_asan_ubsan(tmp_path):
                    check=True, capture_output=True, text=True)
     subprocess.check_call([clangxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
                            "-fno-sanitize-recover=all", "-I", os.path.join(ROOT, "include"),
-                           "-c", os.path.join(SAN, "capi_driver.cpp"), "-o", drv_o])
-    subprocess.check_call([clangxx, "-fsanitize=address,undefined", "-o", exe, drv_o, capi_o, *others,
+                           "-c", os.path.join(SAN, "capi_exercise.cpp"), "-o", ex_o])
+    subprocess.check_call([clangxx, "-fsanitize=address,undefined", "-o", exe, ex_o, capi_o, *others,
                            "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
                            "-Wl,-rpath," + os.path.join(ROCM, "lib")])
     _run(exe)
