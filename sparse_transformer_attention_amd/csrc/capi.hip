@@ -161,6 +161,7 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
     P.mfma = false;
     P.seg = 1;
     P.win_offset = 0;
+    P.win_chunks = 0;
     P.zmass_offset = 0;
     // Many bf16 query vectors per KV head: the MFMA passes (bound, then candidate lists in the
     // segment layout of the chunked path: 4 segments of kMfmaSeg keys per query). They address
@@ -202,6 +203,11 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
             P.summ_offset = 0;
             P.scratch_offset = up(P.summ_offset + rq * 2 * sizeof(uint4));
             P.ws_bytes = P.scratch_offset + (size_t)P.units * P.G * (size_t)P.rstride * sizeof(uint32_t);
+            if (P.W >= ca::kDecodeWinSplit) {
+                P.win_chunks = (int)((P.W + 1 + ca::kWinChunkRows - 1) / ca::kWinChunkRows);
+                P.win_offset = up(P.ws_bytes);
+                P.ws_bytes = P.win_offset + (size_t)P.nqv * P.win_chunks * (size_t)(P.d + 2) * sizeof(float);
+            }
             return CA_OK;
         }
     }
@@ -261,7 +267,7 @@ int run_path(const ca::Plan &pl, const void *q, const void *k, const void *v, in
         // selection, set assembly and attend.
         {
             ProfScope pd(K_DSTREAM, s);
-            e = ca::launch_decode_stream(pl, q, k, ws, mass != nullptr, s);
+            e = ca::launch_decode_stream(pl, q, k, v, ws, mass != nullptr, out != nullptr, s);
             pd.done();
             if (e != hipSuccess) return hip_fail(e, "decode_stream launch");
         }

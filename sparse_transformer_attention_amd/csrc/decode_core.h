@@ -42,6 +42,8 @@ struct DecodeArgs {
     int32_t *out_idx;   // [nqv][cap]
     float *out;         // [nqv][D] (null: select only)
     float *mass;        // [nqv][4] (null: no diagnostic)
+    float *win;         // [nqv][nch][D + 2] anchor-and-window partials (decode_window), or null
+    int nch;            // chunks of kWinChunkRows rows per query vector (win only)
 };
 
 template <int N>
@@ -163,6 +165,8 @@ inline DecodeArgs decode_args(const Plan &pl, void *ws, int32_t *out_idx, float 
     a.out_idx = out_idx;
     a.out = out;
     a.mass = mass;
+    a.nch = pl.win_chunks;
+    a.win = pl.win_chunks > 0 ? reinterpret_cast<float *>(w + pl.win_offset) : nullptr;
     return a;
 }
 

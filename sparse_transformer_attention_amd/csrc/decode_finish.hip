@@ -249,11 +249,37 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
     const int wstep = NWW * AS::RPW;
     const int wv = wave - 1;
     RowSlices<D, T, UW> rs;
-    if (ATTEND && wave > 0) load_rows<D, T, UW>(rs, kb, vb, row_at, wn, wv * AS::RPW, wstep);
+    // Long windows come as decode_window's chunk partials (a.win): each of wavefronts 1..7
+    // merges every 7th of them.
+    const bool pre_win = a.win != nullptr;
+    if (ATTEND && wave > 0 && !pre_win) load_rows<D, T, UW>(rs, kb, vb, row_at, wn, wv * AS::RPW, wstep);
     bool win_done = !ATTEND;
     auto window_partial = [&]() {
         if constexpr (ATTEND) {
-            if (wave > 0) {
+            if (wave > 0 && pre_win) {
+                constexpr int EW = D / 64;  // elements per lane
+                float m = -INFINITY, l = 0.f, acc[EW];
+#pragma unroll
+                for (int e = 0; e < EW; ++e) acc[e] = 0.f;
+                for (int c = wv; c < a.nch; c += NWW) {
+                    const float *src = a.win + ((size_t)qi.qv * a.nch + c) * (D + 2);
+                    const float pm = src[0], pl = src[1];
+                    if (pm == -INFINITY) continue;  // (uniform: an empty chunk)
+                    const float mn = fmaxf(m, pm);
+                    const float f0 = m == -INFINITY ? 0.f : exp2f((m - mn) * a.scale_log2e);
+                    const float f1 = exp2f((pm - mn) * a.scale_log2e);
+                    l = l * f0 + pl * f1;
+#pragma unroll
+                    for (int e = 0; e < EW; ++e) acc[e] = acc[e] * f0 + src[2 + lane + 64 * e] * f1;
+                    m = mn;
+                }
+#pragma unroll
+                for (int e = 0; e < EW; ++e) sh.part.acc[wv][lane + 64 * e] = acc[e];
+                if (lane == 0) {
+                    sh.part.m[wv] = m;
+                    sh.part.l[wv] = l;
+                }
+            } else if (wave > 0) {
                 SlotState<D, T> st;
                 auto use = [&](int c) { return c < wn; };
                 accumulate_rows<D, T, UW>(st, rs, qs, use, wv * AS::RPW, wstep, a.scale_log2e);

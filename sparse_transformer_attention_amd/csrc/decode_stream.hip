@@ -5,20 +5,89 @@
 // block's four best rows as (key, offset), ties to the smaller offset, and X, the largest key of
 // its other rows; with the mass diagnostic also the block's largest score m_b and the sum of
 // exp2((s - m_b) * scale) over its candidate rows.
+#include "attend_core.h"
 #include "decode_core.h"
 
 namespace ca {
 namespace dec {
 namespace {
 
+// ---- long windows: anchor-and-window partials in the first workgroups ------------------------
+// Workgroup b (< units * G * nch): chunk c = b % nch of query t = (b / nch) / units of unit
+// (b / nch) % units, entries [c * kWinChunkRows, (c + 1) * kWinChunkRows) of the query's
+// anchor-and-window list ({0} if the window does not reach it, then i - W + 1 .. i). Its eight
+// wavefronts take their share (wave_partial) and the merged partial (m, l, acc[D],
+// unnormalised) goes to a.win. They stream with the key rows instead of after them.
+template <typename T, int D, int G>
+__device__ __forceinline__ void window_chunk(const T *__restrict__ q, const T *__restrict__ k,
+                                             const T *__restrict__ v, const DecodeArgs &a, uint32_t blk,
+                                             SoftmaxPartials<D, kWaves> &part) {
+    using AS = AttendShape<D, T>;
+    constexpr int UWIN = kWinChunkRows / (kWaves * AS::RPW) < 8 ? kWinChunkRows / (kWaves * AS::RPW) : 8;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t c = blk % (uint32_t)a.nch, b = blk / (uint32_t)a.nch;
+    const int t = (int)(b / a.units);
+    const uint32_t uu = b - (uint32_t)t * a.units;
+    const uint32_t ng = (uint32_t)a.groups;
+    const uint32_t bk = uu / ng, grp = uu - bk * ng;
+    const QInfo qi = query_info<G>(a, bk, grp, t);
+    if (!qi.valid) return;  // (uniform: the whole workgroup)
+    const size_t kv0 = (size_t)bk * (size_t)a.n * D;
+    const T *kb = k + kv0, *vb = v + kv0;
+    const int wn = qi.base + qi.wcount;
+    const int c0 = (int)c * kWinChunkRows;
+    const int cnt = wn - c0 < kWinChunkRows ? wn - c0 : kWinChunkRows;  // (may be <= 0)
+    const uint4 qs = reinterpret_cast<const uint4 *>(q + (size_t)qi.qv * D)[lane % AS::LPR];
+    auto row_at = [&](int e) -> size_t {
+        const int f = c0 + e;
+        return f < qi.base ? 0 : (size_t)(qi.wlo - qi.base + f);
+    };
+    if (cnt > 0) {
+        wave_partial<D, T, UWIN>(qs, kb, vb, row_at, cnt, wave, kWaves, a.scale_log2e, part, wave);
+    } else {
+        for (int e = lane; e < D; e += 64) part.acc[wave][e] = 0.f;
+        if (lane == 0) { part.m[wave] = -INFINITY; part.l[wave] = 0.f; }
+    }
+    __syncthreads();
+    float *dst = a.win + ((size_t)qi.qv * a.nch + c) * (D + 2);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, part.m[w]);
+    float f[kWaves], l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        f[w] = part.m[w] == -INFINITY ? 0.f : exp2f((part.m[w] - mx) * a.scale_log2e);
+        l += part.l[w] * f[w];
+    }
+    for (int e = tid; e < D; e += kNT) {
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) o = fmaf(part.acc[w][e], f[w], o);
+        dst[2 + e] = o;
+    }
+    if (tid == 0) {
+        dst[0] = mx;
+        dst[1] = l;
+    }
+}
+
 // ---- decode_stream: keys of two blocks into LDS, then the block records ---------------------
 template <typename T, int D, int G, bool MASS>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 5 : 4))) void decode_stream_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, DecodeArgs a) {
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, DecodeArgs a) {
     __shared__ uint32_t kst[G][kBW * kRows];  // keys of the workgroup's rows, per query
-    // Workgroup s: unit s % units, its part s / units.
-    const uint32_t part = blockIdx.x / a.units;
-    const uint32_t uu = blockIdx.x - part * a.units;
+    // Long windows: the first units * G * nch workgroups make the anchor-and-window partials.
+    const uint32_t nwin = a.win ? a.units * (uint32_t)G * (uint32_t)a.nch : 0u;
+    if (blockIdx.x < nwin) {
+        __shared__ SoftmaxPartials<D, kWaves> wpart;
+        window_chunk<T, D, G>(q, k, v, a, blockIdx.x, wpart);
+        return;
+    }
+    // Workgroup nwin + s: unit s % units, its part s / units.
+    const uint32_t sblk = blockIdx.x - nwin;
+    const uint32_t part = sblk / a.units;
+    const uint32_t uu = sblk - part * a.units;
     using S = StreamShape<T, D>;
     constexpr int LPR = S::LPR, RPG = S::RPG, P = S::P, NG = S::NG, U = S::U, TR = S::TR;
     constexpr int WROWS = kBW * kRows;
@@ -153,17 +222,19 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
 }  // namespace
 }  // namespace dec
 
-hipError_t launch_decode_stream(const Plan &pl, const void *q, const void *k, void *ws, bool mass,
-                                hipStream_t s) {
+hipError_t launch_decode_stream(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
+                                bool mass, bool attend, hipStream_t s) {
     using namespace dec;
-    const DecodeArgs a = decode_args(pl, ws, nullptr, nullptr, nullptr);
+    DecodeArgs a = decode_args(pl, ws, nullptr, nullptr, nullptr);
+    if (!attend) a.win = nullptr;  // (no output: the window partials are not needed)
     const uint32_t wpb = (uint32_t)((pl.nblk + kBW - 1) / kBW);
-    const dim3 grid((unsigned)((uint64_t)pl.units * wpb)), block(kNT);
+    const uint64_t nwin = a.win ? (uint64_t)pl.units * pl.G * pl.win_chunks : 0;
+    const dim3 grid((unsigned)((uint64_t)pl.units * wpb + nwin)), block(kNT);
 #define CA_DS(T, D, G)                                                                                   \
     do {                                                                                                 \
-        const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k);                        \
-        if (mass) hipLaunchKernelGGL((decode_stream_kernel<T, D, G, true>), grid, block, 0, s, qt, kt, a); \
-        else hipLaunchKernelGGL((decode_stream_kernel<T, D, G, false>), grid, block, 0, s, qt, kt, a);   \
+        const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v); \
+        if (mass) hipLaunchKernelGGL((decode_stream_kernel<T, D, G, true>), grid, block, 0, s, qt, kt, vt, a); \
+        else hipLaunchKernelGGL((decode_stream_kernel<T, D, G, false>), grid, block, 0, s, qt, kt, vt, a);   \
     } while (0)
 #define CA_DS_G(T, D)                                   \
     do {                                                \
