@@ -37,6 +37,9 @@ CASES = {
     "f32_d128_multi_query": W_(dtype="f32", heads=4, kv_heads=1, n=2500, nq=3, W=33, topk=17),
     "bf16_d64_gqa8": W_(d=64, heads=16, kv_heads=2, n=2100, nq=5, W=50, topk=100),
     "f32_W1_prefill": W_(dtype="f32", d=64, heads=1, kv_heads=1, n=700, nq=700, W=1, topk=5),
+    # W >= 512: the window part comes from the chunk partials of extra stream workgroups.
+    "long_window_bf16": W_(heads=8, kv_heads=2, n=5000, W=600, topk=32),
+    "long_window_f32_d64": W_(dtype="f32", d=64, heads=2, kv_heads=1, n=900, nq=600, W=512, topk=16),
 }
 
 
