@@ -182,6 +182,49 @@ __device__ __forceinline__ void wave_partial(const uint4 &qs, const T *__restric
     store_wave_partial<D, T>(st, scale_log2e, out, p);
 }
 
+// As wave_partial, with the scores given (score_at(c), the same for every lane of a row slot)
+// instead of computed: only the V rows are read.
+template <int D, typename T, int U, int NP, typename RowAt, typename ScoreAt>
+__device__ __forceinline__ void wave_partial_scored(const T *__restrict__ vbase, RowAt row_at,
+                                                    ScoreAt score_at, int count, int wv, int nw,
+                                                    float scale_log2e, SoftmaxPartials<D, NP> &out, int p) {
+    using S = AttendShape<D, T>;
+    SlotState<D, T> st;
+    const int step = nw * S::RPW;
+    const int lane = threadIdx.x & 63, slot = lane / S::LPR, cs = lane % S::LPR;
+    for (int c0 = wv * S::RPW; c0 < count; c0 += U * step) {
+        uint4 vr[U];
+        float s[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * step + slot;
+            ok[u] = c < count;
+            const int cc = ok[u] ? c : count - 1;
+            vr[u] = reinterpret_cast<const uint4 *>(vbase + row_at(cc) * D)[cs];
+            s[u] = score_at(cc);
+        }
+        float mr = st.m;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (ok[u]) mr = fmaxf(mr, s[u]);
+        const float f = st.m == -INFINITY ? 0.f : exp2f((st.m - mr) * scale_log2e);
+        st.l *= f;
+#pragma unroll
+        for (int e = 0; e < S::EPL; ++e) st.acc[e] *= f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (ok[u]) {
+                const float w = exp2f((s[u] - mr) * scale_log2e);
+                st.l += w;
+                accumulate16(st.acc, vr[u], w, T());
+            }
+        }
+        st.m = mr;
+    }
+    store_wave_partial<D, T>(st, scale_log2e, out, p);
+}
+
 // out[0..D) from partials p0..p1-1 (at most 64 of them, all written, at least one row in all),
 // combined in index order: wavefront 0 turns their m[p], l[p] into normalised factors
 // f[p] = exp2((m[p] - M) * scale_log2e) / L, then each column sums f[p] acc[p][t]. Called by all

@@ -55,7 +55,8 @@ __device__ __forceinline__ int64_t block_qv() {
 constexpr int kRankSelectMax = 256;
 static_assert(2 * kRankSelectMax <= kGather && 2 * 128 <= kGatherFor<128>, "rank select room");
 template <int NT>
-__device__ __forceinline__ void select_by_rank(int n, int kp, uint64_t *gathered, int32_t *js) {
+__device__ __forceinline__ void select_by_rank(int n, int kp, uint64_t *gathered, int32_t *js,
+                                               uint32_t *jk = nullptr) {
     const int tid = threadIdx.x;
     int lg = 4;
     while (lg > 0 && (n << lg) > NT) --lg;
@@ -82,19 +83,23 @@ __device__ __forceinline__ void select_by_rank(int n, int kp, uint64_t *gathered
         }
     }
     for (int off = 1; off < S; off <<= 1) rank += __shfl_xor(rank, off);
-    if (chosen && sl == 0) js[rank] = pos;
+    if (chosen && sl == 0) {
+        js[rank] = pos;
+        if (jk) jk[rank] = (uint32_t)(x >> 32);  // its score key, in the same place
+    }
     lds_barrier();
 }
 
 // Candidates from the segments of score_topk or of the MFMA passes (the first cnt[w] keys of
 // each segment w of lists[w][0..seg)), gathered into LDS by wavefront 0 while the other wavefronts run
-// overlap(); then the exact top-kp.
+// overlap(); then the exact top-kp: positions to js[0..kp), ascending, and their score keys to
+// jk[0..kp) (room for 2*kp).
 template <int NT, typename Overlap>
 __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt,
                                                 const uint64_t *__restrict__ lists, int wpu,
                                                 int topk, int kp, int32_t *js, uint64_t *sel,
                                                 uint64_t *gathered, SelectShared<NT> &sh,
-                                                Overlap overlap) {
+                                                Overlap overlap, uint32_t *jk) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (wave == 0) {
         // Every slot of every segment, four per lane in flight with their segments' lengths,
@@ -129,7 +134,7 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
     const int n = sh.sel_count;
     __syncthreads();
     if (n >= kp && n <= kRankSelectMax && n <= NT) {
-        select_by_rank<NT>(n, kp, gathered, js);
+        select_by_rank<NT>(n, kp, gathered, js, jk);
         return;
     }
     auto key_at = [&](int64_t f) -> uint64_t {
@@ -137,7 +142,7 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
         const int e = (int)(f - (int64_t)w * topk);
         return e < (int)cnt[w] ? lists[f] : 0ull;
     };
-    select_exact<NT>(n, (int64_t)wpu * topk, key_at, kp, js, sel, gathered, sh);
+    select_exact<NT>(n, (int64_t)wpu * topk, key_at, kp, js, sel, gathered, sh, jk);
 }
 
 // Rows per lane in flight in the attend phase (rows past the set's end are loaded as clamped
@@ -160,6 +165,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     __shared__ SoftmaxPartials<D, ATTEND ? 2 * NW : 1> part;
     int32_t *js = fsm;
     uint64_t *sel = reinterpret_cast<uint64_t *>(fsm + 2 * a.cap);
+    uint32_t *jk = reinterpret_cast<uint32_t *>(sel + a.topk);  // score keys of the top-k' (2 topk)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     if (kp > 0) {
         auto overlap = [&]() { window_part(wave - 1, NW - 1); };
         select_segments<NT>(a.cnt + qv * a.wpu, a.lists + qv * a.wpu * a.seg, a.wpu, a.seg,
-                            kp, js + base, sel, gathered, ssh, overlap);
+                            kp, js + base, sel, gathered, ssh, overlap, jk);
     } else {
         window_part(wave, NW);
     }
@@ -232,8 +238,11 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
         if (kp > 0) {
             const int32_t *top = js + base;
             auto row_at = [&](int c) -> size_t { return (size_t)(uint32_t)top[c]; };
+            // The selected rows' scores are those their candidate keys were ranked by (the
+            // same fp32 products), so only their V rows are read.
+            auto score_at = [&](int c) { return key_score(jk[c]); };
             if (wave < top_waves)
-                wave_partial<D, T, kTopU>(qs, kb, vb, row_at, kp, wave, top_waves, a.scale_log2e, part, NW + wave);
+                wave_partial_scored<D, T, kTopU>(vb, row_at, score_at, kp, wave, top_waves, a.scale_log2e, part, NW + wave);
         }
         // (The index row's stores need not complete before the merge: LDS only.)
         lds_barrier();
@@ -370,7 +379,7 @@ hipError_t launch_finish_t(const Plan &pl, const void *ws, const void *q, const 
                            const void *v, int32_t *out_idx, float *out, hipStream_t s, float *mass) {
     FinishArgs a = finish_args(pl, ws);
     a.mass = mass;
-    const size_t shmem = (size_t)pl.cap * (2 * sizeof(int32_t)) + (size_t)pl.topk * sizeof(uint64_t);
+    const size_t shmem = (size_t)pl.cap * (2 * sizeof(int32_t)) + (size_t)pl.topk * (sizeof(uint64_t) + 2 * sizeof(uint32_t));
     const dim3 grid = qv_grid(pl.nqv);
     const T *qt = static_cast<const T *>(q), *kt = static_cast<const T *>(k), *vt = static_cast<const T *>(v);
     const size_t fixed1024 = kGather * sizeof(uint64_t) + sizeof(SelectShared<1024>) + sizeof(SoftmaxPartials<D, 32>);

@@ -27,13 +27,14 @@ struct SelectShared {
 
 // Exact top-kp of one query's candidates, given as n keys gathered in LDS (gathered[0..n) when
 // n <= kGatherFor<NT>) and as key_at(f) over f in [0, slots) (0 = no candidate): the distinct,
-// non-zero ranking keys. The kp positions go to js[0..kp), ascending (js needs room for 2*kp).
+// non-zero ranking keys. The kp positions go to js[0..kp), ascending (js needs room for 2*kp),
+// and with jk their score keys to jk[0..kp) in the same order (jk needs room for 2*kp too).
 // Up to kGatherFor<NT> candidates are selected by wavefront 0 alone with the keys in registers; more
 // by the whole workgroup, calling key_at on every radix pass.
 template <int NT, typename KeyAt>
 __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at, int kp, int32_t *js,
                                              uint64_t *sel, const uint64_t *gathered,
-                                             SelectShared<NT> &sh) {
+                                             SelectShared<NT> &sh, uint32_t *jk = nullptr) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (n <= kGatherFor<NT>) {
@@ -47,7 +48,10 @@ __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at,
             (void)wave_keep_top_u64(kk, kp, &sh.hist[0][0], sel);
         }
         __syncthreads();
-        for (int t = tid; t < kp; t += NT) js[t] = rank_key_pos(sel[t]);
+        for (int t = tid; t < kp; t += NT) {
+            js[t] = rank_key_pos(sel[t]);
+            if (jk) jk[t] = (uint32_t)(sel[t] >> 32);
+        }
     } else if constexpr (NT >= 256) {
         // (128-thread workgroups select from at most 256 keys: never here.)
         uint64_t kmax = 0ull, kmin = ~0ull;
@@ -119,7 +123,10 @@ __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at,
             const uint64_t x = key_at(f);
             if (x && (x & mask) >= prefix) {
                 const int pos = atomicAdd(&sh.sel_count, 1);
-                if (pos < kp) js[pos] = rank_key_pos(x);
+                if (pos < kp) {
+                    js[pos] = rank_key_pos(x);
+                    if (jk) jk[pos] = (uint32_t)(x >> 32);
+                }
             }
         }
     }
@@ -134,10 +141,14 @@ __device__ __forceinline__ void select_exact(int n, int64_t slots, KeyAt key_at,
 #pragma unroll 8
             for (int u = 0; u < kp; ++u) rank += js[u] < j;
             js[kp + rank] = j;
+            if (jk) jk[kp + rank] = jk[t];
         }
     }
     __syncthreads();
-    for (int t = tid; t < kp; t += NT) js[t] = js[kp + t];
+    for (int t = tid; t < kp; t += NT) {
+        js[t] = js[kp + t];
+        if (jk) jk[t] = jk[kp + t];
+    }
     __syncthreads();
 }
 
