@@ -50,9 +50,8 @@ struct Plan {
                           // (reference score, sum) over R_i
     int64_t rstride;
     int nblk;
-    // Decode path with a long window: the anchor-and-window rows of a query in chunks of
-    // kWinChunkRows, one extra decode_stream workgroup each; partials [nqv][win_chunks][d + 2]
-    // at win_offset. 0: decode_finish attends over those rows itself.
+    // Decode path: the anchor-and-window rows of a query in chunks of kWinChunkRows, one extra
+    // decode_stream workgroup each; partials [nqv][win_chunks][d + 2] at win_offset.
     int win_chunks;
     size_t summ_offset, scratch_offset;
 };
@@ -74,19 +73,17 @@ hipError_t launch_gather_softmax_av(const Plan &pl, const void *q, const void *k
                                     const int32_t *idx, float *out, hipStream_t s);
 size_t topk_lds_bytes(const Plan &pl);
 // Decode path, first kernel: every key row scored once; per block of 256 rows and query vector a
-// record of its best rows (mass: also the block's softmax sums). With win_chunks > 0 and attend,
-// extra workgroups first make the anchor-and-window partials.
+// record of its best rows (mass: also the block's softmax sums). With attend, extra workgroups
+// at the end of the grid make the anchor-and-window partials.
 hipError_t launch_decode_stream(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
                                 bool mass, bool attend, hipStream_t s);
 // Decode path, second kernel: per query vector the exact top-k' from the records, out_idx and
 // (out != nullptr) the restricted softmax times V (mass != nullptr: also the mass diagnostic).
 hipError_t launch_decode_finish(const Plan &pl, const void *q, const void *k, const void *v, void *ws,
                                 int32_t *out_idx, float *out, float *mass, hipStream_t s);
-// Anchor-and-window rows per window workgroup of decode_stream, and the window length from
-// which the decode path uses them (shorter windows: decode_finish reads those rows while it
-// selects).
-constexpr int kWinChunkRows = 256;
-constexpr int kDecodeWinSplit = 512;
+// Anchor-and-window rows per window workgroup of decode_stream. Small chunks run in the
+// stream's tail, where CUs fall idle; decode_finish then only merges their partials.
+constexpr int kWinChunkRows = 64;
 // Query blocks of 16 per wavefront of the two MFMA passes (16 * QB * kMfmaWaves query vectors per
 // workgroup).
 // Bound pass, per d. Measured: 3 at d = 64 (more products per operand read, 2 wavefronts per

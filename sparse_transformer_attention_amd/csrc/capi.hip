@@ -188,8 +188,12 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
         const double kb = (double)P.units * (double)(nblk * kStreamBlockRows) * P.G * 4.0;
         // (Index math of the decode kernels in 32 bits.)
         const int64_t wpb = (nblk + 1) / 2;
+        // decode_stream's grid: the key workgroups, then one per query vector and window chunk;
+        // workgroups times 512 threads stay below 2^32.
+        const int64_t nch = (P.W + 1 + ca::kWinChunkRows - 1) / ca::kWinChunkRows;
+        const int64_t stream_wg = P.units * wpb + P.units * P.G * nch;
         if (kb <= kStreamKeysMax && P.units * nblk < ((int64_t)1 << 31) && nvec < ((int64_t)1 << 31) &&
-            P.topk <= kDecodeMaxTopk && P.units * wpb < ((int64_t)1 << 31) &&
+            P.topk <= kDecodeMaxTopk && stream_wg < ((int64_t)1 << 23) &&
             P.units * P.G < ((int64_t)1 << 31)) {
             P.stream = true;
             P.nblk = (int)nblk;
@@ -203,11 +207,9 @@ int make_plan(const ca_params *p, ca::Plan *pl) {
             P.summ_offset = 0;
             P.scratch_offset = up(P.summ_offset + rq * 2 * sizeof(uint4));
             P.ws_bytes = P.scratch_offset + (size_t)P.units * P.G * (size_t)P.rstride * sizeof(uint32_t);
-            if (P.W >= ca::kDecodeWinSplit) {
-                P.win_chunks = (int)((P.W + 1 + ca::kWinChunkRows - 1) / ca::kWinChunkRows);
-                P.win_offset = up(P.ws_bytes);
-                P.ws_bytes = P.win_offset + (size_t)P.nqv * P.win_chunks * (size_t)(P.d + 2) * sizeof(float);
-            }
+            P.win_chunks = (int)nch;
+            P.win_offset = up(P.ws_bytes);
+            P.ws_bytes = P.win_offset + (size_t)P.nqv * P.win_chunks * (size_t)(P.d + 2) * sizeof(float);
             return CA_OK;
         }
     }

@@ -4,16 +4,18 @@
 // position; section 2.3, the softmax restricted to C_i times V; section 3.2.2, the mass outside
 // C_i).
 //
-// The records of decode_stream and the anchor and window rows are requested first. A bound T0
-// comes from the blocks' best keys (k' blocks, so k' distinct rows, reach it: no row below it
-// can be in the top k'). The record rows whose ranking key (score_key << 32) | ~position reaches
-// the bound are gathered in a fixed order and cut to their exact top k' (one wavefront). A block
-// whose X reaches the k'-th key has rows beyond its record that may rank: those are scored again
-// (row_key, the same bits) and the cut repeated. The V rows of the top k' are requested while
-// their places in out_idx are counted; the anchor-and-window partial and the top-k partials
-// (weights exp2((s - m) * scale), s read back from the keys) merge into the output. Too many
-// candidates or such blocks (dense clusters of high scores, exact ties) switch the query to an
-// exact fallback: all its candidate rows scored into scratch keys and a workgroup radix select.
+// The records of decode_stream and the anchor-and-window chunk partials (made by decode_stream's
+// window workgroups) are requested first. A bound T0 comes from the blocks' best keys (k' blocks,
+// so k' distinct rows, reach it: no row below it can be in the top k'). The record rows whose
+// ranking key (score_key << 32) | ~position reaches the bound are gathered in a fixed order; their
+// V rows are requested at once, and the list is cut to its exact top k' by counting each key's
+// rank on all wavefronts. A block whose X reaches the k'-th key has rows beyond its record that
+// may rank: those are scored again (row_key, the same bits) and the cut repeated (their V rows
+// are then requested after it). The top k''s places in out_idx are counted while the V rows
+// load; the anchor-and-window partial and the top-k partials (weights exp2((s - m) * scale), s
+// read back from the keys) merge into the output. Too many candidates or such blocks (dense
+// clusters of high scores, exact ties) switch the query to an exact fallback: all its candidate
+// rows scored into scratch keys and a workgroup radix select.
 #include "attend_core.h"
 #include "decode_core.h"
 #include "merge_core.h"
@@ -27,6 +29,8 @@ constexpr int kCand = 1024;        // candidate keys per query held in LDS
 constexpr int kDef = 64;           // blocks whose X reaches the threshold, held in LDS
 constexpr int kResc = 8;           // such blocks scored again on the common path
 constexpr int kSelMax = 256;       // largest k' of the common path (larger: the fallback)
+constexpr int kRankMax = 256;      // candidate lists cut by rank counting (longer: one wavefront)
+static_assert(kSelMax <= kRankMax && 2 * kRankMax <= kCand, "rank_cut's output room");
 
 // Keeps the top kp of the n distinct non-zero ranking keys list[0..n) (n <= 64 E) in
 // list[0..kp) and returns a value that exactly those reach. One wavefront.
@@ -58,7 +62,7 @@ __device__ __forceinline__ uint64_t keep_top(uint64_t *list, int n, int kp) {
 // ---- decode_finish ---------------------------------------------------------------------------
 template <int D>
 struct FinShared {
-    uint64_t cand[kCand];  // candidate ranking keys; after each cut the top k'
+    alignas(16) uint64_t cand[kCand];  // candidate ranking keys; after each cut the top k'
     union {
         uint32_t bmax[kNT];  // best keys of the round's blocks (threshold of the single wavefront)
         struct {
@@ -80,11 +84,13 @@ struct FinShared {
 
 // Appends, in a fixed order (wavefront, then e, then lane), the keys key[e] with ok[e] of every
 // wavefront after list[0..sh.n), and the blocks with okd (entry dk, offsets doff) after
-// def[0..sh.ndef). Called by all threads; two workgroup barriers. Entries past the capacities
-// are dropped (the counts still grow, so the caller sees the overflow).
+// def[0..sh.ndef). Called by all threads; two workgroup barriers, after which the entries are
+// visible; returns the new list length (sh.n and sh.ndef are written after the second barrier).
+// Entries past the capacities are dropped (the counts still grow, so the caller sees the
+// overflow).
 template <int D, int E>
-__device__ __forceinline__ void append_all(FinShared<D> &sh, const bool (&ok)[E], const uint64_t (&key)[E],
-                                           bool okd, uint64_t dk, uint32_t doff) {
+__device__ __forceinline__ int append_all(FinShared<D> &sh, const bool (&ok)[E], const uint64_t (&key)[E],
+                                          bool okd, uint64_t dk, uint32_t doff) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     uint64_t bal[E];
@@ -127,6 +133,7 @@ __device__ __forceinline__ void append_all(FinShared<D> &sh, const bool (&ok)[E]
         sh.n = n_all;
         sh.ndef = d_all;
     }
+    return n_all;
 }
 
 // Keeps the top kp of the n distinct non-zero ranking keys list[0..n) (n <= 64 E, n > kp) in
@@ -183,6 +190,59 @@ __device__ __forceinline__ void cut_exact(FinShared<D> &sh, int kp) {
     }
 }
 
+// The number of keys list[0..n) (n <= kRankMax) that key beats under `beats`, summed over the 8
+// lanes of each group (every lane of the group gets it): lane `part` of a group reads keys
+// 16 i + 2 part and 16 i + 2 part + 1 (the group reads 128 contiguous bytes, four 16-byte reads
+// in flight per lane; reads past n stay inside the list's storage and are not counted).
+template <typename Beats>
+__device__ __forceinline__ uint32_t group8_count(const uint64_t *list, int n, Beats beats) {
+    const int part = threadIdx.x & 7;
+    uint32_t r = 0u;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        uint4 x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = *reinterpret_cast<const uint4 *>(list + j0 + 16 * e + 2 * part);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = j0 + 16 * e + 2 * part;
+            const uint64_t y0 = ((uint64_t)x[e].y << 32) | x[e].x, y1 = ((uint64_t)x[e].w << 32) | x[e].z;
+            r += (j < n && beats(y0)) ? 1u : 0u;
+            r += (j + 1 < n && beats(y1)) ? 1u : 0u;
+        }
+    }
+    r += dpp_u32<0xB1>(0u, r);   // lane ^ 1
+    r += dpp_u32<0x4E>(0u, r);   // lane ^ 2
+    r += dpp_u32<0x141>(0u, r);  // the mirrored lane of the group of 8: the other quad
+    return r;
+}
+
+// Exact top kp of the n distinct ranking keys sh.cand[0..n) (kp < n <= kRankMax), all threads:
+// each key's rank (the number of keys above it) is counted by a group of 8 lanes; the keys of
+// rank < kp go to sh.cand[0..kp) in descending order, and the threshold becomes the kp-th key.
+// On the way, sh.anyd[wave] says whether some thread's block key X (0: none) reaches the new
+// threshold's score key. Two barriers, on LDS traffic only (vector loads stay in flight).
+template <int D>
+__device__ __forceinline__ void rank_cut(FinShared<D> &sh, int n, int kp, uint32_t X) {
+    const int tid = threadIdx.x;
+    uint64_t *const top = sh.cand + (kCand - kRankMax);  // (past every read: n <= kRankMax)
+    for (int c0 = 0; c0 < n; c0 += kNT / 8) {
+        const int c = c0 + (tid >> 3);
+        const uint64_t key = c < n ? sh.cand[c] : ~0ull;
+        const uint32_t r = group8_count(sh.cand, n, [&](uint64_t y) { return y > key; });
+        if ((tid & 7) == 0 && c < n && r < (uint32_t)kp) top[r] = key;
+    }
+    lds_barrier();
+    const bool okd = X != 0u && X >= (uint32_t)(top[kp - 1] >> 32);
+    const bool wany = __ballot(okd) != 0ull;
+    if ((tid & 63) == 0) sh.anyd[tid >> 6] = wany ? 1 : 0;
+    for (int c = tid; c < kp; c += kNT) sh.cand[c] = top[c];
+    if (tid == 0) {
+        sh.thr = top[kp - 1];
+        sh.n = kp;
+    }
+    lds_barrier();
+}
+
 // Deferred blocks whose X fell below the threshold's score key leave the list, in order (one
 // wavefront).
 template <int D>
@@ -210,7 +270,6 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
     static_assert(kDef <= 64 && kCand <= 64 * 16, "one wavefront holds the lists");
     using AS = AttendShape<D, T>;
     using S = StreamShape<T, D>;
-    constexpr int UW = 10;  // window rows per lane requested before the selection (10 * 28 >= 257)
     __shared__ FinShared<D> sh;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -228,40 +287,44 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
     const T *kb = k + kv0, *vb = v + kv0;
     int32_t *row = a.out_idx + (size_t)qi.qv * a.cap;
     const uint4 *R = a.rec + ((size_t)uu * G + t) * (size_t)a.nblk * 2;
-    // Requests first: the first round's records, then the first rows of the anchor and window.
+    // Requests first: the first round's records, then the first anchor-and-window chunk partial
+    // of each of wavefronts 1..kWaves-1 (made by decode_stream's window workgroups).
     uint4 ra = make_uint4(0, 0, 0, 0), rb = make_uint4(0, 0, 0, 0);
     if (tid < qi.nbq && kp > 0) {
         ra = R[2 * tid];
         rb = R[2 * tid + 1];
     }
-    const uint4 qs = reinterpret_cast<const uint4 *>(q + (size_t)qi.qv * D)[lane % AS::LPR];
-    // Mass diagnostic: row 0's key, for its score at the end (the last wavefront, which the
-    // output merge leaves free).
-    uint4 k0 = make_uint4(0, 0, 0, 0);
-    if constexpr (MASS) {
-        if (wave == kWaves - 1) k0 = reinterpret_cast<const uint4 *>(kb)[lane % AS::LPR];
-    }
-    const int wn = qi.base + qi.wcount;  // anchor and window rows
-    auto row_at = [&](int c) -> size_t { return c < qi.base ? 0 : (size_t)(qi.wlo - qi.base + c); };
-    // Anchor and window on wavefronts 1..kWaves-1 (partials 0..kWaves-2), computed while
-    // wavefront 0 makes the first round's cut.
     constexpr int NWW = kWaves - 1;
-    const int wstep = NWW * AS::RPW;
+    constexpr int EW = D / 64;  // window partial elements per lane
     const int wv = wave - 1;
-    RowSlices<D, T, UW> rs;
-    // Long windows come as decode_window's chunk partials (a.win): each of wavefronts 1..7
-    // merges every 7th of them.
-    const bool pre_win = a.win != nullptr;
-    if (ATTEND && wave > 0 && !pre_win) load_rows<D, T, UW>(rs, kb, vb, row_at, wn, wv * AS::RPW, wstep);
-    bool win_done = !ATTEND;
-    auto window_partial = [&]() {
-        if constexpr (ATTEND) {
-            if (wave > 0 && pre_win) {
-                constexpr int EW = D / 64;  // elements per lane
-                float m = -INFINITY, l = 0.f, acc[EW];
+    float wm = -INFINITY, wl = 0.f, wacc[EW];
 #pragma unroll
-                for (int e = 0; e < EW; ++e) acc[e] = 0.f;
-                for (int c = wv; c < a.nch; c += NWW) {
+    for (int e = 0; e < EW; ++e) wacc[e] = 0.f;
+    if (ATTEND && wave > 0 && wv < a.nch) {
+        const float *src = a.win + ((size_t)qi.qv * a.nch + wv) * (D + 2);
+        wm = src[0];
+        wl = src[1];
+#pragma unroll
+        for (int e = 0; e < EW; ++e) wacc[e] = src[2 + lane + 64 * e];
+    }
+    // Mass diagnostic: the query slice and row 0's key, for row 0's score at the end (the last
+    // wavefront, which the output merge leaves free).
+    uint4 qs = make_uint4(0, 0, 0, 0), k0 = make_uint4(0, 0, 0, 0);
+    if constexpr (MASS) {
+        if (wave == kWaves - 1) {
+            qs = reinterpret_cast<const uint4 *>(q + (size_t)qi.qv * D)[lane % AS::LPR];
+            k0 = reinterpret_cast<const uint4 *>(kb)[lane % AS::LPR];
+        }
+    }
+    // Wavefront w >= 1 merges chunks w - 1, w - 1 + NWW, ... into partial w - 1 (the first one
+    // from the registers requested above).
+    auto window_merge = [&]() {
+        if constexpr (ATTEND) {
+            if (wave > 0) {
+                float m = wm, l = wl, acc[EW];
+#pragma unroll
+                for (int e = 0; e < EW; ++e) acc[e] = wacc[e];
+                for (int c = wv + NWW; c < a.nch; c += NWW) {
                     const float *src = a.win + ((size_t)qi.qv * a.nch + c) * (D + 2);
                     const float pm = src[0], pl = src[1];
                     if (pm == -INFINITY) continue;  // (uniform: an empty chunk)
@@ -279,18 +342,8 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
                     sh.part.m[wv] = m;
                     sh.part.l[wv] = l;
                 }
-            } else if (wave > 0) {
-                SlotState<D, T> st;
-                auto use = [&](int c) { return c < wn; };
-                accumulate_rows<D, T, UW>(st, rs, qs, use, wv * AS::RPW, wstep, a.scale_log2e);
-                for (int c0 = wv * AS::RPW + UW * wstep; c0 < wn; c0 += UW * wstep) {
-                    load_rows<D, T, UW>(rs, kb, vb, row_at, wn, c0, wstep);
-                    accumulate_rows<D, T, UW>(st, rs, qs, use, c0, wstep, a.scale_log2e);
-                }
-                store_wave_partial<D, T>(st, a.scale_log2e, sh.part, wv);
             }
         }
-        win_done = true;
     };
     if (tid == 0) {
         sh.n = 0;
@@ -303,6 +356,17 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
         if (e >= qi.base && e < qi.base + kp) continue;
         row[e] = e < qi.base ? 0 : (e < qi.base + kp + qi.wcount ? qi.wlo + (e - qi.base - kp) : -1);
     }
+    // V rows of the top k': lane slot `slot` of wavefront `wave` takes the rows
+    // c = wave * RPW + slot + u * step of a list. With one round of records and at most UT * step
+    // candidates, the candidates' V rows are requested before the cut (pv, with their keys pk)
+    // and the cut's threshold then picks the members among them.
+    constexpr int UT = 4;
+    const int cs = lane % AS::LPR, slot = lane / AS::LPR;
+    const int step = kWaves * AS::RPW;
+    const uint32_t last_row = (uint32_t)(a.n - 1);
+    uint4 pv[UT];
+    uint64_t pk[UT];
+    bool pre = false, resc = false;
     // Rounds of kNT blocks (one record per thread).
     float zm = -INFINITY, zl = 0.f;
     for (int r0 = 0; r0 < qi.nbq && kp > 0; r0 += kNT) {
@@ -320,6 +384,7 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
                 zm = mn;
             }
         }
+        int n;  // candidates after the append (uniform)
         // A bound from the round's best keys: with q = ceil(kp / 8), each wavefront's q-th
         // largest; their minimum is reached by q blocks of each wavefront, kp distinct rows in
         // all. A wavefront with fewer than q blocks leaves it to one wavefront searching all of
@@ -356,7 +421,7 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
             const uint64_t b0 = (uint64_t)t0 << 32;
             const uint64_t thr = b0 > sh.thr ? b0 : sh.thr;
             const uint32_t ks[4] = {ra.x, ra.y, ra.z, ra.w};
-            const uint32_t offs = rb.x, X = rb.y;
+            const uint32_t offs = rb.x;
             bool ok[4];
             uint64_t kk[4];
 #pragma unroll
@@ -364,39 +429,62 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
                 kk[e] = make_rank_key(ks[e], (uint32_t)blk * kRows + ((offs >> (8 * e)) & 255u));
                 ok[e] = has && ks[e] != 0u && kk[e] >= thr;
             }
-            append_all<D, 4>(sh, ok, kk, false, 0ull, 0u);
+            n = append_all<D, 4>(sh, ok, kk, false, 0ull, 0u);
             if (tid == 0) sh.thr = thr;
         }
-        __syncthreads();
-        if (wave == 0) {
-            if (sh.n > kCand) {
-                if (lane == 0) sh.flag = 1;
-            } else if (!sh.flag) {
+        if (ATTEND && r0 == 0 && qi.nbq <= kNT && n <= UT * step) {
+            pre = true;
+#pragma unroll
+            for (int u = 0; u < UT; ++u) {
+                const int c = wave * AS::RPW + slot + u * step;
+                pk[u] = c < n ? sh.cand[c] : 0ull;
+                uint32_t pos = c < n ? (uint32_t)rank_key_pos(pk[u]) : 0u;
+                pos = pos < last_row ? pos : last_row;
+                pv[u] = reinterpret_cast<const uint4 *>(vb + (size_t)pos * D)[cs];
+            }
+        }
+        // The cut. Rank counting (all wavefronts) also votes on the blocks to list below, so
+        // that its last barrier serves for both; deferred blocks of earlier rounds are filtered
+        // by wavefront 0 after it (and a barrier follows when there were any).
+        bool voted = false;
+        const uint32_t X = has ? rb.y : 0u;
+        if (n > kCand) {
+            if (tid == 0) sh.flag = 1;
+        } else if (!sh.flag) {
+            if (n > kp && n <= kRankMax) {
+                const bool had_def = sh.ndef > 0;  // (uniform)
+                rank_cut<D>(sh, n, kp, X);
+                voted = true;
+                if (had_def) {
+                    if (wave == 0) filter_deferred<D>(sh);
+                    lds_barrier();
+                }
+            } else if (wave == 0) {
                 cut_exact<D>(sh, kp);
                 wave_sync();
                 filter_deferred<D>(sh);
             }
-        } else if (!win_done) {
-            window_partial();
         }
-        win_done = true;
-        __syncthreads();
-        if (sh.flag) break;
+        if (!voted) {
+            lds_barrier();
+            if (sh.flag) break;
+        }
         {
             // Blocks whose X reaches the round's final threshold's score key: rows beyond the
-            // record may rank. Usually there is none, and one barrier says so.
-            const uint32_t X = rb.y;
-            const bool okd = has && X != 0u && X >= (uint32_t)(sh.thr >> 32);
-            const bool wany = __ballot(okd) != 0ull;
-            if (lane == 0) sh.anyd[wave] = wany ? 1 : 0;
-            lds_barrier();
+            // record may rank. Usually there is none, and one barrier (or the cut's) says so.
+            const bool okd = X != 0u && X >= (uint32_t)(sh.thr >> 32);
+            if (!voted) {
+                const bool wany = __ballot(okd) != 0ull;
+                if (lane == 0) sh.anyd[wave] = wany ? 1 : 0;
+                lds_barrier();
+            }
             int any = 0;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) any |= sh.anyd[w];
             if (any) {
                 const bool no[1] = {false};
                 const uint64_t nk[1] = {0ull};
-                append_all<D, 1>(sh, no, nk, okd, ((uint64_t)X << 32) | (uint32_t)blk, rb.x);
+                (void)append_all<D, 1>(sh, no, nk, okd, ((uint64_t)X << 32) | (uint32_t)blk, rb.x);
                 __syncthreads();
                 if (sh.ndef > kDef) {
                     __syncthreads();
@@ -415,6 +503,7 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
             if (tid == 0) sh.flag = 1;
             __syncthreads();
         } else {
+            resc = true;
             constexpr int LPR = S::LPR, RPG = S::RPG, P = S::P;
             constexpr int RW = kRows / kWaves;  // rows per wavefront
             constexpr int NL = RW / RPG;        // row groups per wavefront
@@ -500,14 +589,10 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
         }
         __syncthreads();
     }
-    // The top-k' rows are sh.cand[0..kp), in an order fixed by the inputs. Their V rows are
-    // requested first (partial of wavefront `wave`: rows c = wave*RPW + slot + u*kWaves*RPW);
-    // while they load, the top-k' places in out_idx (the number of selected positions below)
-    // and the anchor-and-window partial.
-    constexpr int UT = 4;
-    const int cs = lane % AS::LPR, slot = lane / AS::LPR;
-    const int step = kWaves * AS::RPW;
-    const uint32_t last_row = (uint32_t)(a.n - 1);
+    // The top-k' rows are sh.cand[0..kp), in an order fixed by the inputs. Unless they were
+    // requested before the cut, their V rows are requested now; while they load, the top-k'
+    // places in out_idx and the anchor-and-window partial.
+    const bool use_pre = pre && !sh.flag && !resc;  // (uniform)
     uint4 vv[UT];
     uint32_t sk[UT];
     auto request = [&](int c0) {
@@ -522,47 +607,25 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
             vv[u] = reinterpret_cast<const uint4 *>(vb + (size_t)pos * D)[cs];
         }
     };
-    if (ATTEND && kp > 0) request(wave * AS::RPW);
-    if (kp <= 64) {
-        if (wave == kWaves - 1) {
-            // One candidate per lane (0xFFFFFFFF past k'): a bitonic sort across the wavefront
-            // leaves the c-th smallest position in lane c.
-            uint32_t pos = lane < kp ? (uint32_t)rank_key_pos(sh.cand[lane]) : 0xFFFFFFFFu;
-#pragma unroll
-            for (int kk = 2; kk <= 64; kk <<= 1) {
-#pragma unroll
-                for (int j = kk >> 1; j > 0; j >>= 1) {
-                    const uint32_t other = (uint32_t)__shfl_xor((int)pos, j);
-                    const bool up = (lane & kk) == 0, low = (lane & j) == 0;
-                    const uint32_t lo = other < pos ? other : pos, hi = other < pos ? pos : other;
-                    pos = (low == up) ? lo : hi;
-                }
-            }
-            if (lane < kp) row[qi.base + lane] = (int32_t)pos;
-        }
-    } else {
-        const int kp8 = (kp + 7) & ~7;
-        for (int cb = 64 * (kWaves - 1 - wave); cb < kp; cb += 64 * kWaves) {
-            const int c = cb + lane;
+    if (ATTEND && kp > 0 && !use_pre) request(wave * AS::RPW);
+    // Places of the top-k' in out_idx (positions ascending), on wavefronts w0 .. w0 + nw - 1: a
+    // group of 8 lanes per member counts the smaller positions. With the output, wavefronts 2..
+    // do it while 0 and 1 write the merged output (the last one is kept for the mass diagnostic).
+    auto place_top = [&](int w0, int nw) {
+        if (wave < w0 || wave >= w0 + nw) return;
+        const int rel = tid - 64 * w0;
+        for (int c0 = 0; c0 < kp; c0 += nw * 8) {
+            const int c = c0 + (rel >> 3);
             const uint32_t pos = c < kp ? (uint32_t)rank_key_pos(sh.cand[c]) : 0u;
-            int rank = 0;
-            for (int f0 = 0; f0 < kp8; f0 += 8) {
-                // (Whole groups of 8 read: kp8 <= kSelMax <= kCand.)
-                const uint4 *src = reinterpret_cast<const uint4 *>(sh.cand + f0);
-                uint4 y[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = src[e];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    rank += (f0 + 2 * e < kp) && ~y[e].x < pos;
-                    rank += (f0 + 2 * e + 1 < kp) && ~y[e].z < pos;
-                }
-            }
-            if (c < kp) row[qi.base + rank] = (int32_t)pos;
+            // (The position is the complement of a key's low word.)
+            const uint32_t r = group8_count(sh.cand, kp, [&](uint64_t y) { return ~(uint32_t)y < pos; });
+            if ((tid & 7) == 0 && c < kp) row[qi.base + r] = (int32_t)pos;
         }
-    }
+    };
+    static_assert(D <= 128, "the merged output is written by wavefronts 0 and 1");
+    if constexpr (!ATTEND) place_top(0, kWaves);
     if constexpr (ATTEND) {
-        if (!win_done) window_partial();
+        window_merge();
         // Top-k rows: weights exp2((s - m) * scale), m the largest selected score.
         float acc[AS::EPL];
 #pragma unroll
@@ -574,14 +637,28 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
             kmax = x > kmax ? x : kmax;
         }
         const float m = kp > 0 ? key_score(wave_max_u32_dpp(kmax)) : -INFINITY;
-        for (int c0 = wave * AS::RPW; c0 < kp; c0 += UT * step) {
-            if (c0 != wave * AS::RPW) request(c0);
+        if (use_pre) {
+            // The candidates requested before the cut: the members are those reaching the
+            // final threshold (the k'-th key, or the admission bound when all were kept).
+            const uint64_t thr = sh.thr;
 #pragma unroll
             for (int u = 0; u < UT; ++u) {
-                if (c0 + u * step + slot < kp) {
-                    const float w = exp2f((key_score(sk[u]) - m) * a.scale_log2e);
+                if (pk[u] != 0ull && pk[u] >= thr) {
+                    const float w = exp2f((key_score((uint32_t)(pk[u] >> 32)) - m) * a.scale_log2e);
                     l += w;
-                    accumulate16(acc, vv[u], w, T());
+                    accumulate16(acc, pv[u], w, T());
+                }
+            }
+        } else {
+            for (int c0 = wave * AS::RPW; c0 < kp; c0 += UT * step) {
+                if (c0 != wave * AS::RPW) request(c0);
+#pragma unroll
+                for (int u = 0; u < UT; ++u) {
+                    if (c0 + u * step + slot < kp) {
+                        const float w = exp2f((key_score(sk[u]) - m) * a.scale_log2e);
+                        l += w;
+                        accumulate16(acc, vv[u], w, T());
+                    }
                 }
             }
         }
@@ -618,6 +695,7 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
         lds_barrier();
         float *o = a.out + (size_t)qi.qv * D;
         merge_partials<kNT, D, 2 * kWaves>(sh.part, 0, NWW + kWaves, a.scale_log2e, o);
+        place_top(2, MASS ? kWaves - 3 : kWaves - 2);
         if constexpr (MASS) {
             // Mass diagnostic (section 3.2.2, the full-softmax mass outside C_i; sections
             // 2.2.1-2.2.3, the parts of C_i): the candidates' part from the blocks' sums, the

@@ -12,12 +12,13 @@ namespace ca {
 namespace dec {
 namespace {
 
-// ---- long windows: anchor-and-window partials in the first workgroups ------------------------
-// Workgroup b (< units * G * nch): chunk c = b % nch of query t = (b / nch) / units of unit
+// ---- anchor-and-window partials in the last workgroups of the grid ---------------------------
+// Window workgroup b (< units * G * nch): chunk c = b % nch of query t = (b / nch) / units of unit
 // (b / nch) % units, entries [c * kWinChunkRows, (c + 1) * kWinChunkRows) of the query's
 // anchor-and-window list ({0} if the window does not reach it, then i - W + 1 .. i). Its eight
 // wavefronts take their share (wave_partial) and the merged partial (m, l, acc[D],
-// unnormalised) goes to a.win. They stream with the key rows instead of after them.
+// unnormalised) goes to a.win. They are dispatched after the key workgroups, into the CUs that
+// the stream's last workgroups leave idle, so decode_finish only merges their partials.
 template <typename T, int D, int G>
 __device__ __forceinline__ void window_chunk(const T *__restrict__ q, const T *__restrict__ k,
                                              const T *__restrict__ v, const DecodeArgs &a, uint32_t blk,
@@ -77,15 +78,15 @@ template <typename T, int D, int G, bool MASS>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 5 : 4))) void decode_stream_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, DecodeArgs a) {
     __shared__ uint32_t kst[G][kBW * kRows];  // keys of the workgroup's rows, per query
-    // Long windows: the first units * G * nch workgroups make the anchor-and-window partials.
-    const uint32_t nwin = a.win ? a.units * (uint32_t)G * (uint32_t)a.nch : 0u;
-    if (blockIdx.x < nwin) {
+    // The workgroups after the units' key workgroups make the anchor-and-window partials.
+    const uint32_t nkey = a.units * (uint32_t)((a.nblk + kBW - 1) / kBW);
+    if (blockIdx.x >= nkey) {
         __shared__ SoftmaxPartials<D, kWaves> wpart;
-        window_chunk<T, D, G>(q, k, v, a, blockIdx.x, wpart);
+        if (a.win) window_chunk<T, D, G>(q, k, v, a, blockIdx.x - nkey, wpart);
         return;
     }
-    // Workgroup nwin + s: unit s % units, its part s / units.
-    const uint32_t sblk = blockIdx.x - nwin;
+    // Key workgroup s: unit s % units, its part s / units.
+    const uint32_t sblk = blockIdx.x;
     const uint32_t part = sblk / a.units;
     const uint32_t uu = sblk - part * a.units;
     using S = StreamShape<T, D>;

@@ -41,10 +41,11 @@ SMALL = {
     "window_covers_all": W_(dtype="f32", d=64, heads=2, kv_heads=2, n=200, nq=200, W=512, topk=8),
     "single_key": W_(dtype="f32", d=64, heads=2, kv_heads=1, n=1, nq=1, W=1, topk=4, needles_per_kv_head=0),
     "W1_prefill": W_(dtype="f32", d=64, heads=1, kv_heads=1, n=700, nq=700, W=1, topk=5),
-    # Windows of 512 rows and more on the decode path: the anchor-and-window rows go through
-    # decode_window in chunks of 256 (3 chunks here; 5 and 12 in the 131K and near-limit cases):
-    # a last chunk of 89 rows, windows that reach position 0 (the first 212 rows of the fp32
-    # case, with no candidates, beside rows that have them), and 768 rows in exactly 3 chunks.
+    # Long windows on the decode path: the anchor-and-window rows go through decode_stream's
+    # window workgroups in chunks of 64 (10 chunks here, 5 in the 131K decode and 47 in the
+    # near-limit cases): a last chunk of 25 rows, windows that reach position 0 (the first 212
+    # rows of the fp32 case, with no candidates, beside rows that have them), and 768 rows in
+    # exactly 12 chunks, more than the 7 that decode_finish's wavefronts take at once.
     "long_window_bf16_d128": W_(heads=8, kv_heads=2, n=5000, W=600, topk=32),
     "long_window_f32_d64_early": W_(dtype="f32", d=64, heads=2, kv_heads=1, n=900, nq=600, W=512, topk=16),
     "long_window_bf16_d64_full_chunks": W_(d=64, heads=4, kv_heads=2, n=3000, nq=2, W=767, topk=24),
