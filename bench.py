@@ -240,15 +240,21 @@ def main():
             "avg_launch_us": pass_s * 1e6,
         }
     if "decode_stream" in prof and not args.dense:
-        # Decode path: decode_stream reads every candidate key row once (the score stage);
+        # Decode path: decode_stream reads every candidate key row once (the score stage) and,
+        # in its last workgroups, the K and V rows of the anchors and windows (the distinct
+        # rows: the windows of the nq query rows of a KV head overlap, position 0 once);
         # decode_finish (selection, set assembly, attend) follows it.
         launches, dec_ms = prof["decode_stream"]
         dec_avg_s = dec_ms / max(1, launches) / 1e3
+        win_rows = min(w.n, w.W + w.nq - 1)
+        win_rows += 1 if w.n - w.nq - w.W + 1 > 0 else 0
+        score_bytes += w.batch * w.kv_heads * win_rows * 2 * w.d * eb
         achieved = score_bytes / dec_avg_s / 1e9
         # The recorded counters are those of the kernel without the mass diagnostic.
         traffic = recorded_traffic(w.name) if not args.mass else None
         roofline = {
-            "kernel": "decode_stream (score stage: every key row once, block records)",
+            "kernel": "decode_stream (score stage: every key row once, block records; "
+                      "anchor-and-window partials)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
