@@ -190,14 +190,15 @@ __device__ __forceinline__ void cut_exact(FinShared<D> &sh, int kp) {
     }
 }
 
-// The number of keys list[0..n) (n <= kRankMax) that key beats under `beats`, summed over the 8
-// lanes of each group (every lane of the group gets it): lane `part` of a group reads keys
+// The number of keys y of list[0..n) (n <= kRankMax) with beats(y, s), s = 0 and 1, summed over
+// the 8 lanes of each group (every lane of the group gets both): lane `part` of a group reads keys
 // 16 i + 2 part and 16 i + 2 part + 1 (the group reads 128 contiguous bytes, four 16-byte reads
 // in flight per lane; reads past n stay inside the list's storage and are not counted).
+// Both counts come from the same reads (beats(y, 0) and beats(y, 1): two members per group).
 template <typename Beats>
-__device__ __forceinline__ uint32_t group8_count(const uint64_t *list, int n, Beats beats) {
+__device__ __forceinline__ uint2 group8_count(const uint64_t *list, int n, Beats beats) {
     const int part = threadIdx.x & 7;
-    uint32_t r = 0u;
+    uint32_t r0 = 0u, r1 = 0u;
     for (int j0 = 0; j0 < n; j0 += 64) {
         uint4 x[4];
 #pragma unroll
@@ -206,18 +207,24 @@ __device__ __forceinline__ uint32_t group8_count(const uint64_t *list, int n, Be
         for (int e = 0; e < 4; ++e) {
             const int j = j0 + 16 * e + 2 * part;
             const uint64_t y0 = ((uint64_t)x[e].y << 32) | x[e].x, y1 = ((uint64_t)x[e].w << 32) | x[e].z;
-            r += (j < n && beats(y0)) ? 1u : 0u;
-            r += (j + 1 < n && beats(y1)) ? 1u : 0u;
+            r0 += (j < n && beats(y0, 0)) ? 1u : 0u;
+            r0 += (j + 1 < n && beats(y1, 0)) ? 1u : 0u;
+            r1 += (j < n && beats(y0, 1)) ? 1u : 0u;
+            r1 += (j + 1 < n && beats(y1, 1)) ? 1u : 0u;
         }
     }
-    r += dpp_u32<0xB1>(0u, r);   // lane ^ 1
-    r += dpp_u32<0x4E>(0u, r);   // lane ^ 2
-    r += dpp_u32<0x141>(0u, r);  // the mirrored lane of the group of 8: the other quad
-    return r;
+    r0 += dpp_u32<0xB1>(0u, r0);   // lane ^ 1
+    r1 += dpp_u32<0xB1>(0u, r1);
+    r0 += dpp_u32<0x4E>(0u, r0);   // lane ^ 2
+    r1 += dpp_u32<0x4E>(0u, r1);
+    r0 += dpp_u32<0x141>(0u, r0);  // the mirrored lane of the group of 8: the other quad
+    r1 += dpp_u32<0x141>(0u, r1);
+    return make_uint2(r0, r1);
 }
 
 // Exact top kp of the n distinct ranking keys sh.cand[0..n) (kp < n <= kRankMax), all threads:
-// each key's rank (the number of keys above it) is counted by a group of 8 lanes; the keys of
+// each key's rank (the number of keys above it) is counted by a group of 8 lanes (two keys per
+// group, from the same reads); the keys of
 // rank < kp go to sh.cand[0..kp) in descending order, and the threshold becomes the kp-th key.
 // On the way, sh.anyd[wave] says whether some thread's block key X (0: none) reaches the new
 // threshold's score key. Two barriers, on LDS traffic only (vector loads stay in flight).
@@ -225,11 +232,12 @@ template <int D>
 __device__ __forceinline__ void rank_cut(FinShared<D> &sh, int n, int kp, uint32_t X) {
     const int tid = threadIdx.x;
     uint64_t *const top = sh.cand + (kCand - kRankMax);  // (past every read: n <= kRankMax)
-    for (int c0 = 0; c0 < n; c0 += kNT / 8) {
-        const int c = c0 + (tid >> 3);
-        const uint64_t key = c < n ? sh.cand[c] : ~0ull;
-        const uint32_t r = group8_count(sh.cand, n, [&](uint64_t y) { return y > key; });
-        if ((tid & 7) == 0 && c < n && r < (uint32_t)kp) top[r] = key;
+    for (int c0 = 0; c0 < n; c0 += kNT / 4) {
+        const int c = c0 + (tid >> 3), c1 = c + kNT / 8;
+        const uint64_t key = c < n ? sh.cand[c] : ~0ull, key1 = c1 < n ? sh.cand[c1] : ~0ull;
+        const uint2 r = group8_count(sh.cand, n, [&](uint64_t y, int s) { return y > (s ? key1 : key); });
+        if ((tid & 7) == 0 && c < n && r.x < (uint32_t)kp) top[r.x] = key;
+        if ((tid & 7) == 1 && c1 < n && r.y < (uint32_t)kp) top[r.y] = key1;
     }
     lds_barrier();
     const bool okd = X != 0u && X >= (uint32_t)(top[kp - 1] >> 32);
@@ -609,24 +617,27 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
     };
     if (ATTEND && kp > 0 && !use_pre) request(wave * AS::RPW);
     // Places of the top-k' in out_idx (positions ascending), on wavefronts w0 .. w0 + nw - 1: a
-    // group of 8 lanes per member counts the smaller positions. With the output, wavefronts 2..
+    // group of 8 lanes per two members counts the smaller positions. With the output, wavefronts 2..
     // do it while 0 and 1 write the merged output (the last one is kept for the mass diagnostic).
     auto place_top = [&](int w0, int nw) {
         if (wave < w0 || wave >= w0 + nw) return;
         const int rel = tid - 64 * w0;
-        for (int c0 = 0; c0 < kp; c0 += nw * 8) {
-            const int c = c0 + (rel >> 3);
+        for (int c0 = 0; c0 < kp; c0 += nw * 16) {
+            const int c = c0 + (rel >> 3), c1 = c + nw * 8;
             const uint32_t pos = c < kp ? (uint32_t)rank_key_pos(sh.cand[c]) : 0u;
+            const uint32_t pos1 = c1 < kp ? (uint32_t)rank_key_pos(sh.cand[c1]) : 0u;
             // (The position is the complement of a key's low word.)
-            const uint32_t r = group8_count(sh.cand, kp, [&](uint64_t y) { return ~(uint32_t)y < pos; });
-            if ((tid & 7) == 0 && c < kp) row[qi.base + r] = (int32_t)pos;
+            const uint2 r = group8_count(sh.cand, kp, [&](uint64_t y, int s) { return ~(uint32_t)y < (s ? pos1 : pos); });
+            if ((tid & 7) == 0 && c < kp) row[qi.base + r.x] = (int32_t)pos;
+            if ((tid & 7) == 1 && c1 < kp) row[qi.base + r.y] = (int32_t)pos1;
         }
     };
     static_assert(D <= 128, "the merged output is written by wavefronts 0 and 1");
     if constexpr (!ATTEND) place_top(0, kWaves);
     if constexpr (ATTEND) {
         window_merge();
-        // Top-k rows: weights exp2((s - m) * scale), m the largest selected score.
+        // Top-k rows: weights exp2((s - m) * scale), m the largest selected score (the hardware
+        // exponential: a weight below 2^-126 of the largest counts as 0, which no fp32 sum sees).
         float acc[AS::EPL];
 #pragma unroll
         for (int e = 0; e < AS::EPL; ++e) acc[e] = 0.f;
@@ -644,7 +655,7 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
 #pragma unroll
             for (int u = 0; u < UT; ++u) {
                 if (pk[u] != 0ull && pk[u] >= thr) {
-                    const float w = exp2f((key_score((uint32_t)(pk[u] >> 32)) - m) * a.scale_log2e);
+                    const float w = __builtin_amdgcn_exp2f((key_score((uint32_t)(pk[u] >> 32)) - m) * a.scale_log2e);
                     l += w;
                     accumulate16(acc, pv[u], w, T());
                 }
@@ -655,7 +666,7 @@ __global__ __launch_bounds__(kNT) void decode_finish_kernel(const T *__restrict_
 #pragma unroll
                 for (int u = 0; u < UT; ++u) {
                     if (c0 + u * step + slot < kp) {
-                        const float w = exp2f((key_score(sk[u]) - m) * a.scale_log2e);
+                        const float w = __builtin_amdgcn_exp2f((key_score(sk[u]) - m) * a.scale_log2e);
                         l += w;
                         accumulate16(acc, vv[u], w, T());
                     }
