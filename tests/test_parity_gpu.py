@@ -227,6 +227,30 @@ def test_clustered_best_rows(dtype, length, topk):
     assert_outputs(out, oracle.restricted(x["q"], x["k"], x["v"], idx), w.torch_dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_clustered_best_rows_then_a_second_round_of_records(dtype):
+    """A decode over 140,000 keys reads its block records in two rounds of 512 blocks. The
+    cluster sits in the first round, so its blocks are still listed for a second scoring when
+    the second round's candidates are cut (by rank counting: fewer than 257 candidates); the
+    cut must drop the listed blocks whose rows can no longer rank and keep the others."""
+    w = W_(dtype=dtype, heads=4, kv_heads=1, n=140000, nq=1, W=64, topk=48)
+    x = clustered_inputs(w, seed=17, start=3001, length=60)
+    # A second, shorter run in the second round, scaled to displace part of the first: its rows
+    # enter the second round's cut while the first run's block is still listed.
+    q = x["q"].float()
+    k = x["k"].float()
+    d = q[:, 0:4].sum(dim=(1, 2))
+    d = d / d.norm(dim=-1, keepdim=True) * 24.0
+    gains = 1.3 + 0.01 * torch.arange(20, dtype=torch.float32)
+    k[:, 0, 135001:135021] = d[:, None, :] * gains[None, :, None]
+    x["k"] = k.to(w.torch_dtype)
+    announce(f"clustered two rounds {dtype}")
+    out, idx = run_gpu(w, x)
+    ref_idx, _, ref_diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
+    compare_sets(idx, ref_idx, ref_diag, x["q"], x["k"], w.W, w.topk)
+    assert_outputs(out, oracle.restricted(x["q"], x["k"], x["v"], idx), w.torch_dtype)
+
+
 @pytest.mark.parametrize("name", ["prefill_bf16_ragged", "mfma_wave64", "mfma_wave128"])
 def test_select_stage_alone_matches_full_call(name):
     # (The last two: over 4096 bf16 query vectors, the MFMA path with its 64- and 128-thread
