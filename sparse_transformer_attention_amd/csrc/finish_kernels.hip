@@ -46,46 +46,41 @@ __device__ __forceinline__ int64_t block_qv() {
     return (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
 }
 
-// Exact top-kp of n distinct non-zero ranking keys in gathered[0..n) (kp <= n <= kRankSelectMax, n <= NT,
-// so the tail of gathered[] holds a copy clear of them) by rank counting: a key is selected when
-// fewer than kp keys beat it; the selected positions are then placed by their rank among the
-// selected ones (ascending) in js[0..kp). S lanes per candidate (S*n <= NT, S <= 16): lane s
-// compares against keys s, s+S, ..., and the S counts are summed. All threads; ends with an
-// LDS barrier.
+// Exact top-kp of n distinct non-zero ranking keys in gathered[0..n) (kp <= n <= kRankSelectMax,
+// n <= NT) by rank counting: each key's rank, the number of keys above it, is counted by a group
+// of 8 lanes (two keys per group, group8_count); the keys of rank < kp go, in that order, to the
+// tail of gathered[] (64 ceil(kp / 64) entries clear of every read of the first count), and the
+// same count on their positions places them ascending in js[0..kp) (their score keys in
+// jk[0..kp)). All threads; two LDS barriers, the last at the end.
 constexpr int kRankSelectMax = 256;
-static_assert(2 * kRankSelectMax <= kGather && 2 * 128 <= kGatherFor<128>, "rank select room");
+static_assert(kRankSelectMax <= kGather - kRankSelectMax && 128 <= kGatherFor<128> - 128, "rank select room");
 template <int NT>
 __device__ __forceinline__ void select_by_rank(int n, int kp, uint64_t *gathered, int32_t *js,
                                                uint32_t *jk = nullptr) {
-    const int tid = threadIdx.x;
-    int lg = 4;
-    while (lg > 0 && (n << lg) > NT) --lg;
-    const int S = 1 << lg, c = tid >> lg, sl = tid & (S - 1);
-    const bool mine = c < n;
-    const uint64_t x = gathered[mine ? c : 0];
-    int above = 0;
-    if (mine) {
-#pragma unroll 4
-        for (int f = sl; f < n; f += S) above += gathered[f] > x;
+    const int tid = threadIdx.x, part = tid & 7;
+    uint64_t *const top = gathered + kGatherFor<NT> - 64 * ((kp + 63) / 64);
+    for (int c0 = 0; c0 < n; c0 += NT / 4) {
+        const int c = c0 + (tid >> 3), c1 = c + NT / 8;
+        const uint64_t x0 = c < n ? gathered[c] : ~0ull, x1 = c1 < n ? gathered[c1] : ~0ull;
+        const uint2 r = group8_count(gathered, n, [&](uint64_t y, int s) { return y > (s ? x1 : x0); });
+        if (part == 0 && c < n && r.x < (uint32_t)kp) top[r.x] = x0;
+        if (part == 1 && c1 < n && r.y < (uint32_t)kp) top[r.y] = x1;
     }
-    for (int off = 1; off < S; off <<= 1) above += __shfl_xor(above, off);
-    const bool chosen = mine && above < kp;
-    // Selected keys (0 = not) in the tail of gathered[], clear of [0, n).
-    if (mine && sl == 0) gathered[kGatherFor<NT> - 1 - c] = chosen ? x : 0ull;
     lds_barrier();
-    const int32_t pos = rank_key_pos(x);
-    int rank = 0;
-    if (chosen) {
-#pragma unroll 4
-        for (int f = sl; f < n; f += S) {
-            const uint64_t y = gathered[kGatherFor<NT> - 1 - f];
-            rank += y != 0ull && rank_key_pos(y) < pos;
+    for (int c0 = 0; c0 < kp; c0 += NT / 4) {
+        const int c = c0 + (tid >> 3), c1 = c + NT / 8;
+        const uint64_t x0 = c < kp ? top[c] : 0ull, x1 = c1 < kp ? top[c1] : 0ull;
+        const uint32_t p0 = (uint32_t)rank_key_pos(x0), p1 = (uint32_t)rank_key_pos(x1);
+        // (A position is the complement of its key's low word.)
+        const uint2 r = group8_count(top, kp, [&](uint64_t y, int s) { return ~(uint32_t)y < (s ? p1 : p0); });
+        if (part == 0 && c < kp) {
+            js[r.x] = (int32_t)p0;
+            if (jk) jk[r.x] = (uint32_t)(x0 >> 32);  // its score key, in the same place
         }
-    }
-    for (int off = 1; off < S; off <<= 1) rank += __shfl_xor(rank, off);
-    if (chosen && sl == 0) {
-        js[rank] = pos;
-        if (jk) jk[rank] = (uint32_t)(x >> 32);  // its score key, in the same place
+        if (part == 1 && c1 < kp) {
+            js[r.y] = (int32_t)p1;
+            if (jk) jk[r.y] = (uint32_t)(x1 >> 32);
+        }
     }
     lds_barrier();
 }
@@ -159,7 +154,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const T *__restrict__ q, con
     constexpr int NW = NT / 64;
     extern __shared__ int32_t fsm[];  // js[2*cap] positions, then sel[topk] keys
     __shared__ SelectShared<NT> ssh;
-    __shared__ uint64_t gathered[kGatherFor<NT>];
+    __shared__ alignas(16) uint64_t gathered[kGatherFor<NT>];  // (16-byte reads in select_by_rank)
     // Softmax partials: [0, NW) the anchor and window rows (wavefronts 1..NW-1 when wavefront 0
     // takes the bound), [NW, 2NW) the top-k rows.
     __shared__ SoftmaxPartials<D, ATTEND ? 2 * NW : 1> part;

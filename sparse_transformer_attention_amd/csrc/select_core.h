@@ -314,4 +314,39 @@ __device__ __forceinline__ int wave_thin_u64(const uint64_t (&kr)[E], int keep, 
     return tot;
 }
 
+// ---- rank counting by groups of 8 lanes ----
+
+// The number of keys y of list[0..n) with beats(y, s), s = 0 and 1, summed over
+// the 8 lanes of each group (every lane of the group gets both): lane `part` of a group reads keys
+// 16 i + 2 part and 16 i + 2 part + 1 (the group reads 128 contiguous bytes, four 16-byte reads
+// in flight per lane). Reads reach list[64 ceil(n / 64) - 1]: the caller's storage must hold that
+// much, 16-byte aligned; entries past n are not counted.
+// Both counts come from the same reads (beats(y, 0) and beats(y, 1): two members per group).
+template <typename Beats>
+__device__ __forceinline__ uint2 group8_count(const uint64_t *list, int n, Beats beats) {
+    const int part = threadIdx.x & 7;
+    uint32_t r0 = 0u, r1 = 0u;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        uint4 x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = *reinterpret_cast<const uint4 *>(list + j0 + 16 * e + 2 * part);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = j0 + 16 * e + 2 * part;
+            const uint64_t y0 = ((uint64_t)x[e].y << 32) | x[e].x, y1 = ((uint64_t)x[e].w << 32) | x[e].z;
+            r0 += (j < n && beats(y0, 0)) ? 1u : 0u;
+            r0 += (j + 1 < n && beats(y1, 0)) ? 1u : 0u;
+            r1 += (j < n && beats(y0, 1)) ? 1u : 0u;
+            r1 += (j + 1 < n && beats(y1, 1)) ? 1u : 0u;
+        }
+    }
+    r0 += dpp_u32<0xB1>(0u, r0);   // lane ^ 1
+    r1 += dpp_u32<0xB1>(0u, r1);
+    r0 += dpp_u32<0x4E>(0u, r0);   // lane ^ 2
+    r1 += dpp_u32<0x4E>(0u, r1);
+    r0 += dpp_u32<0x141>(0u, r0);  // the mirrored lane of the group of 8: the other quad
+    r1 += dpp_u32<0x141>(0u, r1);
+    return make_uint2(r0, r1);
+}
+
 }  // namespace ca
