@@ -208,14 +208,16 @@ __device__ __forceinline__ void wave_partial_scored(const T *__restrict__ vbase,
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (ok[u]) mr = fmaxf(mr, s[u]);
-        const float f = st.m == -INFINITY ? 0.f : exp2f((st.m - mr) * scale_log2e);
+        // (The hardware exponential: a weight below 2^-126 of the largest counts as 0, which
+        // no fp32 sum sees.)
+        const float f = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - mr) * scale_log2e);
         st.l *= f;
 #pragma unroll
         for (int e = 0; e < S::EPL; ++e) st.acc[e] *= f;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (ok[u]) {
-                const float w = exp2f((s[u] - mr) * scale_log2e);
+                const float w = __builtin_amdgcn_exp2f((s[u] - mr) * scale_log2e);
                 st.l += w;
                 accumulate16(st.acc, vr[u], w, T());
             }

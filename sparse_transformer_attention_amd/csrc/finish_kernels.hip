@@ -99,8 +99,12 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
     if (wave == 0) {
         // Every slot of every segment, four per lane in flight with their segments' lengths,
         // kept when inside its segment's length (compacted by ballot).
+        // (Segments of a power-of-two length, as on the MFMA path, take shifts and masks
+        // instead of integer divisions.)
         constexpr int GU = 4;
         const int slots = wpu * topk;
+        const bool p2 = (topk & (topk - 1)) == 0;
+        const int lg = p2 ? __builtin_ctz((unsigned)topk) : 0;
         int base = 0;
         for (int f0 = 0; f0 < slots; f0 += 64 * GU) {
             uint64_t x[GU];
@@ -109,12 +113,13 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
             for (int u = 0; u < GU; ++u) {
                 const int f = f0 + u * 64 + lane, fc = f < slots ? f : slots - 1;
                 x[u] = lists[fc];
-                c[u] = cnt[fc / topk];
+                c[u] = cnt[p2 ? fc >> lg : fc / topk];
             }
 #pragma unroll
             for (int u = 0; u < GU; ++u) {
                 const int f = f0 + u * 64 + lane;
-                const bool ok = f < slots && (uint32_t)(f % topk) < c[u];
+                const int e = p2 ? (f & (topk - 1)) : f % topk;
+                const bool ok = f < slots && (uint32_t)e < c[u];
                 const uint64_t bal = __ballot(ok);
                 const int pos = base + lanes_below(bal);
                 if (ok && pos < kGatherFor<NT>) gathered[pos] = x[u];
