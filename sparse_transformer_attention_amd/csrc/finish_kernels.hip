@@ -47,39 +47,54 @@ __device__ __forceinline__ int64_t block_qv() {
 }
 
 // Exact top-kp of n distinct non-zero ranking keys in gathered[0..n) (kp <= n <= kRankSelectMax,
-// n <= NT) by rank counting: each key's rank, the number of keys above it, is counted by a group
-// of 8 lanes (two keys per group, group8_count); the keys of rank < kp go, in that order, to the
-// tail of gathered[] (64 ceil(kp / 64) entries clear of every read of the first count), and the
-// same count on their positions places them ascending in js[0..kp) (their score keys in
-// jk[0..kp)). All threads; two LDS barriers, the last at the end.
+// n <= NT; gathered[n .. 64 ceil(n / 64)) holds 0 keys) by rank counting: each key's rank, the
+// number of keys above it, is counted by a group of 8 lanes (four keys per group,
+// group8_count4); the keys of rank < kp go, in that order, to the tail of gathered[]
+// (64 ceil(kp / 64) entries clear of every read of the first count, 0 past kp), and the same
+// count on their positions places them ascending in js[0..kp) (their score keys in jk[0..kp)).
+// All threads; two LDS barriers, the last at the end.
 constexpr int kRankSelectMax = 256;
 static_assert(kRankSelectMax <= kGather - kRankSelectMax && 128 <= kGatherFor<128> - 128, "rank select room");
 template <int NT>
 __device__ __forceinline__ void select_by_rank(int n, int kp, uint64_t *gathered, int32_t *js,
                                                uint32_t *jk = nullptr) {
     const int tid = threadIdx.x, part = tid & 7;
-    uint64_t *const top = gathered + kGatherFor<NT> - 64 * ((kp + 63) / 64);
-    for (int c0 = 0; c0 < n; c0 += NT / 4) {
-        const int c = c0 + (tid >> 3), c1 = c + NT / 8;
-        const uint64_t x0 = c < n ? gathered[c] : ~0ull, x1 = c1 < n ? gathered[c1] : ~0ull;
-        const uint2 r = group8_count(gathered, n, [&](uint64_t y, int s) { return y > (s ? x1 : x0); });
-        if (part == 0 && c < n && r.x < (uint32_t)kp) top[r.x] = x0;
-        if (part == 1 && c1 < n && r.y < (uint32_t)kp) top[r.y] = x1;
+    const int kp64 = 64 * ((kp + 63) / 64);
+    uint64_t *const top = gathered + kGatherFor<NT> - kp64;
+    for (int t = kp + tid; t < kp64; t += NT) top[t] = 0ull;
+    for (int c0 = 0; c0 < n; c0 += NT / 2) {
+        uint64_t x[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int c = c0 + (tid >> 3) + s * (NT / 8);
+            x[s] = c < n ? gathered[c] : ~0ull;
+        }
+        const uint4 r = group8_count4(gathered, n, [&](uint64_t y, int s) { return y > x[s]; });
+        const uint32_t rs[4] = {r.x, r.y, r.z, r.w};
+        if (part < 4) {
+            const int c = c0 + (tid >> 3) + part * (NT / 8);
+            if (c < n && rs[part] < (uint32_t)kp) top[rs[part]] = x[part];
+        }
     }
     lds_barrier();
-    for (int c0 = 0; c0 < kp; c0 += NT / 4) {
-        const int c = c0 + (tid >> 3), c1 = c + NT / 8;
-        const uint64_t x0 = c < kp ? top[c] : 0ull, x1 = c1 < kp ? top[c1] : 0ull;
-        const uint32_t p0 = (uint32_t)rank_key_pos(x0), p1 = (uint32_t)rank_key_pos(x1);
-        // (A position is the complement of its key's low word.)
-        const uint2 r = group8_count(top, kp, [&](uint64_t y, int s) { return ~(uint32_t)y < (s ? p1 : p0); });
-        if (part == 0 && c < kp) {
-            js[r.x] = (int32_t)p0;
-            if (jk) jk[r.x] = (uint32_t)(x0 >> 32);  // its score key, in the same place
+    for (int c0 = 0; c0 < kp; c0 += NT / 2) {
+        uint64_t x[4];
+        uint32_t p[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int c = c0 + (tid >> 3) + s * (NT / 8);
+            x[s] = c < kp ? top[c] : 0ull;
+            p[s] = (uint32_t)rank_key_pos(x[s]);
         }
-        if (part == 1 && c1 < kp) {
-            js[r.y] = (int32_t)p1;
-            if (jk) jk[r.y] = (uint32_t)(x1 >> 32);
+        // (A position is the complement of its key's low word.)
+        const uint4 r = group8_count4(top, kp, [&](uint64_t y, int s) { return ~(uint32_t)y < p[s]; });
+        const uint32_t rs[4] = {r.x, r.y, r.z, r.w};
+        if (part < 4) {
+            const int c = c0 + (tid >> 3) + part * (NT / 8);
+            if (c < kp) {
+                js[rs[part]] = (int32_t)p[part];
+                if (jk) jk[rs[part]] = (uint32_t)(x[part] >> 32);  // its score key, in the same place
+            }
         }
     }
     lds_barrier();
@@ -126,6 +141,8 @@ __device__ __forceinline__ void select_segments(const uint32_t *__restrict__ cnt
                 base += __popcll(bal);
             }
         }
+        // 0 keys up to the next multiple of 64 (the rank count reads whole groups of 64).
+        if (base + lane < kGatherFor<NT> && lane < 64 * ((base + 63) / 64) - base) gathered[base + lane] = 0ull;
         if (lane == 0) sh.sel_count = base;
     } else {
         overlap();

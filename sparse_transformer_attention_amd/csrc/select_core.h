@@ -349,4 +349,31 @@ __device__ __forceinline__ uint2 group8_count(const uint64_t *list, int n, Beats
     return make_uint2(r0, r1);
 }
 
+// As group8_count with four members per group (beats(y, s), s = 0..3) and no bounds test: the
+// entries from n up to 64 ceil(n / 64) must be 0 keys, which beat no member under either use
+// (y > x, and a position ~low word below p).
+template <typename Beats>
+__device__ __forceinline__ uint4 group8_count4(const uint64_t *list, int n, Beats beats) {
+    const int part = threadIdx.x & 7;
+    uint32_t r[4] = {0u, 0u, 0u, 0u};
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        uint4 x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = *reinterpret_cast<const uint4 *>(list + j0 + 16 * e + 2 * part);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint64_t y0 = ((uint64_t)x[e].y << 32) | x[e].x, y1 = ((uint64_t)x[e].w << 32) | x[e].z;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) r[s] += (beats(y0, s) ? 1u : 0u) + (beats(y1, s) ? 1u : 0u);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        r[s] += dpp_u32<0xB1>(0u, r[s]);
+        r[s] += dpp_u32<0x4E>(0u, r[s]);
+        r[s] += dpp_u32<0x141>(0u, r[s]);
+    }
+    return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
 }  // namespace ca
