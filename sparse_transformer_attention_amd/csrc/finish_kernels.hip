@@ -47,22 +47,54 @@ __device__ __forceinline__ int64_t block_qv() {
 }
 
 // Exact top-kp of n distinct non-zero ranking keys in gathered[0..n) (kp <= n <= kRankSelectMax,
-// n <= NT; gathered[n .. 64 ceil(n / 64)) holds 0 keys) by rank counting: each key's rank, the
-// number of keys above it, is counted by a group of 8 lanes (four keys per group,
-// group8_count4); the keys of rank < kp go, in that order, to the tail of gathered[]
-// (64 ceil(kp / 64) entries clear of every read of the first count, 0 past kp), and the same
-// count on their positions places them ascending in js[0..kp) (their score keys in jk[0..kp)).
-// All threads; two LDS barriers, the last at the end.
+// n <= NT; gathered[n .. 64 ceil(n / 64)) holds 0 keys): the keys that reach the kp-th largest
+// score key when exactly kp do, else by rank counting: each key's rank, the number of keys above
+// it, is counted by a group of 8 lanes (four keys per group, group8_count4) and the keys of rank
+// < kp are kept. They go to the tail of gathered[] (64 ceil(kp / 64) entries clear of every read
+// of the first count, 0 past kp), and the same count on their positions places them ascending in
+// js[0..kp) (their score keys in jk[0..kp)). All threads; two or three LDS barriers, the last at
+// the end.
 constexpr int kRankSelectMax = 256;
 static_assert(kRankSelectMax <= kGather - kRankSelectMax && 128 <= kGatherFor<128> - 128, "rank select room");
 template <int NT>
 __device__ __forceinline__ void select_by_rank(int n, int kp, uint64_t *gathered, int32_t *js,
                                                uint32_t *jk = nullptr) {
-    const int tid = threadIdx.x, part = tid & 7;
+    const int tid = threadIdx.x, part = tid & 7, lane = tid & 63;
     const int kp64 = 64 * ((kp + 63) / 64);
     uint64_t *const top = gathered + kGatherFor<NT> - kp64;
     for (int t = kp + tid; t < kp64; t += NT) top[t] = 0ull;
-    for (int c0 = 0; c0 < n; c0 += NT / 2) {
+    // First, on wavefront 0: the kp-th largest 32-bit score key by a bitwise search (no pairwise
+    // compares). When exactly kp keys reach it they are the top kp, in list order; otherwise
+    // (equal score keys at the kp-th place) the rank count below decides on the 64-bit keys.
+    __shared__ int found;
+    if (tid < 64) {
+        constexpr int E = NT / 64;  // (n <= NT)
+        uint64_t kk[E];
+        uint32_t sk[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int c = lane + 64 * e;
+            kk[e] = c < n ? gathered[c] : 0ull;
+            sk[e] = (uint32_t)(kk[e] >> 32);
+        }
+        const uint32_t t32 = wave_loose_kth_u32(sk, kp, 0);
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(sk[e] != 0u && sk[e] >= t32));
+        if (cnt == kp) {
+            int base = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bool ok = sk[e] != 0u && sk[e] >= t32;
+                const uint64_t bal = __ballot(ok);
+                if (ok) top[base + lanes_below(bal)] = kk[e];
+                base += __popcll(bal);
+            }
+        }
+        if (lane == 0) found = cnt == kp ? 1 : 0;
+    }
+    lds_barrier();
+    for (int c0 = 0; !found && c0 < n; c0 += NT / 2) {
         uint64_t x[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -76,7 +108,7 @@ __device__ __forceinline__ void select_by_rank(int n, int kp, uint64_t *gathered
             if (c < n && rs[part] < (uint32_t)kp) top[rs[part]] = x[part];
         }
     }
-    lds_barrier();
+    if (!found) lds_barrier();
     for (int c0 = 0; c0 < kp; c0 += NT / 2) {
         uint64_t x[4];
         uint32_t p[4];
