@@ -49,16 +49,26 @@ def draw(i: int) -> synth.Workload:
                           needles_per_kv_head=int(r.choice([0, 4, 16])))
 
 
-@pytest.mark.parametrize("i", range(N_PROBLEMS))
-def test_random_problem_matches_oracle(i):
+def check(i, chunk):
     w = draw(i)
-    print(f"[gpu-case] sweep {i}: B={w.batch} Hq={w.heads} Hkv={w.kv_heads} d={w.d} n={w.n} nq={w.nq} "
-          f"{w.dtype} W={w.W} k={w.topk}", file=sys.stderr, flush=True)
+    print(f"[gpu-case] sweep {i} chunk {chunk}: B={w.batch} Hq={w.heads} Hkv={w.kv_heads} d={w.d} "
+          f"n={w.n} nq={w.nq} {w.dtype} W={w.W} k={w.topk}", file=sys.stderr, flush=True)
     x = synth.make_inputs(w, seed=1000 + i)
     q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
-    out, idx = ca.condensate(q, k, v, w.W, w.topk)
+    out, idx = ca.condensate(q, k, v, w.W, w.topk, chunk=chunk)
     torch.cuda.synchronize()
     out, idx = out.cpu().numpy(), idx.cpu().numpy()
     ref_idx, _, ref_diag = oracle.condensate(x["q"], x["k"], x["v"], w.W, w.topk)
     compare_sets(idx, ref_idx, ref_diag, x["q"], x["k"], w.W, w.topk)
     assert_outputs(out, oracle.restricted(x["q"], x["k"], x["v"], idx), w.torch_dtype)
+
+
+@pytest.mark.parametrize("i", range(N_PROBLEMS))
+def test_random_problem_matches_oracle(i):
+    check(i, 0)
+
+
+@pytest.mark.parametrize("i", range(0, N_PROBLEMS, 4))
+def test_random_problem_on_the_chunked_path_matches_oracle(i):
+    """Every fourth problem again with the chunked path forced (chunks of 256 rows)."""
+    check(i, 256)
