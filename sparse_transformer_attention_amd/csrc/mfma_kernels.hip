@@ -591,18 +591,24 @@ struct WinArgs {
 
 // K and V rows base..base+63 of a tile (clamped to n - 1): 16-byte chunks, NCH per thread.
 // (Native 4 x u32 vectors: arrays of HIP's uint4 struct filled from memory stay on the stack.)
-// K: chunk c of row r per thread, D / 8 threads to a row. V at d = 128: the same chunk of two
-// consecutive rows per thread (rows 2p and 2p + 1, p = lane % 32), so that its transposed copy is
-// written as 4-byte pairs: chunk v_chunk(u) of the rows, the two half-wavefronts two chunks apart
-// (a wavefront's 2-byte stores of the K-like layout fell on 4 banks: dense kernel 3.50 -> 2.44 ms
-// on the 4K x 32K chunk). At d = 64, V as K.
+// K: chunk c of row r per thread, D / 8 threads to a row. V: the same chunk of two consecutive
+// rows per thread (rows 2p and 2p + 1), so that its transposed copy is written as 4-byte pairs.
+// d = 128: p = lane % 32, chunk v_chunk(u), the two half-wavefronts two chunks (32 banks) apart;
+// a wavefront's 2-byte stores of the K-like layout fell on 4 banks (dense kernel 3.50 -> 2.44 ms
+// on the 4K x 32K chunk). d = 64: the 8 lanes of a group take the 8 chunks of one row pair, so a
+// wavefront still reads whole rows (16 of them), with 2-way conflicts left (dense kernel on the
+// 131K prefill 20.14 -> 19.79 ms).
 typedef unsigned int win_u32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 __device__ __forceinline__ int v_chunk(int u, int tid) {
-    constexpr int NU = kWinTile * D / 8 / 256 / 2;  // chunks per thread (2 rows each): 2 or 1
-    const int w = tid >> 6, half = (tid >> 5) & 1;
-    return (NU == 2 ? u : (w & 1)) + 2 * half + 4 * (NU == 2 ? w : (w >> 1));
+    if constexpr (D == 128) return u + 2 * ((tid >> 5) & 1) + 4 * (tid >> 6);
+    else return tid & 7;
+}
+template <int D>
+__device__ __forceinline__ int v_pair(int tid) {
+    if constexpr (D == 128) return tid & 31;
+    else return ((tid & 63) >> 3) + 8 * (tid >> 6);
 }
 
 template <int D>
@@ -622,18 +628,14 @@ __device__ __forceinline__ void win_tile_load(win_u32x4 (&pk)[kWinTile * D / 8 /
     }
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-        // (d = 64: V like K; its 128-byte rows load better whole, and its stores conflict less.)
-        const int cid = tid + 256 * u;
-        const int row = D == 128 ? 2 * (tid & 31) + (u & 1) : cid / CPR;
-        const int c = D == 128 ? v_chunk<D>(u >> 1, tid) : cid % CPR;
+        const int row = 2 * v_pair<D>(tid) + (u & 1), c = v_chunk<D>(u >> 1, tid);
         const int j = base + row < nlast ? base + row : nlast;
         const uint32_t off = (uint32_t)j * (uint32_t)(D * sizeof(__bf16)) + (uint32_t)c * 16u;
         pv[u] = *reinterpret_cast<const win_u32x4 *>(vc + off);
     }
 }
-// The tile into LDS: K with swizzled chunks; V transposed ([d][row], bf16 bits): at d = 128 each
-// element of the thread's two rows as one 4-byte word (consecutive lanes: consecutive words; the
-// other half-wavefront 32 banks away), at d = 64 as single elements.
+// The tile into LDS: K with swizzled chunks; V transposed ([d][row], bf16 bits), each element of
+// the thread's two rows as one 4-byte word.
 template <int D>
 __device__ __forceinline__ void win_tile_store(const win_u32x4 (&pk)[kWinTile * D / 8 / 256],
                                                const win_u32x4 (&pv)[kWinTile * D / 8 / 256], uint4 *kt,
@@ -644,28 +646,15 @@ __device__ __forceinline__ void win_tile_store(const win_u32x4 (&pk)[kWinTile * 
         const int cid = tid + 256 * u, row = cid / CPR, c = cid % CPR;
         reinterpret_cast<win_u32x4 *>(kt)[chunk_at<D>(row, c)] = pk[u];
     }
-    if constexpr (D == 128) {
 #pragma unroll
-        for (int u = 0; u < NCH / 2; ++u) {
-            const int row = 2 * (tid & 31), c = v_chunk<D>(u, tid);
-            uint32_t *vd = reinterpret_cast<uint32_t *>(vt + (c * 8) * kVtStride + row);
+    for (int u = 0; u < NCH / 2; ++u) {
+        const int row = 2 * v_pair<D>(tid), c = v_chunk<D>(u, tid);
+        uint32_t *vd = reinterpret_cast<uint32_t *>(vt + (c * 8) * kVtStride + row);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t a = pv[2 * u][e], b = pv[2 * u + 1][e];
-                vd[(2 * e) * (kVtStride / 2)] = (a & 0xFFFFu) | (b << 16);
-                vd[(2 * e + 1) * (kVtStride / 2)] = (a >> 16) | (b & 0xFFFF0000u);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int cid = tid + 256 * u, row = cid / CPR, c = cid % CPR;
-            uint16_t *vd = vt + (c * 8) * kVtStride + row;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vd[(2 * e) * kVtStride] = (uint16_t)pv[u][e];
-                vd[(2 * e + 1) * kVtStride] = (uint16_t)(pv[u][e] >> 16);
-            }
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t a = pv[2 * u][e], b = pv[2 * u + 1][e];
+            vd[(2 * e) * (kVtStride / 2)] = (a & 0xFFFFu) | (b << 16);
+            vd[(2 * e + 1) * (kVtStride / 2)] = (a >> 16) | (b & 0xFFFF0000u);
         }
     }
 }
