@@ -9,7 +9,8 @@
 //                   queries in fp32 (row_key); per block and query a 32-byte record: four of its
 //                   rows (key, offset) and a key X that every other row of the block stays at or
 //                   below (with the mass diagnostic also the block's largest score and its sum of
-//                   exp2((s - m_b) * scale)).
+//                   exp2((s - m_b) * scale)). Its last workgroups make the softmax partials of the
+//                   anchor and window rows, in chunks of kWinChunkRows per query vector.
 //   decode_finish   one workgroup per query vector: the exact top-k' from the records, C_i to
 //                   out_idx, and the restricted softmax times V.
 #pragma once
@@ -42,7 +43,8 @@ struct DecodeArgs {
     int32_t *out_idx;   // [nqv][cap]
     float *out;         // [nqv][D] (null: select only)
     float *mass;        // [nqv][4] (null: no diagnostic)
-    float *win;         // [nqv][nch][D + 2] anchor-and-window partials (decode_window), or null
+    float *win;         // [nqv][nch][D + 2] anchor-and-window partials (decode_stream's last
+                        // workgroups), or null (no output)
     int nch;            // chunks of kWinChunkRows rows per query vector (win only)
 };
 
